@@ -1,0 +1,109 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its pins
+catch every one of them.  Nothing here touches the HIP library."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fibottention as fo
+import tests.test_oracle as pins
+
+
+def _expect_pin_failure(pin, *args):
+    with pytest.raises(AssertionError):
+        pin(*args)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = fo._head_scores
+
+    def unscaled(q, k, deltas):
+        return orig(q, k, deltas) * math.sqrt(q.shape[-1])
+
+    monkeypatch.setattr(fo, "_head_scores", unscaled)
+    _expect_pin_failure(pins.test_forward_matches_torch_sdpa_fp64)
+
+
+def test_transposed_operands_are_caught(monkeypatch):
+    orig = fo._head_scores
+    monkeypatch.setattr(fo, "_head_scores", lambda q, k, deltas: orig(k, q, deltas))
+    _expect_pin_failure(pins.test_forward_matches_torch_sdpa_fp64)
+
+
+def test_one_sided_offsets_are_caught(monkeypatch):
+    monkeypatch.setattr(fo, "signed_offsets", lambda offs: sorted(int(f) for f in offs))
+    _expect_pin_failure(pins.test_forward_matches_dense_brute_force, 13)
+
+
+def test_one_sided_mask_is_caught(monkeypatch):
+    def upper_only(n, offsets):
+        allowed = set(int(f) for f in offsets)
+        m = np.zeros((n, n), dtype=bool)
+        for j in range(n):
+            for k in range(n):
+                if k - j in allowed:
+                    m[j, k] = True
+        return m
+
+    monkeypatch.setattr(oracle, "support_mask", upper_only)
+    _expect_pin_failure(pins.test_support_pair_count_closed_form_and_symmetry, 17)
+
+
+def test_missing_D_term_is_caught(monkeypatch):
+    orig_probs = fo._head_probs
+    # Returning P unchanged but with the backward's D forced to zero is the
+    # classic mistake dS = P * dP; emulate it by zeroing D through P's sum.
+    src = fo.backward
+
+    def bad_backward(q, k, v, do, offs):
+        dq, dk, dv = src(q, k, v, do, offs)
+        # add back P * D K-terms: equivalent to dropping "- D_j"
+        q64, k64, v64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        o, _ = fo.forward(q64, k64, v64, offs)
+        D = (o * do64).sum(-1)
+        B, H, N, d = q64.shape
+        for h in range(H):
+            for dl in fo.signed_offsets(offs[h]):
+                lo, hi = max(0, -dl), min(N, N - dl)
+                if lo >= hi:
+                    continue
+                S = fo._head_scores(q64[:, h], k64[:, h], fo.signed_offsets(offs[h]))
+                P, _ = orig_probs(S)
+                i = fo.signed_offsets(offs[h]).index(dl)
+                dq[:, h, lo:hi] += (P[i, :, lo:hi] * D[:, h, lo:hi])[..., None] * \
+                    k64[:, h, lo + dl:hi + dl] / math.sqrt(d)
+        return dq, dk, dv
+
+    monkeypatch.setattr(oracle, "backward", bad_backward)
+    _expect_pin_failure(pins.test_backward_matches_torch_autograd_fp64)
+
+
+def test_literal_paper_wythoff_formula_is_caught(monkeypatch):
+    # The garbled printed form a_i = floor(i phi), b_i = floor(floor(i phi) phi^2)
+    phi = (1 + 5 ** 0.5) / 2
+
+    def literal(i):
+        a = math.floor(i * phi)
+        return a, math.floor(a * phi * phi)
+
+    monkeypatch.setattr(oracle, "wythoff_row", literal)
+    _expect_pin_failure(pins.test_wythoff_rows_partition_the_positive_integers)
+
+
+def test_literal_readme_wythoff_formula_is_caught(monkeypatch):
+    phi = (1 + 5 ** 0.5) / 2
+    monkeypatch.setattr(oracle, "wythoff_row",
+                        lambda i: (int(i * phi * phi), int(i * phi * phi ** 2)))
+    _expect_pin_failure(pins.test_wythoff_rows_partition_the_positive_integers)
+
+
+def test_window_overshoot_is_caught(monkeypatch):
+    # Algorithm 1's raw output keeps the first term >= w; forgetting the
+    # set definition's |j-k| <= w filter must be caught.
+    def overshoot(a, b, w, n):
+        return sorted({f for f in fo.fib_sequence_alg1(a, b, w) if f <= n - 1})
+
+    monkeypatch.setattr(oracle, "fib_offsets", overshoot)
+    _expect_pin_failure(pins.test_offsets_brute_force_membership, 300, 20, "small")

@@ -1,0 +1,142 @@
+/*
+ * fibatt.h -- C ABI of the Fibottention sparse-attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  Fibottention restricts multi-head self-attention to a
+ * per-head support set.  Head i (1-based) uses the generalized Fibonacci
+ * sequence Fib(a_i, b_i) (f_1 = a, f_2 = b, f_{n+1} = f_n + f_{n-1}) and a
+ * window w_i; query j attends key k iff |j - k| is a term of that sequence
+ * and |j - k| <= w_i.  Scores are Q_j . K_k / sqrt(d_h) on the support and
+ * -inf elsewhere; a softmax over each query row weights the value rows.
+ * (Fibottention paper, arXiv 2406.19391, method section: eq. (1) with the
+ * -inf indicator, the definition of Omega_w^{Fib(a,b)}, the Wythoff array
+ * paragraph for (a_i, b_i) and eq. (3) for the per-head support; the project
+ * README's Algorithms 1 and 3 for the sequence loop and the softmax/P.V
+ * steps; the 1/sqrt(d_h) scale is that of scaled dot-product attention as
+ * restated in the "Dilated Neighborhood Attention Transformer" background.)
+ *
+ * Conventions shared by every entry point
+ *  - Return value: FIBATT_OK (0) or one of the fibatt_status codes.  No entry
+ *    point throws or aborts.  On error a message is available from
+ *    fibatt_last_error() (per calling thread) and no output is written and no
+ *    GPU work is enqueued.
+ *  - Tensor layout: Q, K, V, O, dO, dQ, dK, dV are dense row-major
+ *    [B, H, N, d_h] (head-major slabs of N rows of d_h elements); LSE and the
+ *    backward workspace are [B, H, N].  Every tensor pointer must be 16-byte
+ *    aligned and outputs must not alias inputs or each other.
+ *  - Ownership: the caller allocates and frees every buffer (device memory
+ *    for tensors, host memory for the per-head parameter arrays).  The library
+ *    allocates no device memory and keeps no state between calls.
+ *  - Streams: GPU work is enqueued on the HIP stream passed as `stream`
+ *    (a hipStream_t; NULL means the default stream) and the call returns
+ *    without synchronising.  A fault inside a kernel surfaces at the caller's
+ *    next synchronisation, as for any HIP launch.
+ *  - Heads: tensor head h (0-based) uses a[h], b[h], w[h]; the usual choice
+ *    is Wythoff row h + 1 (fibatt_wythoff).  Requirements: a[h] >= 0,
+ *    b[h] >= 1 (so the sequence grows and (0, 0) is impossible),
+ *    1 <= w[h] <= N.  A distance of 0 (a[h] = 0) is the diagonal and counts
+ *    once.  Distances >= N have no pairs.
+ */
+#ifndef FIBATT_H
+#define FIBATT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FIBATT_OK = 0,
+  FIBATT_E_INVAL = 1,       /* bad argument: null pointer, bad size, bad a/b/w, misalignment */
+  FIBATT_E_RANGE = 2,       /* a result does not fit the caller's buffer or int32 */
+  FIBATT_E_UNSUPPORTED = 3, /* valid but not implemented: d_h, dtype, H above FIBATT_MAX_HEADS */
+  FIBATT_E_HIP = 4          /* the HIP runtime reported an error while enqueuing work */
+} fibatt_status;
+
+typedef enum {
+  FIBATT_F32 = 0,  /* IEEE binary32 */
+  FIBATT_BF16 = 1  /* bfloat16 */
+} fibatt_dtype;
+
+/* Largest number of heads one call accepts. */
+#define FIBATT_MAX_HEADS 128
+
+/* Problem description shared by fibatt_fwd and fibatt_bwd.
+ *  B, H, N, d_h : batch, heads, tokens per sequence, head width (64 or 128).
+ *  dtype        : element type of Q, K, V, O and dO (a fibatt_dtype value).
+ *  a, b, w      : HOST arrays of H int32 each (see "Heads" above); read
+ *                 during the call only. */
+typedef struct {
+  int32_t B, H, N, d_h;
+  int32_t dtype;
+  const int32_t* a;
+  const int32_t* b;
+  const int32_t* w;
+} fibatt_desc;
+
+/* Row i >= 1 of the Wythoff array: *a = floor(floor(i*phi)*phi),
+ * *b = floor(floor(i*phi)*phi^2) = *a + floor(i*phi), computed in exact
+ * integer arithmetic.  The Fibottention paper (Wythoff array paragraph) takes
+ * head i's sequence from this row, whose rows are disjoint and cover every
+ * positive integer.  Errors: E_INVAL if i < 1 or a pointer is NULL, E_RANGE
+ * if *b would exceed INT32_MAX. */
+int fibatt_wythoff(int32_t i, int32_t* a, int32_t* b);
+
+/* Host-only offset table (no GPU involved).  For each head h, the distinct
+ * distances f of Fib(a[h], b[h]) with f <= min(w[h], N - 1), ascending
+ * (README Algorithm 1 generates the sequence; the paper's set definition
+ * keeps the terms within the window).  Output in CSR form:
+ *   head_ptr[H + 1] : head_ptr[0] = 0, head h owns offs[head_ptr[h] .. head_ptr[h+1]).
+ *   offs[offs_cap]  : the distances (int32).
+ * head_ptr is always written in full on success or E_RANGE.  If the total
+ * exceeds offs_cap the call returns E_RANGE, writes only head_ptr, and
+ * head_ptr[H] is the capacity needed (two-call sizing).  offs may be NULL
+ * when offs_cap is 0.  Errors: E_INVAL for H < 1, N < 1, NULL arrays or bad
+ * a/b/w. */
+int fibatt_offsets(int32_t H, int32_t N, const int32_t* a, const int32_t* b,
+                   const int32_t* w, int32_t* head_ptr, int32_t* offs,
+                   int32_t offs_cap);
+
+/* Forward pass.  Device pointers:
+ *   q, k, v : [B, H, N, d_h] in desc->dtype (read).
+ *   o       : [B, H, N, d_h] in desc->dtype (written): O_j = sum_k P_jk V_k.
+ *   lse     : [B, H, N] fp32 (written): natural-log log-sum-exp of row j's
+ *             scaled scores; -inf for a row with no key in its support, whose
+ *             O row is then 0.
+ * Accumulation is fp32 for either dtype.  Errors: E_INVAL, E_UNSUPPORTED
+ * (d_h not 64/128, dtype not F32/BF16, H > FIBATT_MAX_HEADS), E_HIP. */
+int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k,
+               const void* v, void* o, float* lse, void* stream);
+
+/* Number of fp32 elements of the workspace fibatt_bwd needs (B*H*N), or -1
+ * for an invalid descriptor. */
+int64_t fibatt_bwd_workspace_floats(const fibatt_desc* desc);
+
+/* Backward pass: gradients of sum(O * dO) for the forward above.
+ *   q, k, v, o, dout : [B, H, N, d_h] in desc->dtype (read); o and lse must be
+ *                      what fibatt_fwd produced for the same q, k, v.
+ *   lse              : [B, H, N] fp32 (read).
+ *   dq, dk, dv       : [B, H, N, d_h] fp32 (written).
+ *   workspace        : fibatt_bwd_workspace_floats(desc) fp32 elements of
+ *                      device scratch (contents on entry ignored, clobbered).
+ * With P the support-restricted softmax, dP_jk = dO_j . V_k and
+ * D_j = dO_j . O_j: dS = P (dP - D), dQ = dS K / sqrt(d_h),
+ * dK = dS^T Q / sqrt(d_h), dV = P^T dO.  The support is symmetric, so dK and
+ * dV are gathered key by key over the same offsets (no atomics; results are
+ * bitwise reproducible run to run).  Errors as for fibatt_fwd. */
+int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k,
+               const void* v, const void* o, const float* lse,
+               const void* dout, float* dq, float* dk, float* dv,
+               float* workspace, void* stream);
+
+/* Message describing the last error on the calling thread ("" if none).
+ * The pointer stays valid until the thread's next fibatt_* call. */
+const char* fibatt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIBATT_H */

@@ -1,0 +1,27 @@
+"""Fibottention sparse multi-head attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library libfibatt.so (C ABI in include/fibatt.h);
+this package only marshals arguments to it.
+"""
+
+from .fibatt import (  # noqa: F401
+    BF16,
+    E_HIP,
+    E_INVAL,
+    E_RANGE,
+    E_UNSUPPORTED,
+    EXPORTED,
+    F32,
+    LIB_PATH,
+    MAX_HEADS,
+    OK,
+    FibattError,
+    Fibottention,
+    FibottentionFunction,
+    backward,
+    forward,
+    lib,
+    offsets,
+    wythoff,
+    wythoff_rows,
+)

@@ -1,0 +1,194 @@
+// C entry points of libfibatt: argument validation, the Wythoff helper, the
+// host offset table and dispatch to the kernels.  Every check runs on the
+// host before anything is enqueued; on error nothing is written and the
+// message is kept per thread for fibatt_last_error().
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/fibatt.h"
+#include "fib_offsets.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return FIBATT_OK;
+}
+
+// floor(sqrt(x)) for 0 <= x < 2^63, exact.
+uint64_t isqrt_u64(uint64_t x) {
+  uint64_t r = static_cast<uint64_t>(std::sqrt(static_cast<long double>(x)));
+  while (r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;
+  return r;
+}
+
+// floor(n * phi) = floor((n + sqrt(5 n^2)) / 2); sqrt(5 n^2) is irrational
+// for n >= 1, so flooring it first does not change the result.
+uint64_t floor_n_phi(uint64_t n) { return (n + isqrt_u64(5 * n * n)) / 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int32_t H, int32_t N, const int32_t* a, const int32_t* b, const int32_t* w) {
+  if (!a || !b || !w) return fail(FIBATT_E_INVAL, "a, b and w must be non-NULL host arrays");
+  for (int h = 0; h < H; ++h) {
+    if (a[h] < 0) return fail(FIBATT_E_INVAL, "a[%d] = %d must be >= 0", h, a[h]);
+    if (b[h] < 1) return fail(FIBATT_E_INVAL, "b[%d] = %d must be >= 1", h, b[h]);
+    if (w[h] < 1 || w[h] > N)
+      return fail(FIBATT_E_INVAL, "w[%d] = %d must lie in [1, N = %d]", h, w[h], N);
+  }
+  return FIBATT_OK;
+}
+
+int check_desc(const fibatt_desc* d, fibatt::Problem* p) {
+  if (!d) return fail(FIBATT_E_INVAL, "desc is NULL");
+  if (d->B < 1 || d->H < 1 || d->N < 1)
+    return fail(FIBATT_E_INVAL, "B, H, N must be >= 1 (got %d, %d, %d)", d->B, d->H, d->N);
+  if (d->d_h != 64 && d->d_h != 128)
+    return fail(FIBATT_E_UNSUPPORTED, "d_h = %d: supported head widths are 64 and 128", d->d_h);
+  if (d->dtype != FIBATT_F32 && d->dtype != FIBATT_BF16)
+    return fail(FIBATT_E_UNSUPPORTED, "dtype %d: supported are FIBATT_F32 and FIBATT_BF16",
+                d->dtype);
+  if (d->H > FIBATT_MAX_HEADS)
+    return fail(FIBATT_E_UNSUPPORTED, "H = %d exceeds FIBATT_MAX_HEADS = %d", d->H,
+                FIBATT_MAX_HEADS);
+  const int64_t slabs = static_cast<int64_t>(d->B) * d->H;
+  // Kernel grids are 1-D with at most 2^31 - 1 workgroups (the smallest row
+  // tile is 32 rows, and the streaming backward launches two tiles per
+  // tile); element offsets are computed in 64-bit.
+  if (slabs * ((d->N + 31) / 32) * 2 > 0x7fffffffll)
+    return fail(FIBATT_E_UNSUPPORTED, "B*H*N too large for one launch");
+  int rc = check_heads(d->H, d->N, d->a, d->b, d->w);
+  if (rc) return rc;
+  p->B = d->B;
+  p->H = d->H;
+  p->N = d->N;
+  p->D = d->d_h;
+  p->dtype = d->dtype == FIBATT_BF16 ? fibatt::DType::kBF16 : fibatt::DType::kF32;
+  for (int h = 0; h < d->H; ++h) {
+    p->heads.a[h] = d->a[h];
+    p->heads.b[h] = d->b[h];
+    p->heads.lim[h] = (d->w[h] < d->N - 1) ? d->w[h] : d->N - 1;
+  }
+  return FIBATT_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(FIBATT_E_INVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FIBATT_E_INVAL, "%s is not 16-byte aligned", name);
+  return FIBATT_OK;
+}
+
+// Test hook: FIBATT_PATH=slab|stream forces a kernel variant (default auto).
+fibatt::Path path_from_env() {
+  const char* s = std::getenv("FIBATT_PATH");
+  if (!s) return fibatt::Path::kAuto;
+  if (std::string(s) == "slab") return fibatt::Path::kSlab;
+  if (std::string(s) == "stream") return fibatt::Path::kStream;
+  return fibatt::Path::kAuto;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fibatt_wythoff(int32_t i, int32_t* a, int32_t* b) {
+  if (!a || !b) return fail(FIBATT_E_INVAL, "output pointers must be non-NULL");
+  if (i < 1) return fail(FIBATT_E_INVAL, "Wythoff rows are numbered from 1 (got %d)", i);
+  const uint64_t p = floor_n_phi(static_cast<uint64_t>(i));
+  const uint64_t av = floor_n_phi(p);
+  const uint64_t bv = av + p;
+  if (bv > 0x7fffffffull) return fail(FIBATT_E_RANGE, "row %d does not fit int32", i);
+  *a = static_cast<int32_t>(av);
+  *b = static_cast<int32_t>(bv);
+  return ok();
+}
+
+int fibatt_offsets(int32_t H, int32_t N, const int32_t* a, const int32_t* b, const int32_t* w,
+                   int32_t* head_ptr, int32_t* offs, int32_t offs_cap) {
+  if (H < 1 || N < 1) return fail(FIBATT_E_INVAL, "H and N must be >= 1 (got %d, %d)", H, N);
+  if (!head_ptr) return fail(FIBATT_E_INVAL, "head_ptr is NULL");
+  if (offs_cap < 0 || (offs_cap > 0 && !offs))
+    return fail(FIBATT_E_INVAL, "offs must be non-NULL when offs_cap > 0");
+  int rc = check_heads(H, N, a, b, w);
+  if (rc) return rc;
+  int32_t tmp[fibatt::kMaxOffsets];
+  int64_t total = 0;
+  head_ptr[0] = 0;
+  for (int h = 0; h < H; ++h) {
+    const int64_t lim = w[h] < N - 1 ? w[h] : N - 1;
+    const int n = fibatt::fib_offsets_gen(a[h], b[h], lim, tmp, fibatt::kMaxOffsets);
+    if (total + n > 0x7fffffffll) return fail(FIBATT_E_RANGE, "offset table exceeds int32");
+    total += n;
+    head_ptr[h + 1] = static_cast<int32_t>(total);
+  }
+  if (total > offs_cap)
+    return fail(FIBATT_E_RANGE, "offs needs %lld entries, capacity %d", (long long)total,
+                offs_cap);
+  for (int h = 0; h < H; ++h) {
+    const int64_t lim = w[h] < N - 1 ? w[h] : N - 1;
+    fibatt::fib_offsets_gen(a[h], b[h], lim, offs + head_ptr[h], fibatt::kMaxOffsets);
+  }
+  return ok();
+}
+
+int64_t fibatt_bwd_workspace_floats(const fibatt_desc* desc) {
+  fibatt::Problem p;
+  if (check_desc(desc, &p)) return -1;
+  ok();
+  return static_cast<int64_t>(p.B) * p.H * p.N;
+}
+
+int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k, const void* v, void* o,
+               float* lse, void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
+    return rc;
+  const hipError_t e =
+      fibatt::launch_fwd(p, q, k, v, o, lse, static_cast<hipStream_t>(stream), path_from_env());
+  if (e != hipSuccess) return fail(FIBATT_E_HIP, "fibatt_fwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k, const void* v,
+               const void* o, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+               float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")) ||
+      (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const hipError_t e =
+      fibatt::launch_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                         static_cast<hipStream_t>(stream), path_from_env());
+  if (e != hipSuccess) return fail(FIBATT_E_HIP, "fibatt_bwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* fibatt_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

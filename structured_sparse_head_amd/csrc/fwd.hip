@@ -1,0 +1,270 @@
+// Forward kernels: sparse Fibottention attention O = softmax_Omega(Q K^T / sqrt(d)) V.
+//
+// Fibottention paper (arXiv 2406.19391), method section, eq. (1) and (3):
+// only the dot products on the head's support Omega_i are formed; every
+// other score is -inf.  The README's Algorithm 3 then applies a row softmax
+// and weights V.  Omega_i = {(j, k) : |j - k| in Fib(a_i, b_i), |j - k| <= w_i},
+// so for a fixed signed displacement delta the keys k = j + delta of
+// consecutive queries j are consecutive rows: a query tile meets, per
+// displacement, one contiguous shifted key/value tile.
+//
+// One lane group (G lanes) owns one query row j and walks the head's signed
+// displacements in chunks of C.  Per chunk it forms C scores, rescales its
+// running (max, sum, accumulator) once, and accumulates p * V rows: an online
+// softmax whose state never leaves registers.  Scores are kept in base 2
+// (scaled by log2(e) / sqrt(d)) so the exponentials are single v_exp_f32.
+//
+// Two variants:
+//  * slab: one workgroup per (b, h) slab; the slab's K and V are staged once
+//    into LDS with coalesced 16-byte loads (swizzled against bank conflicts)
+//    and every shifted tile is read from LDS.  Used when 2*N*d*sizeof(T)
+//    fits the LDS budget (e.g. ViT-B/16, N = 197).
+//  * stream: one workgroup per query tile; each lane group reads its shifted
+//    K/V rows straight from global memory (L2-resident for neighbouring
+//    tiles).  Used for long sequences.
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace fibatt {
+namespace {
+
+struct FwdArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;
+  int H;
+  int N;
+  int tiles;          // query tiles per slab (stream variant)
+  float scale_log2;   // log2(e) / sqrt(d)
+  HeadTable ht;
+};
+
+template <typename T, int D, int G>
+struct LdsKV {
+  const char* k;
+  const char* v;
+  __device__ void load_k(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
+    frag_load_lds<T, D, G>(k, r, part, f);
+  }
+  __device__ void load_v(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
+    frag_load_lds<T, D, G>(v, r, part, f);
+  }
+};
+
+template <typename T, int D, int G>
+struct GlobalKV {
+  const char* k;  // slab base
+  const char* v;
+  __device__ void load_k(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
+    frag_load_cached<T, D, G>(k + static_cast<size_t>(r) * Geom<T, D, G>::kRowBytes, part, f);
+  }
+  __device__ void load_v(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
+    frag_load_cached<T, D, G>(v + static_cast<size_t>(r) * Geom<T, D, G>::kRowBytes, part, f);
+  }
+};
+
+// Online softmax over the signed displacements for query row j.
+template <typename T, int D, int G, int C, typename KV>
+__device__ __forceinline__ void attend_row(const KV& kv, int j, int N, int part, const int* deltas,
+                                           int nd, float scale_log2,
+                                           const uint32_t (&qf)[Geom<T, D, G>::kWPL],
+                                           float (&acc)[Geom<T, D, G>::kDL], float& m, float& l) {
+  using Gm = Geom<T, D, G>;
+  using M = FragMath<T, Gm::kWPL>;
+  for (int i0 = 0; i0 < nd; i0 += C) {
+    float s[C];
+    int key[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int i = i0 + c;
+      const int kk = j + deltas[i < nd ? i : 0];
+      const bool ok = (i < nd) && (kk >= 0) && (kk < N);
+      key[c] = ok ? kk : -1;
+      float sc = -INFINITY;
+      if (ok) {
+        uint32_t kf[Gm::kWPL];
+        kv.load_k(kk, part, kf);
+        sc = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+      }
+      s[c] = sc;
+    }
+    float mc = s[0];
+#pragma unroll
+    for (int c = 1; c < C; ++c) mc = fmaxf(mc, s[c]);
+    const float mn = fmaxf(m, mc);
+    if (mn == -INFINITY) continue;  // nothing in range yet
+    const float alpha = fast_exp2(m - mn);  // 0 when m = -inf
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (key[c] >= 0) {
+        const float p = fast_exp2(s[c] - mn);
+        l += p;
+        uint32_t vf[Gm::kWPL];
+        kv.load_v(key[c], part, vf);
+        M::axpy(acc, p, vf);
+      }
+    }
+    m = mn;
+  }
+}
+
+// Normalise and write O (in T) and LSE (natural log) for row j.
+template <typename T, int D, int G>
+__device__ __forceinline__ void finish_row(const FwdArgs& a, size_t slab, int j, int part,
+                                           float (&acc)[Geom<T, D, G>::kDL], float m, float l) {
+  using Gm = Geom<T, D, G>;
+  const bool has = l > 0.f;
+  const float inv = has ? 1.0f / l : 0.f;
+  u32x4* orow = reinterpret_cast<u32x4*>(a.o + (slab * a.N + j) * Gm::kRowBytes) + part * Gm::kCPL;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int t = 0; t < Gm::kCPL; ++t) {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 8 * t + 2 * u;
+        w[u] = f32_to_bf16(acc[e] * inv) | (f32_to_bf16(acc[e + 1] * inv) << 16);
+      }
+      orow[t] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < Gm::kCPL; ++t) {
+      orow[t] = u32x4{__float_as_uint(acc[4 * t + 0] * inv), __float_as_uint(acc[4 * t + 1] * inv),
+                      __float_as_uint(acc[4 * t + 2] * inv), __float_as_uint(acc[4 * t + 3] * inv)};
+    }
+  }
+  if (part == 0) a.lse[slab * a.N + j] = has ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D, int G, int NT, int C>
+__global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs a) {
+  using Gm = Geom<T, D, G>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_deltas[kMaxSigned];
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ int s_nd;
+  const int tid = threadIdx.x;
+  const size_t slab = blockIdx.x;
+  const int h = static_cast<int>(slab % a.H);
+  const int N = a.N;
+  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  const size_t base = slab * N * Gm::kRowBytes;
+  char* lds_k = smem;
+  char* lds_v = smem + N * Gm::kRowBytes;
+  stage_rows_lds<T, D, NT, true>(lds_k, a.k + base, N, tid);
+  stage_rows_lds<T, D, NT, true>(lds_v, a.v + base, N, tid);
+  __syncthreads();
+  const int nd = s_nd;
+  const int part = tid % G;
+  const LdsKV<T, D, G> kv{lds_k, lds_v};
+  for (int j = tid / G; j < N; j += NT / G) {
+    uint32_t qf[Gm::kWPL];
+    frag_load_global<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
+    float acc[Gm::kDL];
+#pragma unroll
+    for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    attend_row<T, D, G, C>(kv, j, N, part, s_deltas, nd, a.scale_log2, qf, acc, m, l);
+    finish_row<T, D, G>(a, slab, j, part, acc, m, l);
+  }
+}
+
+template <typename T, int D, int G, int NT, int C>
+__global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs a) {
+  using Gm = Geom<T, D, G>;
+  __shared__ int s_deltas[kMaxSigned];
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ int s_nd;
+  const int tid = threadIdx.x;
+  const size_t slab = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x % a.tiles;
+  const int h = static_cast<int>(slab % a.H);
+  const int N = a.N;
+  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  __syncthreads();
+  const int j = tile * (NT / G) + tid / G;
+  if (j >= N) return;
+  const int part = tid % G;
+  const size_t base = slab * N * Gm::kRowBytes;
+  const GlobalKV<T, D, G> kv{a.k + base, a.v + base};
+  uint32_t qf[Gm::kWPL];
+  frag_load_global<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
+  float acc[Gm::kDL];
+#pragma unroll
+  for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  attend_row<T, D, G, C>(kv, j, N, part, s_deltas, s_nd, a.scale_log2, qf, acc, m, l);
+  finish_row<T, D, G>(a, slab, j, part, acc, m, l);
+}
+
+// Lane-group width per (dtype, d): each lane owns 128 bytes of a row.
+template <typename T, int D>
+constexpr int fwd_group() {
+  return (D * static_cast<int>(sizeof(T))) / 128;
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                        float* lse, hipStream_t stream, Path path) {
+  constexpr int G = fwd_group<T, D>();
+  constexpr int NT = 256;
+  constexpr int C = 8;
+  using Gm = Geom<T, D, G>;
+  FwdArgs a;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.o = static_cast<char*>(o);
+  a.lse = lse;
+  a.H = p.H;
+  a.N = p.N;
+  a.scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+  a.ht = p.heads;
+  const size_t slabs = static_cast<size_t>(p.B) * p.H;
+  const bool slab_ok = fwd_slab_fits(p);
+  if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
+    if (!slab_ok) return hipErrorInvalidValue;
+    const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes;
+    auto kern = fwd_slab_kernel<T, D, G, NT, C>;
+    // Opt the kernel into the full slab budget once per process.
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kSlabLdsBudget);
+    if (attr != hipSuccess) return attr;
+    a.tiles = 1;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NT), lds, stream, a);
+  } else {
+    const int rows = NT / G;
+    a.tiles = (p.N + rows - 1) / rows;
+    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C>),
+                       dim3(static_cast<unsigned>(slabs * a.tiles)), dim3(NT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_slab_fits(const Problem& p) {
+  const int esize = p.dtype == DType::kBF16 ? 2 : 4;
+  return 2ll * p.N * p.D * esize <= kSlabLdsBudget;
+}
+
+hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t stream, Path path) {
+  if (p.dtype == DType::kBF16) {
+    if (p.D == 64) return launch_fwd_t<bf16_t, 64>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 128) return launch_fwd_t<bf16_t, 128>(p, q, k, v, o, lse, stream, path);
+  } else {
+    if (p.D == 64) return launch_fwd_t<float, 64>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 128) return launch_fwd_t<float, 128>(p, q, k, v, o, lse, stream, path);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fibatt

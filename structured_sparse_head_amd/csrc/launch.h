@@ -1,0 +1,37 @@
+// Internal interface between the C entry points and the kernel translation
+// units.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_common.h"
+
+namespace fibatt {
+
+enum class DType : int { kF32 = 0, kBF16 = 1 };
+
+struct Problem {
+  int B, H, N, D;
+  DType dtype;
+  HeadTable heads;  // a, b, lim = min(w, N - 1) per head
+};
+
+// LDS bytes a workgroup may use on the slab-resident paths (two workgroups
+// per CU fit in gfx950's 160 KiB).
+constexpr int kSlabLdsBudget = 80 * 1024;
+
+// Which kernels a problem runs on; exposed so tests can force either path.
+enum class Path : int { kAuto = 0, kSlab = 1, kStream = 2 };
+
+hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t stream, Path path);
+
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, float* workspace, hipStream_t stream, Path path);
+
+bool fwd_slab_fits(const Problem& p);
+bool bwd_slab_fits(const Problem& p);
+
+}  // namespace fibatt

@@ -1,0 +1,218 @@
+"""Thin Python binding of libfibatt (include/fibatt.h) via ctypes.
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the current HIP
+stream.  If the shared library is missing the first call raises; there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfibatt.so")
+
+OK, E_INVAL, E_RANGE, E_UNSUPPORTED, E_HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+MAX_HEADS = 128
+
+EXPORTED = ("fibatt_wythoff", "fibatt_offsets", "fibatt_fwd", "fibatt_bwd",
+            "fibatt_bwd_workspace_floats", "fibatt_last_error")
+
+
+class FibattError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"fibatt error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("d_h", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("a", ctypes.POINTER(ctypes.c_int32)),
+        ("b", ctypes.POINTER(ctypes.c_int32)),
+        ("w", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m structured_sparse_head_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vp = ctypes.c_void_p
+    L.fibatt_wythoff.argtypes = [ctypes.c_int32, i32p, i32p]
+    L.fibatt_wythoff.restype = ctypes.c_int
+    L.fibatt_offsets.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p, i32p, i32p,
+                                 ctypes.c_int32]
+    L.fibatt_offsets.restype = ctypes.c_int
+    L.fibatt_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp]
+    L.fibatt_fwd.restype = ctypes.c_int
+    L.fibatt_bwd.argtypes = [ctypes.POINTER(Desc)] + [vp] * 11
+    L.fibatt_bwd.restype = ctypes.c_int
+    L.fibatt_bwd_workspace_floats.argtypes = [ctypes.POINTER(Desc)]
+    L.fibatt_bwd_workspace_floats.restype = ctypes.c_int64
+    L.fibatt_last_error.argtypes = []
+    L.fibatt_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise FibattError(rc, lib().fibatt_last_error().decode())
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(arr: np.ndarray):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def wythoff(i: int) -> Tuple[int, int]:
+    """(a_i, b_i) of Wythoff row i >= 1."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().fibatt_wythoff(i, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def wythoff_rows(H: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(a, b) int32 arrays for tensor heads 0..H-1 (Wythoff rows 1..H)."""
+    pairs = [wythoff(i) for i in range(1, H + 1)]
+    return _i32([p[0] for p in pairs]), _i32([p[1] for p in pairs])
+
+
+def offsets(N: int, a, b, w) -> Tuple[np.ndarray, np.ndarray]:
+    """CSR offset table (head_ptr[H+1], offs) from the host generator."""
+    a, b, w = _i32(a), _i32(b), _i32(w)
+    H = len(a)
+    head_ptr = np.zeros(H + 1, dtype=np.int32)
+    rc = lib().fibatt_offsets(H, N, _ptr(a), _ptr(b), _ptr(w), _ptr(head_ptr), None, 0)
+    if rc not in (OK, E_RANGE):
+        _check(rc)
+    offs = np.zeros(max(int(head_ptr[-1]), 1), dtype=np.int32)
+    _check(lib().fibatt_offsets(H, N, _ptr(a), _ptr(b), _ptr(w), _ptr(head_ptr), _ptr(offs),
+                                len(offs)))
+    return head_ptr, offs[:head_ptr[-1]]
+
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class Fibottention:
+    """A fixed problem shape (B, H, N, d_h, dtype) and per-head (a, b, w).
+
+    Keeps the marshalled descriptor so repeated calls cost one ctypes call.
+    """
+
+    def __init__(self, B: int, H: int, N: int, d_h: int, dtype: torch.dtype,
+                 a: Sequence[int], b: Sequence[int], w: Sequence[int]):
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.shape = (B, H, N, d_h)
+        self.dtype = dtype
+        self._a, self._b, self._w = _i32(a), _i32(b), _i32(w)
+        if not (len(self._a) == len(self._b) == len(self._w) == H):
+            raise ValueError("a, b, w must have H entries")
+        self.desc = Desc(B, H, N, d_h, _DTYPES[dtype], _ptr(self._a), _ptr(self._b), _ptr(self._w))
+        self._dp = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    def _args(self, *tensors):
+        for t in tensors:
+            if t is None:
+                continue
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous device tensors")
+        return [None if t is None else t.data_ptr() for t in tensors]
+
+    def workspace_floats(self) -> int:
+        n = self._lib.fibatt_bwd_workspace_floats(self._dp)
+        if n < 0:
+            _check(E_INVAL)
+        return int(n)
+
+    def forward(self, q, k, v, o=None, lse=None, stream: Optional[int] = None):
+        """(o, lse).  o in the input dtype, lse fp32 [B, H, N]."""
+        for t in (q, k, v):
+            if tuple(t.shape) != self.shape or t.dtype != self.dtype:
+                raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(self.shape[:3], dtype=torch.float32, device=q.device)
+        ptrs = self._args(q, k, v, o, lse)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        _check(self._lib.fibatt_fwd(self._dp, *ptrs, s))
+        return o, lse
+
+    def backward(self, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
+                 stream: Optional[int] = None):
+        """(dq, dk, dv) in fp32."""
+        for t in (q, k, v, o, do):
+            if tuple(t.shape) != self.shape or t.dtype != self.dtype:
+                raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
+        dev = q.device
+        mk = lambda: torch.empty(self.shape, dtype=torch.float32, device=dev)  # noqa: E731
+        dq = mk() if dq is None else dq
+        dk = mk() if dk is None else dk
+        dv = mk() if dv is None else dv
+        if workspace is None:
+            workspace = torch.empty(self.workspace_floats(), dtype=torch.float32, device=dev)
+        ptrs = self._args(q, k, v, o, lse, do, dq, dk, dv, workspace)
+        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        _check(self._lib.fibatt_bwd(self._dp, *ptrs, s))
+        return dq, dk, dv
+
+
+def forward(q, k, v, a, b, w):
+    """One-shot forward for q, k, v of shape [B, H, N, d_h] on the GPU."""
+    B, H, N, d = q.shape
+    return Fibottention(B, H, N, d, q.dtype, a, b, w).forward(q, k, v)
+
+
+def backward(q, k, v, o, lse, do, a, b, w):
+    """One-shot backward; returns fp32 (dq, dk, dv)."""
+    B, H, N, d = q.shape
+    return Fibottention(B, H, N, d, q.dtype, a, b, w).backward(q, k, v, o, lse, do)
+
+
+class FibottentionFunction(torch.autograd.Function):
+    """autograd wrapper: y = Fibottention(q, k, v); gradients from fibatt_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, a, b, w):
+        B, H, N, d = q.shape
+        op = Fibottention(B, H, N, d, q.dtype, a, b, w)
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = op.forward(q, k, v)
+        ctx.op = op
+        ctx.save_for_backward(q, k, v, o, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = ctx.op.backward(q, k, v, o, lse, do.to(q.dtype).contiguous())
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None

@@ -1,0 +1,194 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its
+host-only results match the oracle bit for bit, and every invalid argument is
+rejected before any GPU work.  No kernel is launched here."""
+
+import ctypes
+import os
+import re
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import structured_sparse_head_amd as fa
+from structured_sparse_head_amd import fibatt as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "fibatt.h")) as fh:
+        text = fh.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(fibatt_\w+)\s*\(", text, re.M))
+    assert declared == set(fa.EXPORTED)
+    L = fa.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_wythoff_matches_oracle():
+    for i in range(1, 1001):
+        assert fa.wythoff(i) == oracle.wythoff_row(i), i
+
+
+def test_wythoff_large_rows_match_decimal_closed_form():
+    getcontext().prec = 80
+    phi = (Decimal(1) + Decimal(5).sqrt()) / 2
+    rng = np.random.default_rng(5)
+    rows = [int(x) for x in rng.integers(1000, 800_000_000, size=300)] + [820_000_000]
+    for i in rows:
+        p = int((Decimal(i) * phi).to_integral_value(rounding="ROUND_FLOOR"))
+        a = int((Decimal(p) * phi).to_integral_value(rounding="ROUND_FLOOR"))
+        b = int((Decimal(p) * phi * phi).to_integral_value(rounding="ROUND_FLOOR"))
+        if b > 2 ** 31 - 1:
+            with pytest.raises(fa.FibattError) as ei:
+                fa.wythoff(i)
+            assert ei.value.code == fa.E_RANGE
+        else:
+            assert fa.wythoff(i) == (a, b), i
+
+
+def test_wythoff_rejects_bad_rows():
+    for i in (0, -1, -(2 ** 31)):
+        with pytest.raises(fa.FibattError) as ei:
+            fa.wythoff(i)
+        assert ei.value.code == fa.E_INVAL
+
+
+@pytest.mark.parametrize("num", sorted(workloads.WORKLOADS))
+def test_offset_tables_bit_exact_for_workloads(num):
+    wl = workloads.WORKLOADS[num]
+    a, b = oracle.wythoff_rows(wl.H)
+    w = workloads.windows(wl)
+    ptr, offs = fa.offsets(wl.N, a, b, w)
+    optr, ooffs = oracle.offset_table(wl.N, a, b, w)
+    assert np.array_equal(ptr, optr)
+    assert np.array_equal(offs, ooffs)
+
+
+def test_offset_tables_bit_exact_random():
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        H = int(rng.integers(1, 20))
+        N = int(rng.choice([1, 2, 3, 5, 17, 100, 1000, 70000, 2 ** 31 - 1]))
+        a = rng.integers(0, 60, size=H)
+        b = rng.integers(1, 60, size=H)
+        w = rng.integers(1, min(N, 10 ** 9) + 1, size=H)
+        if rng.random() < 0.3:
+            a[:] = rng.integers(0, 3, size=H)
+            b[:] = rng.integers(1, 3, size=H)
+        ptr, offs = fa.offsets(N, a, b, w)
+        optr, ooffs = oracle.offset_table(N, a, b, w)
+        assert np.array_equal(ptr, optr), (N, a, b, w)
+        assert np.array_equal(offs, ooffs), (N, a, b, w)
+
+
+def test_offsets_two_call_sizing_and_errors():
+    L = fa.lib()
+    a, b, w = fb._i32([1, 4]), fb._i32([2, 7]), fb._i32([197, 197])
+    ptr = np.zeros(3, dtype=np.int32)
+    rc = L.fibatt_offsets(2, 197, fb._ptr(a), fb._ptr(b), fb._ptr(w), fb._ptr(ptr), None, 0)
+    assert rc == fa.E_RANGE and list(ptr) == [0, 11, 19]
+    small = np.zeros(5, dtype=np.int32)
+    rc = L.fibatt_offsets(2, 197, fb._ptr(a), fb._ptr(b), fb._ptr(w), fb._ptr(ptr),
+                          fb._ptr(small), 5)
+    assert rc == fa.E_RANGE and ptr[-1] == 19
+    assert b"capacity" in L.fibatt_last_error()
+    bad = [
+        (0, 197, a, b, w), (2, 0, a, b, w),
+        (2, 197, fb._i32([-1, 4]), b, w), (2, 197, a, fb._i32([2, 0]), w),
+        (2, 197, a, b, fb._i32([0, 197])), (2, 197, a, b, fb._i32([197, 198])),
+    ]
+    for H, N, aa, bb, ww in bad:
+        rc = L.fibatt_offsets(H, N, fb._ptr(aa), fb._ptr(bb), fb._ptr(ww), fb._ptr(ptr), None, 0)
+        assert rc == fa.E_INVAL, (H, N)
+        assert L.fibatt_last_error() != b""
+    rc = L.fibatt_offsets(2, 197, None, fb._ptr(b), fb._ptr(w), fb._ptr(ptr), None, 0)
+    assert rc == fa.E_INVAL
+    rc = L.fibatt_offsets(2, 197, fb._ptr(a), fb._ptr(b), fb._ptr(w), None, None, 0)
+    assert rc == fa.E_INVAL
+
+
+# --------------------------------------------------------------------------
+# fwd / bwd argument validation (fails before any launch, so no GPU needed)
+# --------------------------------------------------------------------------
+
+class _Case:
+    def __init__(self, **kw):
+        p = dict(B=2, H=3, N=65, d_h=64, dtype=fa.BF16, a=[1, 4, 6], b=[2, 7, 10],
+                 w=[65, 65, 65])
+        p.update(kw)
+        self.a, self.b, self.w = fb._i32(p["a"]), fb._i32(p["b"]), fb._i32(p["w"])
+        self.desc = fb.Desc(p["B"], p["H"], p["N"], p["d_h"], p["dtype"],
+                            fb._ptr(self.a), fb._ptr(self.b), fb._ptr(self.w))
+
+
+GOOD = 0x10000  # aligned dummy address, never dereferenced on these paths
+
+
+def _fwd(desc, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD):
+    return fa.lib().fibatt_fwd(ctypes.byref(desc) if desc is not None else None, q, k, v, o, lse,
+                               None)
+
+
+def _bwd(desc, ptrs=None):
+    p = [GOOD] * 10 if ptrs is None else ptrs
+    return fa.lib().fibatt_bwd(ctypes.byref(desc) if desc is not None else None, *p, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), fa.E_INVAL), (dict(H=0, a=[], b=[], w=[]), fa.E_INVAL), (dict(N=0), fa.E_INVAL),
+    (dict(d_h=32), fa.E_UNSUPPORTED), (dict(d_h=96), fa.E_UNSUPPORTED),
+    (dict(dtype=7), fa.E_UNSUPPORTED),
+    (dict(H=129, a=[1] * 129, b=[2] * 129, w=[65] * 129), fa.E_UNSUPPORTED),
+    (dict(a=[-1, 4, 6]), fa.E_INVAL), (dict(b=[2, 0, 10]), fa.E_INVAL),
+    (dict(a=[0, 4, 6], b=[0, 7, 10]), fa.E_INVAL),
+    (dict(w=[65, 0, 65]), fa.E_INVAL), (dict(w=[65, 66, 65]), fa.E_INVAL),
+])
+def test_fwd_bwd_reject_bad_descriptors(kw, code):
+    c = _Case(**kw)
+    assert _fwd(c.desc) == code
+    assert fa.lib().fibatt_last_error() != b""
+    assert _bwd(c.desc) == code
+    assert fa.lib().fibatt_bwd_workspace_floats(ctypes.byref(c.desc)) == -1
+
+
+def test_fwd_bwd_reject_null_and_misaligned_pointers():
+    c = _Case()
+    assert _fwd(None) == fa.E_INVAL
+    for i in range(5):
+        args = [GOOD] * 5
+        args[i] = None
+        assert _fwd(c.desc, *args) == fa.E_INVAL
+        args[i] = GOOD + 4
+        assert _fwd(c.desc, *args) == fa.E_INVAL
+        assert b"aligned" in fa.lib().fibatt_last_error()
+    assert _bwd(None) == fa.E_INVAL
+    for i in range(10):
+        ptrs = [GOOD] * 10
+        ptrs[i] = None
+        assert _bwd(c.desc, ptrs) == fa.E_INVAL
+        ptrs[i] = GOOD + 8
+        assert _bwd(c.desc, ptrs) == fa.E_INVAL
+
+
+def test_null_head_arrays_rejected():
+    c = _Case()
+    c.desc.a = ctypes.POINTER(ctypes.c_int32)()
+    assert _fwd(c.desc) == fa.E_INVAL
+    assert _bwd(c.desc) == fa.E_INVAL
+
+
+def test_workspace_size():
+    c = _Case()
+    assert fa.lib().fibatt_bwd_workspace_floats(ctypes.byref(c.desc)) == 2 * 3 * 65
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    op = fa.Fibottention(2, 3, 65, 64, torch.float32, [1, 4, 6], [2, 7, 10], [65] * 3)
+    q = torch.zeros(2, 3, 65, 64)
+    with pytest.raises(ValueError):
+        op.forward(q, q, q, o=q, lse=torch.zeros(2, 3, 65))

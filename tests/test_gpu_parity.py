@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (max-abs, elementwise): fp32 inputs 1e-4; bf16 inputs with fp32
+accumulation 2e-2 (outputs O in bf16, LSE and gradients in fp32).  Offset
+tables and Wythoff rows must match bit for bit.  Both kernel variants (LDS
+slab and streaming) are exercised where a shape allows both.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import structured_sparse_head_amd as fa
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _set_path(path):
+    if path is None:
+        os.environ.pop("FIBATT_PATH", None)
+    else:
+        os.environ["FIBATT_PATH"] = path
+
+
+def _heads(H, N, w=None, ab=None):
+    if ab is None:
+        a, b = oracle.wythoff_rows(H)
+        ga, gb = fa.wythoff_rows(H)
+        assert np.array_equal(a, ga) and np.array_equal(b, gb)
+    else:
+        a, b = (np.asarray(x, dtype=np.int32) for x in ab)
+    w = np.full(H, N, dtype=np.int32) if w is None else np.asarray(w, dtype=np.int32)
+    ptr, offs = fa.offsets(N, a, b, w)
+    optr, ooffs = oracle.offset_table(N, a, b, w)
+    assert np.array_equal(ptr, optr) and np.array_equal(offs, ooffs)
+    F = [oracle.fib_offsets(int(a[h]), int(b[h]), int(w[h]), N) for h in range(H)]
+    return a, b, w, F
+
+
+def _gpu_run(inp, a, b, w, with_bwd=True):
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    op = fa.Fibottention(B, H, N, d, q.dtype, a, b, w)
+    o, lse = op.forward(q, k, v)
+    out = {"o": o, "lse": lse}
+    if with_bwd:
+        do = inp["do"].to(dev)
+        dq, dk, dv = op.backward(q, k, v, o, lse, do)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {n: t.cpu() for n, t in out.items()}
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True):
+    """Element-by-element comparison on the selected (batch, head) slabs."""
+    sel_b = slice(None) if batches is None else list(batches)
+    x = {n: _f64(inp[n])[sel_b] for n in inp}
+    if heads is not None:
+        x = {n: t[:, heads] for n, t in x.items()}
+        F = [F[h] for h in heads]
+    g = {n: _f64(t)[sel_b] for n, t in gpu.items()}
+    if heads is not None:
+        g = {n: t[:, heads] for n, t in g.items()}
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], F)
+    err = {"o": float(np.abs(g["o"] - o).max()) if o.size else 0.0}
+    fin = np.isfinite(lse)
+    assert np.array_equal(np.isfinite(g["lse"]), fin), "empty-row pattern of LSE differs"
+    assert (g["lse"][~fin] == -np.inf).all()
+    err["lse"] = float(np.abs(g["lse"][fin] - lse[fin]).max()) if fin.any() else 0.0
+    if with_bwd:
+        dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], F)
+        for n, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+            err[n] = float(np.abs(g[n] - ref).max()) if ref.size else 0.0
+    _say(f"    max-abs errors: {err}")
+    for n, e in err.items():
+        assert e <= tol, (n, e, tol)
+    return err
+
+
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
+def test_workload1_tiny_fp32(path):
+    wl = workloads.WORKLOADS[1]
+    _say(f"case: workload 1 {wl.name} path={path}")
+    _set_path(path)
+    try:
+        inp = workloads.make_inputs(wl)
+        a, b, w, F = _heads(wl.H, wl.N)
+        gpu = _gpu_run(inp, a, b, w)
+        _compare(gpu, inp, F, TOL[torch.float32])
+    finally:
+        _set_path(None)
+
+
+@pytest.mark.parametrize("path", [None, "stream"])
+def test_workload2_vit_b(path):
+    wl = workloads.WORKLOADS[2]
+    _say(f"case: workload 2 {wl.name} path={path}")
+    _set_path(path)
+    try:
+        inp = workloads.make_inputs(wl)
+        a, b, w, F = _heads(wl.H, wl.N)
+        gpu = _gpu_run(inp, a, b, w)
+        _compare(gpu, inp, F, TOL[torch.bfloat16])
+    finally:
+        _set_path(None)
+
+
+def test_workload3_video_sampled_batches():
+    wl = workloads.WORKLOADS[3]
+    _say(f"case: workload 3 {wl.name}, full GPU run, oracle on batches 0 and 15")
+    inp = workloads.make_inputs(wl)
+    a, b, w, F = _heads(wl.H, wl.N, w=workloads.windows(wl))
+    gpu = _gpu_run(inp, a, b, w)
+    _compare(gpu, inp, F, TOL[torch.bfloat16], batches=[0, 15])
+
+
+def test_workload4_highres_sampled_batches():
+    wl = workloads.WORKLOADS[4]
+    _say(f"case: workload 4 {wl.name}, full GPU run, oracle on batch 3")
+    inp = workloads.make_inputs(wl)
+    a, b, w, F = _heads(wl.H, wl.N)
+    gpu = _gpu_run(inp, a, b, w)
+    _compare(gpu, inp, F, TOL[torch.bfloat16], batches=[3])
+
+
+def test_workload5_long_sampled_heads():
+    wl = workloads.WORKLOADS[5]
+    _say(f"case: workload 5 {wl.name}, full GPU run, oracle on heads 0 and 15")
+    inp = workloads.make_inputs(wl)
+    a, b, w, F = _heads(wl.H, wl.N)
+    gpu = _gpu_run(inp, a, b, w)
+    _compare(gpu, inp, F, TOL[torch.bfloat16], heads=[0, 15])
+
+
+EDGE = [
+    # (name, B, H, N, d, dtype, ab, w)
+    ("N1", 2, 3, 1, 64, torch.bfloat16, None, None),
+    ("N2", 1, 3, 2, 64, torch.float32, None, None),
+    ("N5 empty rows", 2, 3, 5, 64, torch.float32, None, None),
+    ("N90 f=N-1", 1, 2, 90, 64, torch.float32, None, None),
+    ("diag a=0 dup a=b", 2, 3, 40, 64, torch.float32, ([0, 3, 5], [1, 3, 1]), [40, 40, 3]),
+    ("windows", 2, 4, 150, 64, torch.bfloat16, None, [1, 7, 30, 150]),
+    ("ragged 257", 1, 4, 257, 64, torch.bfloat16, None, None),
+    ("slab max 320", 1, 3, 320, 64, torch.bfloat16, None, None),
+    ("stream 513", 1, 3, 513, 64, torch.bfloat16, None, None),
+    ("d128 bf16 small", 2, 3, 100, 128, torch.bfloat16, None, None),
+    ("d128 fp32", 1, 3, 150, 128, torch.float32, None, None),
+    ("d64 fp32 mid", 1, 5, 700, 64, torch.float32, None, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+@pytest.mark.parametrize("path", [None, "stream"])
+def test_edge_cases(case, path):
+    name, B, H, N, d, dtype, ab, w = case
+    _say(f"case: edge {name} B={B} H={H} N={N} d={d} {dtype} path={path}")
+    _set_path(path)
+    try:
+        inp = workloads.random_case(1234 + N, B, H, N, d, dtype)
+        a, b, w, F = _heads(H, N, w=w, ab=ab)
+        gpu = _gpu_run(inp, a, b, w)
+        _compare(gpu, inp, F, TOL[dtype])
+    finally:
+        _set_path(None)
+
+
+def test_empty_support_gives_zero_and_neg_inf():
+    _say("case: all rows empty (N=4, heads 2..3 have no distance < 4)")
+    inp = workloads.random_case(5, 1, 3, 4, 64, torch.float32)
+    a, b, w, F = _heads(3, 4)
+    assert F[1] == [] and F[2] == []
+    gpu = _gpu_run(inp, a, b, w)
+    assert (gpu["o"][:, 1:] == 0).all() and torch.isneginf(gpu["lse"][:, 1:]).all()
+    for n in ("dq", "dk", "dv"):
+        assert (gpu[n][:, 1:] == 0).all()
+
+
+def test_backward_bitwise_deterministic():
+    _say("case: determinism, workload 2 shape, two backward runs")
+    wl = workloads.WORKLOADS[2]
+    inp = workloads.make_inputs(wl, B=8)
+    a, b, w, F = _heads(wl.H, wl.N)
+    r1 = _gpu_run(inp, a, b, w)
+    r2 = _gpu_run(inp, a, b, w)
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_autograd_function_matches_oracle():
+    _say("case: autograd wrapper, fp32 N=65")
+    inp = workloads.random_case(77, 1, 3, 65, 64, torch.float32)
+    a, b, w, F = _heads(3, 65)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev).requires_grad_() for n in ("q", "k", "v"))
+    y = fa.FibottentionFunction.apply(q, k, v, a, b, w)
+    y.backward(inp["do"].to(dev))
+    o, _ = oracle.forward(*(_f64(inp[n]) for n in ("q", "k", "v")), F)
+    dq, dk, dv = oracle.backward(*(_f64(inp[n]) for n in ("q", "k", "v", "do")), F)
+    assert np.abs(_f64(y.detach().cpu()) - o).max() <= 1e-4
+    for t, ref in ((q, dq), (k, dk), (v, dv)):
+        assert np.abs(_f64(t.grad.cpu()) - ref).max() <= 1e-4

@@ -1,0 +1,223 @@
+"""Benchmark: Fibottention sparse attention forward + backward on one MI355X.
+
+One step = one forward and one backward pass over one batch of the ViT-B/16
+attention workload (B=64, H=12, N=197, d_h=64, bf16 inputs, fp32
+accumulation), with inputs resident in HBM.  Several buffer sets are rotated
+so that each pass reads data that is not left in the 256 MB last-level
+cache by the pass before it (the backward of a step works on a set whose
+forward ran half a rotation earlier, as in a network with other layers in
+between).
+
+Prints one JSON line.  `value` is Q.K pairs per second over forward +
+backward; the line also carries tokens/s, the achieved algorithmic HBM
+bandwidth, per-kernel timings, a roofline entry for the dominant kernel and
+the CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def _pairs_per_slab(N, F):
+    return [int(sum(2 * (N - int(f)) if f > 0 else N for f in fs)) for fs in F]
+
+
+def _bytes(wl, esize):
+    """Algorithmic HBM bytes per pass (whole batch).
+
+    forward : read Q, K, V (input dtype); write O (input dtype), LSE (fp32).
+    backward: read Q, K, V, dO (input dtype), LSE (fp32); write dQ, dK, dV (fp32).
+    """
+    rows = wl.B * wl.H * wl.N
+    row = wl.d * esize
+    fwd = rows * (4 * row + 4)
+    bwd = rows * (4 * row + 4 + 3 * wl.d * 4)
+    return int(fwd), int(bwd)
+
+
+def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0):
+    """The oracle (fp64 numpy), forward + backward over the whole batch,
+    repeated until `budget_s` seconds of CPU time have passed."""
+    import oracle  # test infrastructure; used only for this baseline leg
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    x = {n: inp[n].double().numpy() for n in ("q", "k", "v", "do")}
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(x["q"], x["k"], x["v"], F)
+        oracle.backward(x["q"], x["k"], x["v"], x["do"], F)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    return {
+        "value": pairs_per_pass * reps / el,
+        "unit": "pairs/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole workload (B={wl.B}), forward + backward, {reps} repetitions in "
+                  f"{el:.1f} s, fp64 numpy, one thread",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the op shards over (batch, head) slabs with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    import structured_sparse_head_amd as fa
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    a, b = fa.wythoff_rows(wl.H)
+    w = workloads.windows(wl)
+    ptr, offs = fa.offsets(wl.N, a, b, w)
+    F = [[int(f) for f in offs[ptr[h]:ptr[h + 1]]] for h in range(wl.H)]
+    pairs_per_pass = int(wl.B * sum(_pairs_per_slab(wl.N, F)))
+    esize = 2 if wl.dtype == "bf16" else 4
+    fwd_bytes, bwd_bytes = _bytes(wl, esize)
+
+    inp = workloads.make_inputs(wl)
+    op = fa.Fibottention(wl.B, wl.H, wl.N, wl.d, wl.torch_dtype, a, b, w)
+    R = max(2, args.sets)
+    sets = []
+    for _ in range(R):
+        s = {n: inp[n].to(dev).clone() for n in ("q", "k", "v", "do")}
+        s["o"] = torch.empty_like(s["q"])
+        s["lse"] = torch.empty(wl.B, wl.H, wl.N, dtype=torch.float32, device=dev)
+        for n in ("dq", "dk", "dv"):
+            s[n] = torch.empty(wl.B, wl.H, wl.N, wl.d, dtype=torch.float32, device=dev)
+        s["ws"] = torch.empty(op.workspace_floats(), dtype=torch.float32, device=dev)
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def fwd(s):
+        op.forward(s["q"], s["k"], s["v"], s["o"], s["lse"], stream=stream)
+
+    def bwd(s):
+        op.backward(s["q"], s["k"], s["v"], s["lse"], s["do"], s["dq"], s["dk"], s["dv"],
+                    s["ws"], stream=stream)
+
+    for s in sets:  # every set gets a forward before any backward reads its LSE
+        fwd(s)
+    half = R // 2
+    for i in range(args.warmup):
+        fwd(sets[i % R])
+        bwd(sets[(i + half) % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        fwd(sets[i % R])
+        e[1].record()
+        e[2].record()
+        bwd(sets[(i + half) % R])
+        e[3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    def stats(x):
+        return {"mean_us": float(x.mean() * 1e3), "median_us": float(np.median(x) * 1e3),
+                "p10_us": float(np.percentile(x, 10) * 1e3),
+                "p90_us": float(np.percentile(x, 90) * 1e3)}
+
+    kernels = {
+        "fwd": {**stats(fwd_ms), "bytes": fwd_bytes,
+                "gbps": fwd_bytes / (fwd_ms.mean() * 1e-3) / 1e9},
+        "bwd": {**stats(bwd_ms), "bytes": bwd_bytes,
+                "gbps": bwd_bytes / (bwd_ms.mean() * 1e-3) / 1e9},
+    }
+    dom = "bwd" if bwd_ms.mean() >= fwd_ms.mean() else "fwd"
+    ach = kernels[dom]["gbps"]
+    step_s = ms_step * 1e-3
+    line = {
+        "metric": "sparse Q.K pairs/s (fwd+bwd), ViT-B/16 N=197 H=12, 1 GPU",
+        "value": pairs_per_pass / step_s,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"Fibottention attention, {wl.name} (ViT-B/16 224px tokens)"
+            if args.workload == 2 else f"Fibottention attention, {wl.name}",
+            "B": wl.B, "H": wl.H, "N": wl.N, "d_h": wl.d,
+            "heads": "Wythoff rows 1..H",
+            "pairs_per_pass": pairs_per_pass,
+            "buffer_sets": R,
+        },
+        "tokens_per_s": wl.B * wl.N / step_s,
+        "hbm_gbps_fwd_bwd": (fwd_bytes + bwd_bytes) / step_s / 1e9,
+        "wall_s_timed": wall,
+        "kernels": kernels,
+        "roofline": {
+            "kernel": f"{dom} ({'bwd_slab_kernel' if dom == 'bwd' else 'fwd_slab_kernel'} "
+                      "on this workload)",
+            "bound": "hbm",
+            "achieved": ach,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBPS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inp, F, pairs_per_pass)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -115,21 +115,22 @@ int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k,
 int64_t fibatt_bwd_workspace_floats(const fibatt_desc* desc);
 
 /* Backward pass: gradients of sum(O * dO) for the forward above.
- *   q, k, v, o, dout : [B, H, N, d_h] in desc->dtype (read); o and lse must be
- *                      what fibatt_fwd produced for the same q, k, v.
- *   lse              : [B, H, N] fp32 (read).
- *   dq, dk, dv       : [B, H, N, d_h] fp32 (written).
- *   workspace        : fibatt_bwd_workspace_floats(desc) fp32 elements of
- *                      device scratch (contents on entry ignored, clobbered).
- * With P the support-restricted softmax, dP_jk = dO_j . V_k and
- * D_j = dO_j . O_j: dS = P (dP - D), dQ = dS K / sqrt(d_h),
- * dK = dS^T Q / sqrt(d_h), dV = P^T dO.  The support is symmetric, so dK and
- * dV are gathered key by key over the same offsets (no atomics; results are
- * bitwise reproducible run to run).  Errors as for fibatt_fwd. */
+ *   q, k, v, dout : [B, H, N, d_h] in desc->dtype (read).
+ *   lse           : [B, H, N] fp32 (read): what fibatt_fwd produced for the
+ *                   same q, k, v.  The forward output O itself is not needed.
+ *   dq, dk, dv    : [B, H, N, d_h] fp32 (written).
+ *   workspace     : fibatt_bwd_workspace_floats(desc) fp32 elements of device
+ *                   scratch (contents on entry ignored, clobbered).
+ * With P the support-restricted softmax (recomputed from lse),
+ * dP_jk = dO_j . V_k and D_j = sum_k P_jk dP_jk (summed in fp32, which is
+ * dO_j . O_j without O's storage rounding): dS = P (dP - D),
+ * dQ = dS K / sqrt(d_h), dK = dS^T Q / sqrt(d_h), dV = P^T dO.  The support
+ * is symmetric, so dK and dV are gathered key by key over the same offsets
+ * (no atomics; results are bitwise reproducible run to run).  Errors as for
+ * fibatt_fwd. */
 int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k,
-               const void* v, const void* o, const float* lse,
-               const void* dout, float* dq, float* dk, float* dv,
-               float* workspace, void* stream);
+               const void* v, const float* lse, const void* dout, float* dq,
+               float* dk, float* dv, float* workspace, void* stream);
 
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */

@@ -172,18 +172,18 @@ int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k, const void
 }
 
 int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k, const void* v,
-               const void* o, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+               const float* lse, const void* dout, float* dq, float* dk, float* dv,
                float* workspace, void* stream) {
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
-      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
       (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")) ||
       (rc = check_ptr(workspace, "workspace")))
     return rc;
   const hipError_t e =
-      fibatt::launch_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+      fibatt::launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, workspace,
                          static_cast<hipStream_t>(stream), path_from_env());
   if (e != hipSuccess) return fail(FIBATT_E_HIP, "fibatt_bwd launch: %s", hipGetErrorString(e));
   return ok();

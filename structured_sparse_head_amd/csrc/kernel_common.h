@@ -171,11 +171,15 @@ struct FragMath<float, WPL> {
 #pragma unroll
     for (int t = 0; t < WPL; ++t) acc[t] = __builtin_fmaf(p, __uint_as_float(v[t]), acc[t]);
   }
-  __device__ static __forceinline__ float dot_acc(const float (&a)[kDL], const uint32_t (&b)[WPL]) {
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+  // x += c1 * v and y += c2 * v with one read of v.
+  __device__ static __forceinline__ void axpy2(float (&x)[kDL], float c1, float (&y)[kDL], float c2,
+                                               const uint32_t (&v)[WPL]) {
 #pragma unroll
-    for (int t = 0; t < WPL; ++t) s[t & 3] = __builtin_fmaf(a[t], __uint_as_float(b[t]), s[t & 3]);
-    return (s[0] + s[1]) + (s[2] + s[3]);
+    for (int t = 0; t < WPL; ++t) {
+      const float e = __uint_as_float(v[t]);
+      x[t] = __builtin_fmaf(c1, e, x[t]);
+      y[t] = __builtin_fmaf(c2, e, y[t]);
+    }
   }
 };
 
@@ -196,6 +200,18 @@ struct FragMath<bf16_t, WPL> {
     for (int t = 0; t < WPL; ++t) {
       acc[2 * t + 0] = __builtin_fmaf(p, bf16_lo(v[t]), acc[2 * t + 0]);
       acc[2 * t + 1] = __builtin_fmaf(p, bf16_hi(v[t]), acc[2 * t + 1]);
+    }
+  }
+  __device__ static __forceinline__ void axpy2(float (&x)[kDL], float c1, float (&y)[kDL], float c2,
+                                               const uint32_t (&v)[WPL]) {
+#pragma unroll
+    for (int t = 0; t < WPL; ++t) {
+      const float lo = bf16_lo(v[t]);
+      const float hi = bf16_hi(v[t]);
+      x[2 * t + 0] = __builtin_fmaf(c1, lo, x[2 * t + 0]);
+      x[2 * t + 1] = __builtin_fmaf(c1, hi, x[2 * t + 1]);
+      y[2 * t + 0] = __builtin_fmaf(c2, lo, y[2 * t + 0]);
+      y[2 * t + 1] = __builtin_fmaf(c2, hi, y[2 * t + 1]);
     }
   }
 };

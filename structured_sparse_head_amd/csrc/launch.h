@@ -28,8 +28,8 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
                       float* lse, hipStream_t stream, Path path);
 
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
-                      const void* o, const float* lse, const void* dout, float* dq, float* dk,
-                      float* dv, float* workspace, hipStream_t stream, Path path);
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      float* workspace, hipStream_t stream, Path path);
 
 bool fwd_slab_fits(const Problem& p);
 bool bwd_slab_fits(const Problem& p);

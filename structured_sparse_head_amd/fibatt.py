@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
     L.fibatt_offsets.restype = ctypes.c_int
     L.fibatt_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp]
     L.fibatt_fwd.restype = ctypes.c_int
-    L.fibatt_bwd.argtypes = [ctypes.POINTER(Desc)] + [vp] * 11
+    L.fibatt_bwd.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10
     L.fibatt_bwd.restype = ctypes.c_int
     L.fibatt_bwd_workspace_floats.argtypes = [ctypes.POINTER(Desc)]
     L.fibatt_bwd_workspace_floats.restype = ctypes.c_int64
@@ -167,10 +167,10 @@ class Fibottention:
         _check(self._lib.fibatt_fwd(self._dp, *ptrs, s))
         return o, lse
 
-    def backward(self, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
+    def backward(self, q, k, v, lse, do, dq=None, dk=None, dv=None, workspace=None,
                  stream: Optional[int] = None):
-        """(dq, dk, dv) in fp32."""
-        for t in (q, k, v, o, do):
+        """(dq, dk, dv) in fp32; lse is the forward's."""
+        for t in (q, k, v, do):
             if tuple(t.shape) != self.shape or t.dtype != self.dtype:
                 raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
         dev = q.device
@@ -180,7 +180,7 @@ class Fibottention:
         dv = mk() if dv is None else dv
         if workspace is None:
             workspace = torch.empty(self.workspace_floats(), dtype=torch.float32, device=dev)
-        ptrs = self._args(q, k, v, o, lse, do, dq, dk, dv, workspace)
+        ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
         s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
         _check(self._lib.fibatt_bwd(self._dp, *ptrs, s))
         return dq, dk, dv
@@ -192,10 +192,10 @@ def forward(q, k, v, a, b, w):
     return Fibottention(B, H, N, d, q.dtype, a, b, w).forward(q, k, v)
 
 
-def backward(q, k, v, o, lse, do, a, b, w):
+def backward(q, k, v, lse, do, a, b, w):
     """One-shot backward; returns fp32 (dq, dk, dv)."""
     B, H, N, d = q.shape
-    return Fibottention(B, H, N, d, q.dtype, a, b, w).backward(q, k, v, o, lse, do)
+    return Fibottention(B, H, N, d, q.dtype, a, b, w).backward(q, k, v, lse, do)
 
 
 class FibottentionFunction(torch.autograd.Function):
@@ -208,11 +208,11 @@ class FibottentionFunction(torch.autograd.Function):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o, lse = op.forward(q, k, v)
         ctx.op = op
-        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.save_for_backward(q, k, v, lse)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = ctx.op.backward(q, k, v, o, lse, do.to(q.dtype).contiguous())
+        q, k, v, lse = ctx.saved_tensors
+        dq, dk, dv = ctx.op.backward(q, k, v, lse, do.to(q.dtype).contiguous())
         return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None

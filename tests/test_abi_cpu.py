@@ -134,7 +134,7 @@ def _fwd(desc, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD):
 
 
 def _bwd(desc, ptrs=None):
-    p = [GOOD] * 10 if ptrs is None else ptrs
+    p = [GOOD] * 9 if ptrs is None else ptrs
     return fa.lib().fibatt_bwd(ctypes.byref(desc) if desc is not None else None, *p, None)
 
 
@@ -166,8 +166,8 @@ def test_fwd_bwd_reject_null_and_misaligned_pointers():
         assert _fwd(c.desc, *args) == fa.E_INVAL
         assert b"aligned" in fa.lib().fibatt_last_error()
     assert _bwd(None) == fa.E_INVAL
-    for i in range(10):
-        ptrs = [GOOD] * 10
+    for i in range(9):
+        ptrs = [GOOD] * 9
         ptrs[i] = None
         assert _bwd(c.desc, ptrs) == fa.E_INVAL
         ptrs[i] = GOOD + 8

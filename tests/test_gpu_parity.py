@@ -58,7 +58,7 @@ def _gpu_run(inp, a, b, w, with_bwd=True):
     out = {"o": o, "lse": lse}
     if with_bwd:
         do = inp["do"].to(dev)
-        dq, dk, dv = op.backward(q, k, v, o, lse, do)
+        dq, dk, dv = op.backward(q, k, v, lse, do)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in out.items()}

@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB, 10 times "
+                         "(scale reference for HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -98,6 +101,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 10}), flush=True)
+        return
 
     import workloads
     import structured_sparse_head_amd as fa

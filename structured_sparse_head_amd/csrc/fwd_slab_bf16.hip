@@ -1,0 +1,377 @@
+// Forward kernel specialised for short bf16 sequences with d_h = 64
+// (ViT-scale token counts, N <= 256): one persistent workgroup per CU walks
+// a strided list of (b, h) slabs and overlaps the HBM reads of the next slab
+// with the arithmetic on the current one.
+//
+// Same mathematics as the generic kernels (Fibottention paper, method
+// section, eq. (1) and (3); README Algorithm 3): scores Q_j . K_k / sqrt(d)
+// on the head's support, a row softmax, P V.  Design points:
+//
+//  * Lanes.  Two lanes own a query row, each holding 32 of its 64 elements:
+//    lanes 0-31 of a wave take the first halves of 32 consecutive rows and
+//    lanes 32-63 the second halves, so one v_permlane32_swap plus one add
+//    completes a dot product.
+//  * LDS layout.  K rows are kept in bf16 with a 144-byte stride and V rows
+//    in fp32 (converted once while staging) with a 272-byte stride, both an
+//    odd number of 16-byte units, and one base address plus immediate
+//    offsets reaches a whole fragment.  Measured on gfx950 (64 banks), a
+//    ds_read_b128 serves the two 32-lane halves of a wave separately and,
+//    within a half, the lane quads whose index has even popcount
+//    ({0-3, 12-15, 20-23, 24-27}) together and the odd ones together.  Each
+//    such group then reads 16 rows that are distinct modulo 16, and an odd
+//    stride maps them to 16 distinct 16-byte bank groups: no conflicts.
+//  * Softmax.  All scores of a row (at most 12 distances, each signed, plus
+//    0, for N <= 256) stay in registers: one pass forms them, the row
+//    maximum is taken once, a second pass exponentiates and accumulates P V
+//    in fp32.  No rescaling of the accumulator is needed.  Each pass walks
+//    the +f and -f displacements separately: for a wave's 32 rows the useful
+//    ones are a prefix of the ascending distances in each direction, so the
+//    trip counts are wave-uniform and whole-wave misses are skipped.  Reads
+//    are branch-free (out-of-range keys use a clamped row and score -inf) and
+//    double-buffered so the next fragment is in flight during the arithmetic.
+//  * Overlap.  While a slab is computed from LDS, each thread already holds
+//    the next slab's K, V chunks and its own Q fragment in flight in
+//    registers; they are committed to LDS after the next barrier.
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace fibatt {
+namespace {
+
+constexpr int kThreads = 512;        // 8 waves; 256 query rows at 2 lanes per row
+constexpr int kMaxRows = kThreads / 2;
+constexpr int kMaxPosSlab = 12;      // positive distances below 256: at most 1,2,3,5,...,233
+constexpr int kKStride = 144;        // bytes per bf16 K row in LDS (128 + 16)
+constexpr int kVStride = 272;        // bytes per fp32 V row in LDS (256 + 16)
+constexpr int kRowBytes = 128;       // bf16 row of 64 elements in HBM
+constexpr int kChunksPerThread = kMaxRows * (kRowBytes / 16) / kThreads;  // 4
+
+struct Args {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;
+  int H;
+  int N;
+  int slabs;
+  float scale_log2;
+  HeadTable ht;
+};
+
+struct Prefetch {
+  u32x4 k[kChunksPerThread];
+  u32x4 v[kChunksPerThread];
+  u32x4 q[4];
+};
+
+// Loads are unconditional (indices clamped into the slab) so that every
+// prefetch register is overwritten each time; only the LDS commit is masked.
+__device__ __forceinline__ void issue_prefetch(const Args& a, size_t slab, int tid, int row,
+                                               int part, Prefetch& pf) {
+  const size_t base = slab * static_cast<size_t>(a.N) * kRowBytes;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
+  const int last = a.N * (kRowBytes / 16) - 1;
+#pragma unroll
+  for (int c = 0; c < kChunksPerThread; ++c) {
+    int idx = tid + c * kThreads;
+    idx = idx < last ? idx : last;
+    pf.k[c] = __builtin_nontemporal_load(ks + idx);
+    pf.v[c] = __builtin_nontemporal_load(vs + idx);
+  }
+  const int r = row < a.N ? row : a.N - 1;
+  const u32x4* qs =
+      reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(r) * kRowBytes + part * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pf.q[t] = __builtin_nontemporal_load(qs + t);
+}
+
+__device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, int N, int tid,
+                                                const Prefetch& pf) {
+  const int chunks = N * (kRowBytes / 16);
+#pragma unroll
+  for (int c = 0; c < kChunksPerThread; ++c) {
+    const int idx = tid + c * kThreads;
+    if (idx < chunks) {
+      const int r = idx >> 3;
+      const int ch = idx & 7;
+      *reinterpret_cast<u32x4*>(lds_k + r * kKStride + ch * 16) = pf.k[c];
+      const u32x4 x = pf.v[c];
+      const u32x4 lo = {x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
+      const u32x4 hi = {x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
+      *reinterpret_cast<u32x4*>(lds_v + r * kVStride + ch * 32) = lo;
+      *reinterpret_cast<u32x4*>(lds_v + r * kVStride + ch * 32 + 16) = hi;
+    }
+  }
+}
+
+// Sum of x over the lane pair (l, l ^ 32).
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void load_k(const char* lds_k, int kk, int part, u32x4 (&f)[4]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(lds_k + __umul24(kk, kKStride) + part * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) f[t] = p[t];
+}
+
+__device__ __forceinline__ void load_v(const char* lds_v, int kk, int part, u32x4 (&f)[8]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(lds_v + __umul24(kk, kVStride) + part * 128);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f[t] = p[t];
+}
+
+__device__ __forceinline__ float dot_q_k(const uint32_t (&qw)[16], const u32x4 (&k)[4]) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t kw[4] = {k[t].x, k[t].y, k[t].z, k[t].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[4 * t + u]),
+                                               __builtin_bit_cast(bf16x2_t, kw[u]), acc[u], false);
+  }
+  return pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
+__device__ __forceinline__ void axpy_v(float (&o)[32], float p, const u32x4 (&v)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    o[4 * t + 0] = __builtin_fmaf(p, __uint_as_float(v[t].x), o[4 * t + 0]);
+    o[4 * t + 1] = __builtin_fmaf(p, __uint_as_float(v[t].y), o[4 * t + 1]);
+    o[4 * t + 2] = __builtin_fmaf(p, __uint_as_float(v[t].z), o[4 * t + 2]);
+    o[4 * t + 3] = __builtin_fmaf(p, __uint_as_float(v[t].w), o[4 * t + 3]);
+  }
+}
+
+__device__ __forceinline__ int clamp_row(int r, int N) { return r < 0 ? 0 : (r >= N ? N - 1 : r); }
+
+// Scores for displacements sgn * pos[i], i < n (wave-uniform n).  Out-of-range
+// keys are read from a clamped row and scored -inf.  The next key fragment is
+// requested before the current dot product so LDS latency overlaps arithmetic.
+template <int SGN>
+__device__ __forceinline__ void scores_dir(const char* lds_k, const int (&pos)[kMaxPosSlab], int n,
+                                           int row, int part, int N, const uint32_t (&qw)[16],
+                                           float (&s)[kMaxPosSlab]) {
+  u32x4 kb[2][4];
+  if (n > 0) load_k(lds_k, clamp_row(row + SGN * pos[0], N), part, kb[0]);
+#pragma unroll
+  for (int i = 0; i < kMaxPosSlab; ++i) {
+    s[i] = -INFINITY;
+    if (i < n) {
+      if (i + 1 < kMaxPosSlab && i + 1 < n)
+        load_k(lds_k, clamp_row(row + SGN * pos[i + 1 < kMaxPosSlab ? i + 1 : i], N), part,
+               kb[(i + 1) & 1]);
+      const int kk = row + SGN * pos[i];
+      const float d = dot_q_k(qw, kb[i & 1]);
+      s[i] = (static_cast<unsigned>(kk) < static_cast<unsigned>(N)) ? d : -INFINITY;
+    }
+  }
+}
+
+template <int SGN>
+__device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&pos)[kMaxPosSlab],
+                                               int n, int row, int part, int N, float c, float mc,
+                                               const float (&s)[kMaxPosSlab], float& l,
+                                               float (&o)[32]) {
+  u32x4 vb[2][8];
+  if (n > 0) load_v(lds_v, clamp_row(row + SGN * pos[0], N), part, vb[0]);
+#pragma unroll
+  for (int i = 0; i < kMaxPosSlab; ++i) {
+    if (i < n) {
+      if (i + 1 < kMaxPosSlab && i + 1 < n)
+        load_v(lds_v, clamp_row(row + SGN * pos[i + 1 < kMaxPosSlab ? i + 1 : i], N), part,
+               vb[(i + 1) & 1]);
+      const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
+      l += p;
+      axpy_v(o, p, vb[i & 1]);
+    }
+  }
+}
+
+__device__ __forceinline__ void attend_row(const Args& a, size_t slab, int row, int part,
+                                           const char* lds_k, const char* lds_v,
+                                           const int (&pos)[kMaxPosSlab], int n_plus, int n_minus,
+                                           bool has0, const u32x4 (&q)[4]) {
+  const int N = a.N;
+  uint32_t qw[16];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    qw[4 * t + 0] = q[t].x;
+    qw[4 * t + 1] = q[t].y;
+    qw[4 * t + 2] = q[t].z;
+    qw[4 * t + 3] = q[t].w;
+  }
+  // Pass 1: raw scores Q_j . K_k for every signed displacement.
+  float sp[kMaxPosSlab], sm[kMaxPosSlab];
+  scores_dir<+1>(lds_k, pos, n_plus, row, part, N, qw, sp);
+  scores_dir<-1>(lds_k, pos, n_minus, row, part, N, qw, sm);
+  float s0 = -INFINITY;
+  if (has0) {
+    u32x4 kf[4];
+    load_k(lds_k, row, part, kf);
+    s0 = dot_q_k(qw, kf);
+  }
+  float m = s0;
+#pragma unroll
+  for (int i = 0; i < kMaxPosSlab; ++i) m = fmaxf(m, fmaxf(sp[i], sm[i]));
+
+  const size_t grow = slab * static_cast<size_t>(N) + row;
+  u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes + part * 64);
+  if (m == -INFINITY) {  // no key in the support of this row
+#pragma unroll
+    for (int t = 0; t < 4; ++t) orow[t] = u32x4{0u, 0u, 0u, 0u};
+    if (part == 0) a.lse[grow] = -INFINITY;
+    return;
+  }
+  // Pass 2: P = exp(scale (s - m)), accumulate P V in fp32.
+  const float c = a.scale_log2;
+  const float mc = m * c;
+  float l = 0.f;
+  float o[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) o[e] = 0.f;
+  accumulate_dir<+1>(lds_v, pos, n_plus, row, part, N, c, mc, sp, l, o);
+  accumulate_dir<-1>(lds_v, pos, n_minus, row, part, N, c, mc, sm, l, o);
+  if (has0) {
+    u32x4 vf[8];
+    load_v(lds_v, row, part, vf);
+    const float p = fast_exp2(__builtin_fmaf(s0, c, -mc));
+    l += p;
+    axpy_v(o, p, vf);
+  }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const __bf16 lo = static_cast<__bf16>(o[8 * t + 2 * u] * inv);
+      const __bf16 hi = static_cast<__bf16>(o[8 * t + 2 * u + 1] * inv);
+      w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    orow[t] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  if (part == 0) a.lse[grow] = (mc + fast_log2(l)) * kLn2;
+}
+
+// Thread 0: the head's distances, split into "0 is a distance" and the
+// ascending positive distances.
+__device__ __forceinline__ void build_positive(const HeadTable& ht, int h, int* dist, int* pos,
+                                               int* npos, int* has0) {
+  const int n = fib_offsets_gen(ht.a[h], ht.b[h], ht.lim[h], dist, kMaxOffsets);
+  const int m = n < kMaxOffsets ? n : kMaxOffsets;
+  const int z = (m > 0 && dist[0] == 0) ? 1 : 0;
+  int c = 0;
+  for (int i = z; i < m && c < kMaxPosSlab; ++i) pos[c++] = dist[i];
+  *npos = c;
+  for (int i = c; i < kMaxPosSlab; ++i) pos[i] = 0;  // defined padding
+  *has0 = z;
+}
+
+__global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_pos[kMaxPosSlab];
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ int s_npos, s_has0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int row = 32 * wave + (lane & 31);
+  const int part = lane >> 5;
+  const int N = a.N;
+  char* lds_k = smem;
+  char* lds_v = smem + N * kKStride;
+  // Rows of this wave: [32 w, min(32 w + 32, N)).
+  const int r0 = 32 * wave;
+  const int rl = (r0 + 31 < N ? r0 + 31 : N - 1);
+
+  Prefetch pf;
+  int slab = blockIdx.x;
+  if (slab < a.slabs) issue_prefetch(a, slab, tid, row, part, pf);
+  for (; slab < a.slabs; slab += gridDim.x) {
+    __syncthreads();  // the previous slab is no longer read from LDS
+    if (tid == 0) build_positive(a.ht, slab % a.H, s_dist, s_pos, &s_npos, &s_has0);
+    commit_prefetch(lds_k, lds_v, N, tid, pf);
+    u32x4 q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = pf.q[t];
+    __syncthreads();
+    const int next = slab + gridDim.x;
+    if (next < a.slabs) issue_prefetch(a, next, tid, row, part, pf);
+    if (r0 < N) {
+      // Displacements +f are useful to this wave while r0 + f < N, and -f
+      // while f <= rl; both are prefixes of the ascending distance list.
+      const int npos = __builtin_amdgcn_readfirstlane(s_npos);
+      int pos[kMaxPosSlab];
+      int n_plus = 0, n_minus = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxPosSlab; ++i) {
+        pos[i] = __builtin_amdgcn_readfirstlane(s_pos[i]);
+        if (i < npos) {
+          n_plus += (r0 + pos[i] < N) ? 1 : 0;
+          n_minus += (pos[i] <= rl) ? 1 : 0;
+        }
+      }
+      const bool has0 = __builtin_amdgcn_readfirstlane(s_has0) != 0;
+      if (row < N) attend_row(a, slab, row, part, lds_k, lds_v, pos, n_plus, n_minus, has0, q);
+    }
+  }
+}
+
+int cu_count() {
+  static int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return cus;
+  }();
+  return n;
+}
+
+}  // namespace
+
+bool fwd_slab_bf16_fits(const Problem& p) {
+  if (p.dtype != DType::kBF16 || p.D != 64 || p.N > kMaxRows) return false;
+  for (int h = 0; h < p.H; ++h) {
+    int32_t tmp[kMaxOffsets];
+    const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], tmp, kMaxOffsets);
+    int positive = 0;
+    for (int i = 0; i < n && i < kMaxOffsets; ++i) positive += tmp[i] > 0 ? 1 : 0;
+    if (positive > kMaxPosSlab) return false;
+  }
+  return true;
+}
+
+hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream) {
+  Args a;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.o = static_cast<char*>(o);
+  a.lse = lse;
+  a.H = p.H;
+  a.N = p.N;
+  a.slabs = p.B * p.H;
+  a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
+  a.ht = p.heads;
+  const size_t lds = static_cast<size_t>(p.N) * (kKStride + kVStride);
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_slab_bf16_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxRows * (kKStride + kVStride));
+  if (attr != hipSuccess) return attr;
+  int cus = cu_count();
+  if (cus <= 0) cus = 256;
+  const int grid = a.slabs < cus ? a.slabs : cus;
+  hipLaunchKernelGGL(fwd_slab_bf16_kernel, dim3(grid), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fibatt

@@ -21,7 +21,8 @@ struct Problem {
 // per CU fit in gfx950's 160 KiB).
 constexpr int kSlabLdsBudget = 80 * 1024;
 
-// Which kernels a problem runs on; exposed so tests can force either path.
+// Which kernels a problem runs on; exposed so tests can force a variant.
+// kAuto picks the fastest variant whose constraints the problem meets.
 enum class Path : int { kAuto = 0, kSlab = 1, kStream = 2 };
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
@@ -32,6 +33,11 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       float* workspace, hipStream_t stream, Path path);
 
 bool fwd_slab_fits(const Problem& p);
+
+// Persistent forward for bf16, d_h = 64, N <= 256 (the default when it fits).
+bool fwd_slab_bf16_fits(const Problem& p);
+hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream);
 bool bwd_slab_fits(const Problem& p);
 
 }  // namespace fibatt

@@ -108,7 +108,7 @@ def test_workload1_tiny_fp32(path):
         _set_path(None)
 
 
-@pytest.mark.parametrize("path", [None, "stream"])
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
 def test_workload2_vit_b(path):
     wl = workloads.WORKLOADS[2]
     _say(f"case: workload 2 {wl.name} path={path}")
@@ -167,9 +167,11 @@ EDGE = [
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
-@pytest.mark.parametrize("path", [None, "stream"])
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
 def test_edge_cases(case, path):
     name, B, H, N, d, dtype, ab, w = case
+    if path == "slab" and 2 * N * d * (2 if dtype == torch.bfloat16 else 4) + 8 * N > 80 * 1024:
+        pytest.skip("shape exceeds the LDS slab budget; the slab variant rejects it")
     _say(f"case: edge {name} B={B} H={H} N={N} d={d} {dtype} path={path}")
     _set_path(path)
     try:

@@ -35,6 +35,7 @@
 namespace fibatt {
 namespace {
 
+template <int MH>
 struct BwdArgs {
   const char* q;
   const char* k;
@@ -50,7 +51,7 @@ struct BwdArgs {
   int tiles;         // row tiles per slab (stream variant)
   float scale_log2;  // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
-  HeadTable ht;
+  HeadTableT<MH> ht;
 };
 
 template <int DL>
@@ -138,8 +139,8 @@ __device__ __forceinline__ void dkdv_row(int kr, int N, const int* deltas, int n
   }
 }
 
-template <typename T, int D, int G, int NT>
-__global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs a) {
+template <typename T, int D, int G, int NT, int MH>
+__global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_deltas[kMaxSigned];
@@ -212,8 +213,8 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs a) {
 }
 
 // Stream variant, query launch: dQ and D for a tile of query rows.
-template <typename T, int D, int G, int NT>
-__global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs a) {
+template <typename T, int D, int G, int NT, int MH>
+__global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
   __shared__ int s_dist[kMaxOffsets];
@@ -251,8 +252,8 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs a) {
 }
 
 // Stream variant, key launch: dK and dV for a tile of key rows.
-template <typename T, int D, int G, int NT>
-__global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs a) {
+template <typename T, int D, int G, int NT, int MH>
+__global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
   __shared__ int s_dist[kMaxOffsets];
@@ -300,14 +301,14 @@ constexpr int bwd_group() {
   return (D * static_cast<int>(sizeof(T))) / 64;
 }
 
-template <typename T, int D>
+template <typename T, int D, int MH>
 hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const void* v,
                         const float* lse, const void* dout, float* dq, float* dk, float* dv,
                         float* ws, hipStream_t stream, Path path) {
   constexpr int G = bwd_group<T, D>();
   constexpr int NT = 256;
   using Gm = Geom<T, D, G>;
-  BwdArgs a;
+  BwdArgs<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
@@ -321,13 +322,13 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
   a.N = p.N;
   a.scale = 1.0f / sqrtf(static_cast<float>(D));
   a.scale_log2 = kLog2e * a.scale;
-  a.ht = p.heads;
+  a.ht = shrink_heads<MH>(p.heads, p.H);
   const size_t slabs = static_cast<size_t>(p.B) * p.H;
   const bool slab_ok = bwd_slab_fits(p);
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes + 8 * static_cast<size_t>(p.N);
-    auto kern = bwd_slab_kernel<T, D, G, NT>;
+    auto kern = bwd_slab_kernel<T, D, G, NT, MH>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         kSlabLdsBudget);
@@ -338,11 +339,20 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
     const int per = NT / G;
     a.tiles = (p.N + per - 1) / per;
     const unsigned blocks = static_cast<unsigned>(slabs * a.tiles);
-    hipLaunchKernelGGL((bwd_dq_stream_kernel<T, D, G, NT>), dim3(blocks), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_stream_kernel<T, D, G, NT>), dim3(blocks), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_stream_kernel<T, D, G, NT, MH>), dim3(blocks), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_stream_kernel<T, D, G, NT, MH>), dim3(blocks), dim3(NT), 0, stream,
                        a);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_d(const Problem& p, const void* q, const void* k, const void* v,
+                        const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                        float* ws, hipStream_t stream, Path path) {
+  if (p.H <= kSmallHeads)
+    return launch_bwd_t<T, D, kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+  return launch_bwd_t<T, D, kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
 }
 
 }  // namespace
@@ -357,14 +367,14 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       float* ws, hipStream_t stream, Path path) {
   if (p.dtype == DType::kBF16) {
     if (p.D == 64)
-      return launch_bwd_t<bf16_t, 64>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+      return launch_bwd_d<bf16_t, 64>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
     if (p.D == 128)
-      return launch_bwd_t<bf16_t, 128>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+      return launch_bwd_d<bf16_t, 128>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
   } else {
     if (p.D == 64)
-      return launch_bwd_t<float, 64>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+      return launch_bwd_d<float, 64>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
     if (p.D == 128)
-      return launch_bwd_t<float, 128>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+      return launch_bwd_d<float, 128>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
   }
   return hipErrorInvalidValue;
 }

@@ -28,6 +28,7 @@
 namespace fibatt {
 namespace {
 
+template <int MH>
 struct FwdArgs {
   const char* q;
   const char* k;
@@ -38,7 +39,7 @@ struct FwdArgs {
   int N;
   int tiles;          // query tiles per slab (stream variant)
   float scale_log2;   // log2(e) / sqrt(d)
-  HeadTable ht;
+  HeadTableT<MH> ht;
 };
 
 template <typename T, int D, int G>
@@ -114,8 +115,8 @@ __device__ __forceinline__ void attend_row(const KV& kv, int j, int N, int part,
 }
 
 // Normalise and write O (in T) and LSE (natural log) for row j.
-template <typename T, int D, int G>
-__device__ __forceinline__ void finish_row(const FwdArgs& a, size_t slab, int j, int part,
+template <typename T, int D, int G, typename Args>
+__device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, int part,
                                            float (&acc)[Geom<T, D, G>::kDL], float m, float l) {
   using Gm = Geom<T, D, G>;
   const bool has = l > 0.f;
@@ -142,8 +143,8 @@ __device__ __forceinline__ void finish_row(const FwdArgs& a, size_t slab, int j,
   if (part == 0) a.lse[slab * a.N + j] = has ? (m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D, int G, int NT, int C>
-__global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs a) {
+template <typename T, int D, int G, int NT, int C, int MH>
+__global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_deltas[kMaxSigned];
@@ -175,8 +176,8 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int G, int NT, int C>
-__global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs a) {
+template <typename T, int D, int G, int NT, int C, int MH>
+__global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
   __shared__ int s_dist[kMaxOffsets];
@@ -209,14 +210,14 @@ constexpr int fwd_group() {
   return (D * static_cast<int>(sizeof(T))) / 128;
 }
 
-template <typename T, int D>
+template <typename T, int D, int MH>
 hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                         float* lse, hipStream_t stream, Path path) {
   constexpr int G = fwd_group<T, D>();
   constexpr int NT = 256;
   constexpr int C = 8;
   using Gm = Geom<T, D, G>;
-  FwdArgs a;
+  FwdArgs<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
@@ -225,13 +226,13 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   a.H = p.H;
   a.N = p.N;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-  a.ht = p.heads;
+  a.ht = shrink_heads<MH>(p.heads, p.H);
   const size_t slabs = static_cast<size_t>(p.B) * p.H;
   const bool slab_ok = fwd_slab_fits(p);
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes;
-    auto kern = fwd_slab_kernel<T, D, G, NT, C>;
+    auto kern = fwd_slab_kernel<T, D, G, NT, C, MH>;
     // Opt the kernel into the full slab budget once per process.
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -242,10 +243,18 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   } else {
     const int rows = NT / G;
     a.tiles = (p.N + rows - 1) / rows;
-    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C>),
+    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C, MH>),
                        dim3(static_cast<unsigned>(slabs * a.tiles)), dim3(NT), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_d(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                        float* lse, hipStream_t stream, Path path) {
+  if (p.H <= kSmallHeads)
+    return launch_fwd_t<T, D, kSmallHeads>(p, q, k, v, o, lse, stream, path);
+  return launch_fwd_t<T, D, kMaxHeads>(p, q, k, v, o, lse, stream, path);
 }
 
 }  // namespace
@@ -260,11 +269,11 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
   if (path == Path::kAuto && fwd_slab_bf16_fits(p))
     return launch_fwd_slab_bf16(p, q, k, v, o, lse, stream);
   if (p.dtype == DType::kBF16) {
-    if (p.D == 64) return launch_fwd_t<bf16_t, 64>(p, q, k, v, o, lse, stream, path);
-    if (p.D == 128) return launch_fwd_t<bf16_t, 128>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 64) return launch_fwd_d<bf16_t, 64>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 128) return launch_fwd_d<bf16_t, 128>(p, q, k, v, o, lse, stream, path);
   } else {
-    if (p.D == 64) return launch_fwd_t<float, 64>(p, q, k, v, o, lse, stream, path);
-    if (p.D == 128) return launch_fwd_t<float, 128>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 64) return launch_fwd_d<float, 64>(p, q, k, v, o, lse, stream, path);
+    if (p.D == 128) return launch_fwd_d<float, 128>(p, q, k, v, o, lse, stream, path);
   }
   return hipErrorInvalidValue;
 }

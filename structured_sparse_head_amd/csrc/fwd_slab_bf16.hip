@@ -46,6 +46,10 @@ constexpr int kVStride = 272;        // bytes per fp32 V row in LDS (256 + 16)
 constexpr int kRowBytes = 128;       // bf16 row of 64 elements in HBM
 constexpr int kChunksPerThread = kMaxRows * (kRowBytes / 16) / kThreads;  // 4
 
+// Per-head record: bytes 0..11 the ascending positive distances, byte 12
+// their count, byte 13 whether 0 is a distance.  Built on the host; with at
+// most 16 heads the whole table is 256 bytes of kernel arguments.
+template <int MH>
 struct Args {
   const char* q;
   const char* k;
@@ -56,7 +60,7 @@ struct Args {
   int N;
   int slabs;
   float scale_log2;
-  HeadTable ht;
+  u32x4 rec[MH];
 };
 
 struct Prefetch {
@@ -67,7 +71,8 @@ struct Prefetch {
 
 // Loads are unconditional (indices clamped into the slab) so that every
 // prefetch register is overwritten each time; only the LDS commit is masked.
-__device__ __forceinline__ void issue_prefetch(const Args& a, size_t slab, int tid, int row,
+template <typename A>
+__device__ __forceinline__ void issue_prefetch(const A& a, size_t slab, int tid, int row,
                                                int part, Prefetch& pf) {
   const size_t base = slab * static_cast<size_t>(a.N) * kRowBytes;
   const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
@@ -193,7 +198,8 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&po
   }
 }
 
-__device__ __forceinline__ void attend_row(const Args& a, size_t slab, int row, int part,
+template <typename A>
+__device__ __forceinline__ void attend_row(const A& a, size_t slab, int row, int part,
                                            const char* lds_k, const char* lds_v,
                                            const int (&pos)[kMaxPosSlab], int n_plus, int n_minus,
                                            bool has0, const u32x4 (&q)[4]) {
@@ -260,25 +266,9 @@ __device__ __forceinline__ void attend_row(const Args& a, size_t slab, int row, 
   if (part == 0) a.lse[grow] = (mc + fast_log2(l)) * kLn2;
 }
 
-// Thread 0: the head's distances, split into "0 is a distance" and the
-// ascending positive distances.
-__device__ __forceinline__ void build_positive(const HeadTable& ht, int h, int* dist, int* pos,
-                                               int* npos, int* has0) {
-  const int n = fib_offsets_gen(ht.a[h], ht.b[h], ht.lim[h], dist, kMaxOffsets);
-  const int m = n < kMaxOffsets ? n : kMaxOffsets;
-  const int z = (m > 0 && dist[0] == 0) ? 1 : 0;
-  int c = 0;
-  for (int i = z; i < m && c < kMaxPosSlab; ++i) pos[c++] = dist[i];
-  *npos = c;
-  for (int i = c; i < kMaxPosSlab; ++i) pos[i] = 0;  // defined padding
-  *has0 = z;
-}
-
-__global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args a) {
+template <int MH>
+__global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int s_pos[kMaxPosSlab];
-  __shared__ int s_dist[kMaxOffsets];
-  __shared__ int s_npos, s_has0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -296,7 +286,6 @@ __global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args a) {
   if (slab < a.slabs) issue_prefetch(a, slab, tid, row, part, pf);
   for (; slab < a.slabs; slab += gridDim.x) {
     __syncthreads();  // the previous slab is no longer read from LDS
-    if (tid == 0) build_positive(a.ht, slab % a.H, s_dist, s_pos, &s_npos, &s_has0);
     commit_prefetch(lds_k, lds_v, N, tid, pf);
     u32x4 q[4];
 #pragma unroll
@@ -305,20 +294,22 @@ __global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args a) {
     const int next = slab + gridDim.x;
     if (next < a.slabs) issue_prefetch(a, next, tid, row, part, pf);
     if (r0 < N) {
+      const u32x4 rec = a.rec[slab % a.H];
+      const uint32_t rw[4] = {rec.x, rec.y, rec.z, rec.w};
+      const int npos = static_cast<int>(rw[3] & 0xffu);
+      const bool has0 = ((rw[3] >> 8) & 0xffu) != 0;
       // Displacements +f are useful to this wave while r0 + f < N, and -f
       // while f <= rl; both are prefixes of the ascending distance list.
-      const int npos = __builtin_amdgcn_readfirstlane(s_npos);
       int pos[kMaxPosSlab];
       int n_plus = 0, n_minus = 0;
 #pragma unroll
       for (int i = 0; i < kMaxPosSlab; ++i) {
-        pos[i] = __builtin_amdgcn_readfirstlane(s_pos[i]);
+        pos[i] = static_cast<int>((rw[i >> 2] >> (8 * (i & 3))) & 0xffu);
         if (i < npos) {
           n_plus += (r0 + pos[i] < N) ? 1 : 0;
           n_minus += (pos[i] <= rl) ? 1 : 0;
         }
       }
-      const bool has0 = __builtin_amdgcn_readfirstlane(s_has0) != 0;
       if (row < N) attend_row(a, slab, row, part, lds_k, lds_v, pos, n_plus, n_minus, has0, q);
     }
   }
@@ -337,21 +328,31 @@ int cu_count() {
 
 }  // namespace
 
-bool fwd_slab_bf16_fits(const Problem& p) {
-  if (p.dtype != DType::kBF16 || p.D != 64 || p.N > kMaxRows) return false;
-  for (int h = 0; h < p.H; ++h) {
-    int32_t tmp[kMaxOffsets];
-    const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], tmp, kMaxOffsets);
-    int positive = 0;
-    for (int i = 0; i < n && i < kMaxOffsets; ++i) positive += tmp[i] > 0 ? 1 : 0;
-    if (positive > kMaxPosSlab) return false;
+namespace {
+
+// Positive distances of head h (ascending), or -1 when the head has more
+// than the kernel's per-head capacity.
+int positive_distances(const Problem& p, int h, int (&pos)[kMaxPosSlab], bool& has0) {
+  int32_t dist[kMaxOffsets];
+  const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], dist, kMaxOffsets);
+  if (n > kMaxOffsets) return -1;
+  has0 = false;
+  int c = 0;
+  for (int i = 0; i < n; ++i) {
+    if (dist[i] == 0) {
+      has0 = true;
+      continue;
+    }
+    if (c == kMaxPosSlab) return -1;
+    pos[c++] = dist[i];
   }
-  return true;
+  return c;
 }
 
-hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                                void* o, float* lse, hipStream_t stream) {
-  Args a;
+template <int MH>
+hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, hipStream_t stream) {
+  Args<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
@@ -361,17 +362,47 @@ hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, 
   a.N = p.N;
   a.slabs = p.B * p.H;
   a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
-  a.ht = p.heads;
+  for (int h = 0; h < MH; ++h) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (h < p.H) {
+      int pos[kMaxPosSlab];
+      bool has0 = false;
+      const int n = positive_distances(p, h, pos, has0);
+      if (n < 0) return hipErrorInvalidValue;
+      for (int i = 0; i < n; ++i) w[i >> 2] |= static_cast<uint32_t>(pos[i]) << (8 * (i & 3));
+      w[3] |= static_cast<uint32_t>(n) | (has0 ? 0x100u : 0u);
+    }
+    a.rec[h] = u32x4{w[0], w[1], w[2], w[3]};
+  }
   const size_t lds = static_cast<size_t>(p.N) * (kKStride + kVStride);
+  auto kern = fwd_slab_bf16_kernel<MH>;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_slab_bf16_kernel),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxRows * (kKStride + kVStride));
   if (attr != hipSuccess) return attr;
   int cus = cu_count();
   if (cus <= 0) cus = 256;
   const int grid = a.slabs < cus ? a.slabs : cus;
-  hipLaunchKernelGGL(fwd_slab_bf16_kernel, dim3(grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_slab_bf16_fits(const Problem& p) {
+  if (p.dtype != DType::kBF16 || p.D != 64 || p.N > kMaxRows) return false;
+  for (int h = 0; h < p.H; ++h) {
+    int pos[kMaxPosSlab];
+    bool has0 = false;
+    if (positive_distances(p, h, pos, has0) < 0) return false;
+  }
+  return true;
+}
+
+hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream) {
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace fibatt

@@ -18,12 +18,28 @@ namespace fibatt {
 constexpr int kMaxHeads = 128;
 constexpr int kMaxSigned = 2 * kMaxOffsets;
 
-// Per-head sequence parameters handed to every kernel by value.
-struct HeadTable {
-  int32_t a[kMaxHeads];
-  int32_t b[kMaxHeads];
-  int32_t lim[kMaxHeads];  // min(w, N - 1)
+// Per-head sequence parameters handed to every kernel by value.  Kernel
+// arguments are copied at every launch, so kernels are instantiated for a
+// small table (up to 16 heads, ~200 bytes) and for the full one.
+template <int MH>
+struct HeadTableT {
+  int32_t a[MH];
+  int32_t b[MH];
+  int32_t lim[MH];  // min(w, N - 1)
 };
+using HeadTable = HeadTableT<kMaxHeads>;
+constexpr int kSmallHeads = 16;
+
+template <int MH>
+HeadTableT<MH> shrink_heads(const HeadTable& t, int H) {
+  HeadTableT<MH> r{};
+  for (int h = 0; h < H && h < MH; ++h) {
+    r.a[h] = t.a[h];
+    r.b[h] = t.b[h];
+    r.lim[h] = t.lim[h];
+  }
+  return r;
+}
 
 using bf16_t = uint16_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -19,6 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -48,6 +49,40 @@ def _bytes(wl, esize):
     fwd = rows * (4 * row + 4)
     bwd = rows * (4 * row + 4 + 3 * wl.d * 4)
     return int(fwd), int(bwd)
+
+
+# Dominant kernel on this workload for each pass, and the source files whose
+# hash identifies the build its HBM counters were taken on.
+KERNELS = {
+    "fwd": ("fwd_slab_bf16_kernel", ["fwd_slab_bf16.hip"]),
+    "bwd": ("bwd_slab_kernel", ["bwd.hip"]),
+}
+
+
+def _source_hash(files):
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "structured_sparse_head_amd", "csrc")
+    for f in files + ["kernel_common.h", "fib_offsets.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(pass_name):
+    """HBM bytes per dispatch (read + write) of the pass's kernel from the
+    committed counter summary, or None when the kernel source has changed
+    since the counters were taken."""
+    name, files = KERNELS[pass_name]
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    want = _source_hash(files)
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 4 and f[0] == name and f[1] == want:
+                return int(f[2]) + int(f[3])
+    return None
 
 
 def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0):
@@ -211,14 +246,13 @@ def main():
         "wall_s_timed": wall,
         "kernels": kernels,
         "roofline": {
-            "kernel": f"{dom} ({'bwd_slab_kernel' if dom == 'bwd' else 'fwd_slab_bf16_kernel'} "
-                      "on this workload)",
+            "kernel": f"{KERNELS[dom][0]} ({dom} pass)",
             "bound": "hbm",
             "achieved": ach,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(dom),
         },
     }
     if not args.no_cpu_baseline:

@@ -7,19 +7,9 @@
 // section, eq. (1) and (3); README Algorithm 3): scores Q_j . K_k / sqrt(d)
 // on the head's support, a row softmax, P V.  Design points:
 //
-//  * Lanes.  Two lanes own a query row, each holding 32 of its 64 elements:
-//    lanes 0-31 of a wave take the first halves of 32 consecutive rows and
-//    lanes 32-63 the second halves, so one v_permlane32_swap plus one add
-//    completes a dot product.
-//  * LDS layout.  K rows are kept in bf16 with a 144-byte stride and V rows
-//    in fp32 (converted once while staging) with a 272-byte stride, both an
-//    odd number of 16-byte units, and one base address plus immediate
-//    offsets reaches a whole fragment.  Measured on gfx950 (64 banks), a
-//    ds_read_b128 serves the two 32-lane halves of a wave separately and,
-//    within a half, the lane quads whose index has even popcount
-//    ({0-3, 12-15, 20-23, 24-27}) together and the odd ones together.  Each
-//    such group then reads 16 rows that are distinct modulo 16, and an odd
-//    stride maps them to 16 distinct 16-byte bank groups: no conflicts.
+//  * Lanes and LDS strides as in slab_bf16_common.h.  K rows are kept in
+//    bf16 and V rows in fp32 (converted once while staging), so P V needs
+//    no conversions.
 //  * Softmax.  All scores of a row (at most 12 distances, each signed, plus
 //    0, for N <= 256) stay in registers: one pass forms them, the row
 //    maximum is taken once, a second pass exponentiates and accumulates P V
@@ -32,19 +22,12 @@
 //  * Overlap.  While a slab is computed from LDS, each thread already holds
 //    the next slab's K, V chunks and its own Q fragment in flight in
 //    registers; they are committed to LDS after the next barrier.
-#include "kernel_common.h"
-#include "launch.h"
+#include "slab_bf16_common.h"
 
 namespace fibatt {
 namespace {
 
-constexpr int kThreads = 512;        // 8 waves; 256 query rows at 2 lanes per row
-constexpr int kMaxRows = kThreads / 2;
-constexpr int kMaxPosSlab = 12;      // positive distances below 256: at most 1,2,3,5,...,233
-constexpr int kKStride = 144;        // bytes per bf16 K row in LDS (128 + 16)
-constexpr int kVStride = 272;        // bytes per fp32 V row in LDS (256 + 16)
-constexpr int kRowBytes = 128;       // bf16 row of 64 elements in HBM
-constexpr int kChunksPerThread = kMaxRows * (kRowBytes / 16) / kThreads;  // 4
+using namespace slab;
 
 // Per-head record: bytes 0..11 the ascending positive distances, byte 12
 // their count, byte 13 whether 0 is a distance.  Built on the host; with at
@@ -101,99 +84,56 @@ __device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, int N,
     if (idx < chunks) {
       const int r = idx >> 3;
       const int ch = idx & 7;
-      *reinterpret_cast<u32x4*>(lds_k + r * kKStride + ch * 16) = pf.k[c];
+      *reinterpret_cast<u32x4*>(lds_k + r * kBf16Stride + ch * 16) = pf.k[c];
       const u32x4 x = pf.v[c];
       const u32x4 lo = {x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
       const u32x4 hi = {x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
-      *reinterpret_cast<u32x4*>(lds_v + r * kVStride + ch * 32) = lo;
-      *reinterpret_cast<u32x4*>(lds_v + r * kVStride + ch * 32 + 16) = hi;
+      *reinterpret_cast<u32x4*>(lds_v + r * kF32Stride + ch * 32) = lo;
+      *reinterpret_cast<u32x4*>(lds_v + r * kF32Stride + ch * 32 + 16) = hi;
     }
   }
 }
 
-// Sum of x over the lane pair (l, l ^ 32).
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void load_k(const char* lds_k, int kk, int part, u32x4 (&f)[4]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(lds_k + __umul24(kk, kKStride) + part * 64);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) f[t] = p[t];
-}
-
-__device__ __forceinline__ void load_v(const char* lds_v, int kk, int part, u32x4 (&f)[8]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(lds_v + __umul24(kk, kVStride) + part * 128);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) f[t] = p[t];
-}
-
-__device__ __forceinline__ float dot_q_k(const uint32_t (&qw)[16], const u32x4 (&k)[4]) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t kw[4] = {k[t].x, k[t].y, k[t].z, k[t].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[4 * t + u]),
-                                               __builtin_bit_cast(bf16x2_t, kw[u]), acc[u], false);
-  }
-  return pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-}
-
-__device__ __forceinline__ void axpy_v(float (&o)[32], float p, const u32x4 (&v)[8]) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    o[4 * t + 0] = __builtin_fmaf(p, __uint_as_float(v[t].x), o[4 * t + 0]);
-    o[4 * t + 1] = __builtin_fmaf(p, __uint_as_float(v[t].y), o[4 * t + 1]);
-    o[4 * t + 2] = __builtin_fmaf(p, __uint_as_float(v[t].z), o[4 * t + 2]);
-    o[4 * t + 3] = __builtin_fmaf(p, __uint_as_float(v[t].w), o[4 * t + 3]);
-  }
-}
-
-__device__ __forceinline__ int clamp_row(int r, int N) { return r < 0 ? 0 : (r >= N ? N - 1 : r); }
 
 // Scores for displacements sgn * pos[i], i < n (wave-uniform n).  Out-of-range
 // keys are read from a clamped row and scored -inf.  The next key fragment is
 // requested before the current dot product so LDS latency overlaps arithmetic.
 template <int SGN>
-__device__ __forceinline__ void scores_dir(const char* lds_k, const int (&pos)[kMaxPosSlab], int n,
+__device__ __forceinline__ void scores_dir(const char* lds_k, const int (&pos)[kMaxPos], int n,
                                            int row, int part, int N, const uint32_t (&qw)[16],
-                                           float (&s)[kMaxPosSlab]) {
+                                           float (&s)[kMaxPos]) {
   u32x4 kb[2][4];
-  if (n > 0) load_k(lds_k, clamp_row(row + SGN * pos[0], N), part, kb[0]);
+  if (n > 0) load_bf16_half(lds_k, clamp_row(row + SGN * pos[0], N), part, kb[0]);
 #pragma unroll
-  for (int i = 0; i < kMaxPosSlab; ++i) {
+  for (int i = 0; i < kMaxPos; ++i) {
     s[i] = -INFINITY;
     if (i < n) {
-      if (i + 1 < kMaxPosSlab && i + 1 < n)
-        load_k(lds_k, clamp_row(row + SGN * pos[i + 1 < kMaxPosSlab ? i + 1 : i], N), part,
+      if (i + 1 < kMaxPos && i + 1 < n)
+        load_bf16_half(lds_k, clamp_row(row + SGN * pos[i + 1 < kMaxPos ? i + 1 : i], N), part,
                kb[(i + 1) & 1]);
       const int kk = row + SGN * pos[i];
-      const float d = dot_q_k(qw, kb[i & 1]);
+      const float d = dot_bf16(qw, kb[i & 1]);
       s[i] = (static_cast<unsigned>(kk) < static_cast<unsigned>(N)) ? d : -INFINITY;
     }
   }
 }
 
 template <int SGN>
-__device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&pos)[kMaxPosSlab],
+__device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&pos)[kMaxPos],
                                                int n, int row, int part, int N, float c, float mc,
-                                               const float (&s)[kMaxPosSlab], float& l,
+                                               const float (&s)[kMaxPos], float& l,
                                                float (&o)[32]) {
   u32x4 vb[2][8];
-  if (n > 0) load_v(lds_v, clamp_row(row + SGN * pos[0], N), part, vb[0]);
+  if (n > 0) load_f32_half(lds_v, clamp_row(row + SGN * pos[0], N), part, vb[0]);
 #pragma unroll
-  for (int i = 0; i < kMaxPosSlab; ++i) {
+  for (int i = 0; i < kMaxPos; ++i) {
     if (i < n) {
-      if (i + 1 < kMaxPosSlab && i + 1 < n)
-        load_v(lds_v, clamp_row(row + SGN * pos[i + 1 < kMaxPosSlab ? i + 1 : i], N), part,
+      if (i + 1 < kMaxPos && i + 1 < n)
+        load_f32_half(lds_v, clamp_row(row + SGN * pos[i + 1 < kMaxPos ? i + 1 : i], N), part,
                vb[(i + 1) & 1]);
       const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
       l += p;
-      axpy_v(o, p, vb[i & 1]);
+      axpy_f32(o, p, vb[i & 1]);
     }
   }
 }
@@ -201,7 +141,7 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&po
 template <typename A>
 __device__ __forceinline__ void attend_row(const A& a, size_t slab, int row, int part,
                                            const char* lds_k, const char* lds_v,
-                                           const int (&pos)[kMaxPosSlab], int n_plus, int n_minus,
+                                           const int (&pos)[kMaxPos], int n_plus, int n_minus,
                                            bool has0, const u32x4 (&q)[4]) {
   const int N = a.N;
   uint32_t qw[16];
@@ -213,18 +153,18 @@ __device__ __forceinline__ void attend_row(const A& a, size_t slab, int row, int
     qw[4 * t + 3] = q[t].w;
   }
   // Pass 1: raw scores Q_j . K_k for every signed displacement.
-  float sp[kMaxPosSlab], sm[kMaxPosSlab];
+  float sp[kMaxPos], sm[kMaxPos];
   scores_dir<+1>(lds_k, pos, n_plus, row, part, N, qw, sp);
   scores_dir<-1>(lds_k, pos, n_minus, row, part, N, qw, sm);
   float s0 = -INFINITY;
   if (has0) {
     u32x4 kf[4];
-    load_k(lds_k, row, part, kf);
-    s0 = dot_q_k(qw, kf);
+    load_bf16_half(lds_k, row, part, kf);
+    s0 = dot_bf16(qw, kf);
   }
   float m = s0;
 #pragma unroll
-  for (int i = 0; i < kMaxPosSlab; ++i) m = fmaxf(m, fmaxf(sp[i], sm[i]));
+  for (int i = 0; i < kMaxPos; ++i) m = fmaxf(m, fmaxf(sp[i], sm[i]));
 
   const size_t grow = slab * static_cast<size_t>(N) + row;
   u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes + part * 64);
@@ -245,10 +185,10 @@ __device__ __forceinline__ void attend_row(const A& a, size_t slab, int row, int
   accumulate_dir<-1>(lds_v, pos, n_minus, row, part, N, c, mc, sm, l, o);
   if (has0) {
     u32x4 vf[8];
-    load_v(lds_v, row, part, vf);
+    load_f32_half(lds_v, row, part, vf);
     const float p = fast_exp2(__builtin_fmaf(s0, c, -mc));
     l += p;
-    axpy_v(o, p, vf);
+    axpy_f32(o, p, vf);
   }
   const float inv = 1.0f / l;
 #pragma unroll
@@ -276,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args<MH> a) {
   const int part = lane >> 5;
   const int N = a.N;
   char* lds_k = smem;
-  char* lds_v = smem + N * kKStride;
+  char* lds_v = smem + N * kBf16Stride;
   // Rows of this wave: [32 w, min(32 w + 32, N)).
   const int r0 = 32 * wave;
   const int rl = (r0 + 31 < N ? r0 + 31 : N - 1);
@@ -294,59 +234,21 @@ __global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args<MH> a) {
     const int next = slab + gridDim.x;
     if (next < a.slabs) issue_prefetch(a, next, tid, row, part, pf);
     if (r0 < N) {
-      const u32x4 rec = a.rec[slab % a.H];
-      const uint32_t rw[4] = {rec.x, rec.y, rec.z, rec.w};
-      const int npos = static_cast<int>(rw[3] & 0xffu);
-      const bool has0 = ((rw[3] >> 8) & 0xffu) != 0;
+      const HeadRecord hr = unpack_record(a.rec[slab % a.H]);
       // Displacements +f are useful to this wave while r0 + f < N, and -f
       // while f <= rl; both are prefixes of the ascending distance list.
-      int pos[kMaxPosSlab];
       int n_plus = 0, n_minus = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxPosSlab; ++i) {
-        pos[i] = static_cast<int>((rw[i >> 2] >> (8 * (i & 3))) & 0xffu);
-        if (i < npos) {
-          n_plus += (r0 + pos[i] < N) ? 1 : 0;
-          n_minus += (pos[i] <= rl) ? 1 : 0;
+      for (int i = 0; i < kMaxPos; ++i) {
+        if (i < hr.npos) {
+          n_plus += (r0 + hr.pos[i] < N) ? 1 : 0;
+          n_minus += (hr.pos[i] <= rl) ? 1 : 0;
         }
       }
-      if (row < N) attend_row(a, slab, row, part, lds_k, lds_v, pos, n_plus, n_minus, has0, q);
+      if (row < N)
+        attend_row(a, slab, row, part, lds_k, lds_v, hr.pos, n_plus, n_minus, hr.has0, q);
     }
   }
-}
-
-int cu_count() {
-  static int n = [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    return cus;
-  }();
-  return n;
-}
-
-}  // namespace
-
-namespace {
-
-// Positive distances of head h (ascending), or -1 when the head has more
-// than the kernel's per-head capacity.
-int positive_distances(const Problem& p, int h, int (&pos)[kMaxPosSlab], bool& has0) {
-  int32_t dist[kMaxOffsets];
-  const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], dist, kMaxOffsets);
-  if (n > kMaxOffsets) return -1;
-  has0 = false;
-  int c = 0;
-  for (int i = 0; i < n; ++i) {
-    if (dist[i] == 0) {
-      has0 = true;
-      continue;
-    }
-    if (c == kMaxPosSlab) return -1;
-    pos[c++] = dist[i];
-  }
-  return c;
 }
 
 template <int MH>
@@ -362,26 +264,14 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.N = p.N;
   a.slabs = p.B * p.H;
   a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
-  for (int h = 0; h < MH; ++h) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (h < p.H) {
-      int pos[kMaxPosSlab];
-      bool has0 = false;
-      const int n = positive_distances(p, h, pos, has0);
-      if (n < 0) return hipErrorInvalidValue;
-      for (int i = 0; i < n; ++i) w[i >> 2] |= static_cast<uint32_t>(pos[i]) << (8 * (i & 3));
-      w[3] |= static_cast<uint32_t>(n) | (has0 ? 0x100u : 0u);
-    }
-    a.rec[h] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-  const size_t lds = static_cast<size_t>(p.N) * (kKStride + kVStride);
+  if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(p.N) * (kBf16Stride + kF32Stride);
   auto kern = fwd_slab_bf16_kernel<MH>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxRows * (kKStride + kVStride));
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxRows * (kBf16Stride + kF32Stride));
   if (attr != hipSuccess) return attr;
-  int cus = cu_count();
-  if (cus <= 0) cus = 256;
+  const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
@@ -390,13 +280,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
 }  // namespace
 
 bool fwd_slab_bf16_fits(const Problem& p) {
-  if (p.dtype != DType::kBF16 || p.D != 64 || p.N > kMaxRows) return false;
-  for (int h = 0; h < p.H; ++h) {
-    int pos[kMaxPosSlab];
-    bool has0 = false;
-    if (positive_distances(p, h, pos, has0) < 0) return false;
-  }
-  return true;
+  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kMaxRows && records_fit(p);
 }
 
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,

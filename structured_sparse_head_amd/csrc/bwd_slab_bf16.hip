@@ -31,13 +31,14 @@ using namespace slab;
 
 constexpr int kTableCols = 2 * kMaxPos + 1;  // +f (0..11), -f (12..23), 0 (24)
 
-// LDS: per sequence row, fp32 Q and dO rows (which also cover the bf16 K, V
-// rows of the earlier passes); then the (P, dS) table with one row per lane
-// pair (kMaxRows), so lanes past the last sequence row own private rows.
-constexpr int kLdsPerRow = 2 * kF32Stride;
+// LDS: per sequence row, bf16 K and V plus an fp32 copy of K for the query
+// and dQ passes, later overlaid by fp32 Q and dO rows for the key passes;
+// then the (P, dS) table with one row per lane pair (kMaxRows), so lanes past
+// the last sequence row own private rows.
+constexpr int kLdsPerRow = 2 * kBf16Stride + kF32Stride;  // >= 2 * kF32Stride
 constexpr int kTableBytes = kMaxRows * kTableCols * 8;
 constexpr int kLdsMax = 160 * 1024;
-constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 207
+constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 201
 
 template <int MH>
 struct Args {
@@ -104,7 +105,7 @@ __device__ __forceinline__ void settle(const Prefetch& pf) {
   asm volatile("" ::"v"(pf.lse));
 }
 
-__device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, int N, int tid,
+__device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, char* lds_kf, int N, int tid,
                                           const Prefetch& pf) {
   const int chunks = N * (kRowBytes / 16);
 #pragma unroll
@@ -114,6 +115,11 @@ __device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, int N, int t
       const int off = (idx >> 3) * kBf16Stride + (idx & 7) * 16;
       *reinterpret_cast<u32x4*>(lds_k + off) = pf.k[c];
       *reinterpret_cast<u32x4*>(lds_v + off) = pf.v[c];
+      const u32x4 x = pf.k[c];
+      char* kf = lds_kf + (idx >> 3) * kF32Stride + (idx & 7) * 32;
+      *reinterpret_cast<u32x4*>(kf) = u32x4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
+      *reinterpret_cast<u32x4*>(kf + 16) =
+          u32x4{x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
     }
   }
 }
@@ -203,27 +209,30 @@ __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v,
 // dQ pass: dS = P (dP - D) from the row's table entries, acc += dS K; the
 // entry becomes (P, dS / sqrt(d)) for the key pass.
 template <int SGN>
-__device__ __forceinline__ void dq_pass(const char* lds_k, float2* tbl, Dist dist, int n, int row,
+__device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist dist, int n, int row,
                                         int trow, int N, int part, float d, float scale, int base,
                                         bool wr, float (&acc)[32]) {
-  u32x4 ka[4], kb[4];
-  auto load = [&](int i, u32x4 (&kf)[4]) {
-    load_bf16_half(lds_k, clamp_row(row + SGN * dist.at(i), N), part, kf);
+  // The step's table entry is fetched with its fp32 K fragment, one step
+  // ahead.
+  u32x4 ka[8], kb[8];
+  float2 ea, eb;
+  float2* e0 = tbl + trow * kTableCols + base;
+  auto load = [&](int i, u32x4 (&kf)[8], float2& e) {
+    load_f32_half(lds_kf, clamp_row(row + SGN * dist.at(i), N), part, kf);
+    e = e0[i];
   };
-  auto step = [&](int i, const u32x4 (&kf)[4]) {
-    float2* e = tbl + trow * kTableCols + base + i;
-    const float2 t = *e;
-    const float ds = t.x * (t.y - d);
-    axpy_bf16(acc, ds, kf);
-    if (wr) *e = make_float2(t.x, ds * scale);
+  auto step = [&](int i, const u32x4 (&kf)[8], const float2& e) {
+    const float ds = e.x * (e.y - d);
+    axpy_f32(acc, ds, kf);
+    if (wr) e0[i] = make_float2(e.x, ds * scale);
   };
-  if (n > 0) load(0, ka);
+  if (n > 0) load(0, ka, ea);
   for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(i + 1, kb);
-    step(i, ka);
+    if (i + 1 < n) load(i + 1, kb, eb);
+    step(i, ka, ea);
     if (i + 1 < n) {
-      if (i + 2 < n) load(i + 2, ka);
-      step(i + 1, kb);
+      if (i + 2 < n) load(i + 2, ka, ea);
+      step(i + 1, kb, eb);
     }
   }
 }
@@ -235,17 +244,30 @@ template <int SGN, int C, typename Tick>
 __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, Dist dist, int n,
                                          int k, int N, int part, int base, float (&acc)[32],
                                          Tick& tk) {
-  auto step = [&](int i) {
-    u32x4 xf[8];
+  // Row and weight of a step are fetched together, one step ahead.
+  u32x4 xa[8], xb[8];
+  float wa, wb;
+  auto load = [&](int i, u32x4 (&xf)[8], float& w) {
     const int j = k - SGN * dist.at(i);
-    load_f32_half(lds_x, clamp_row(j, N), part, xf);
+    const int jc = clamp_row(j, N);
+    load_f32_half(lds_x, jc, part, xf);
+    const float2 t = tbl[jc * kTableCols + base + i];
     const bool ok = static_cast<unsigned>(j) < static_cast<unsigned>(N);
-    const float2 t = tbl[clamp_row(j, N) * kTableCols + base + i];
-    const float w = C == 0 ? t.x : t.y;
-    tk.tick();
-    axpy_f32(acc, ok ? w : 0.f, xf);
+    w = ok ? (C == 0 ? t.x : t.y) : 0.f;
   };
-  for (int i = 0; i < n; ++i) step(i);
+  auto step = [&](const u32x4 (&xf)[8], float w) {
+    tk.tick();
+    axpy_f32(acc, w, xf);
+  };
+  if (n > 0) load(0, xa, wa);
+  for (int i = 0; i < n; i += 2) {
+    if (i + 1 < n) load(i + 1, xb, wb);
+    step(xa, wa);
+    if (i + 1 < n) {
+      if (i + 2 < n) load(i + 2, xa, wa);
+      step(xb, wb);
+    }
+  }
 }
 
 template <int MH>
@@ -254,8 +276,8 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int row = 32 * wave + (lane & 31);
-  const int part = lane >> 5;
+  const int row0 = 32 * wave + (lane & 31);
+  const int part0 = lane >> 5;
   const int r0 = 32 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are
@@ -264,18 +286,21 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
   // loads, never for the stores issued after them).
   Prefetch pf;
   int slab = blockIdx.x;
-  issue_prefetch(a, a.N, slab, tid, row, part, false, pf);
+  issue_prefetch(a, a.N, slab, tid, row0, part0, false, pf);
   settle(pf);
   for (; slab < a.slabs; slab += gridDim.x) {
     // An opaque per-slab copy of N keeps row-address arithmetic inside the
     // loop instead of hoisted into registers for its whole duration.
     int N = a.N;
     asm volatile("" : "+s"(N));
+    int row = row0, part = part0;  // likewise for per-lane offsets
+    asm volatile("" : "+v"(row), "+v"(part));
     __syncthreads();  // the previous slab is no longer read from LDS
     // Passes 1-2: K, V in bf16.  Passes 3-4: Q, dO in fp32 over the same
     // bytes.  Then the (P, dS) table, row-major with kTableCols entries.
     char* lds_k = smem;
     char* lds_v = smem + N * kBf16Stride;
+    char* lds_kf = smem + 2 * N * kBf16Stride;
     char* lds_q = smem;
     char* lds_do = smem + N * kF32Stride;
     float2* tbl = reinterpret_cast<float2*>(smem + N * kLdsPerRow);
@@ -287,7 +312,7 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
     const int rr = mine ? row : N - 1;
     const int w0 = r0 < N ? r0 : N - 1;                 // this wave's rows: [w0, wl]
     const int wl = (r0 + 31 < N ? r0 + 31 : N - 1);
-    commit_kv(lds_k, lds_v, N, tid, pf);
+    commit_kv(lds_k, lds_v, lds_kf, N, tid, pf);
     uint32_t qw[16], dw[16];
     unpack_words(pf.q, qw);
     unpack_words(pf.dout, dw);
@@ -334,8 +359,8 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
       float (&acc)[32] = dqa;
 #pragma unroll
       for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-      dq_pass<+1>(lds_k, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, acc);
-      dq_pass<-1>(lds_k, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, acc);
+      dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, acc);
+      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, acc);
       if (has0) {
         u32x4 kb[4];
         load_bf16_half(lds_k, rr, part, kb);

@@ -40,7 +40,7 @@ hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, 
                                 void* o, float* lse, hipStream_t stream);
 bool bwd_slab_fits(const Problem& p);
 
-// Persistent backward for bf16, d_h = 64, N <= 207 (the default when it fits).
+// Persistent backward for bf16, d_h = 64, N <= 201 (the default when it fits).
 bool bwd_slab_bf16_fits(const Problem& p);
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,

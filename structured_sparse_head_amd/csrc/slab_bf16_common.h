@@ -64,12 +64,21 @@ __device__ __forceinline__ void unpack_words(const u32x4 (&x)[4], uint32_t (&w)[
   }
 }
 
+// First product of an accumulation chain: v_dot2_f32_bf16 with an inline
+// zero addend (the builtin with a literal 0 would add a register move).
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Full 64-element dot product of two bf16 rows split over the lane pair,
 // accumulated in fp32.
 __device__ __forceinline__ float dot_bf16(const uint32_t (&a)[16], const u32x4 (&b)[4]) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
+                  dot2_first(a[3], b[0].w)};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 1; t < 4; ++t) {
     const uint32_t bw[4] = {b[t].x, b[t].y, b[t].z, b[t].w};
 #pragma unroll
     for (int u = 0; u < 4; ++u)

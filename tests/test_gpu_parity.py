@@ -164,8 +164,8 @@ EDGE = [
     ("d128 fp32", 1, 3, 150, 128, torch.float32, None, None),
     ("d64 fp32 mid", 1, 5, 700, 64, torch.float32, None, None),
     ("bf16 diag a=0 dup a=b", 2, 3, 40, 64, torch.bfloat16, ([0, 3, 5], [1, 3, 1]), [40, 40, 3]),
-    ("bf16 N207 H12", 2, 12, 207, 64, torch.bfloat16, None, None),
-    ("bf16 N208 H12", 1, 12, 208, 64, torch.bfloat16, None, None),
+    ("bf16 N201 H12", 2, 12, 201, 64, torch.bfloat16, None, None),
+    ("bf16 N202 H12", 1, 12, 202, 64, torch.bfloat16, None, None),
     ("bf16 N256", 1, 4, 256, 64, torch.bfloat16, None, None),
     ("bf16 H20", 2, 20, 100, 64, torch.bfloat16, None, None),
     ("bf16 N33 tail", 3, 5, 33, 64, torch.bfloat16, None, None),

@@ -10,18 +10,29 @@
 //   dV_k  = sum_j P_jk dO_j,
 // with P_jk = exp(S_jk - LSE_j) from the forward's log-sum-exp.
 //
-// Per slab, with K and V (bf16) in LDS:
-//  1. Query pass (two lanes per query row, see slab_bf16_common.h): for every
-//     signed displacement, P and dP from two dot products, kept in an LDS
-//     table indexed by (row, displacement); D exactly as sum P dP in fp32.
-//  2. dQ pass: dS = P (dP - D) and dQ = sum dS K, re-reading K; the table
-//     entries become (P, dS / sqrt(d)).
+// Lanes.  1024 threads (16 waves, four per SIMD so that LDS and arithmetic
+// latency is hidden by other waves); four lanes own a row: lane l of wave w
+// works on row 16 w + (l % 16) and, with p = l / 16, on the element groups
+// {4 g .. 4 g + 3} for g = p, p + 4, p + 8, p + 12.  The four lanes of a row
+// therefore cover each 64-byte span of an fp32 output row together, so every
+// global store instruction writes whole 64-byte pieces.  LDS rows are kept
+// permuted (each lane's 16 elements contiguous, in that group order) so a
+// lane reads its fragment with consecutive 16-byte loads.  A dot product
+// ends with v_permlane32_swap and v_permlane16_swap sums.
+//
+// Per slab, with K and V (bf16) and an fp32 copy of K in LDS:
+//  1. Query pass: for every signed displacement, P and dP from two dot
+//     products, kept in an LDS table indexed by (row, displacement); D
+//     exactly as sum P dP in fp32.
+//  2. dQ pass: dS = P (dP - D) and dQ = sum dS K; the table entries become
+//     (P, dS / sqrt(d)).
 //  3. Q and dO of every row replace K and V in LDS, widened to fp32.
 //  4. Key passes: the support is symmetric in j and k, so key k is seen by
 //     the queries k - delta for the same displacements; dV gathers P dO_j
-//     and then dK gathers dS Q_j from the table and the fp32 rows.  Every output row
-//     has one writer: no atomics, bitwise reproducible.
-// Q, K, V, dO and LSE are each read from HBM once; dQ, dK, dV written once.
+//     and then dK gathers dS Q_j from the table and the fp32 rows.  Every
+//     output row has one writer: no atomics, bitwise reproducible.
+// Q, K, V, dO and LSE are each read from HBM once; dQ, dK, dV written once,
+// dQ and dV a chunk per step of the following pass rather than in bursts.
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -29,14 +40,17 @@ namespace {
 
 using namespace slab;
 
+constexpr int kThreadsB = 1024;                       // 16 waves
+constexpr int kRowsB = kThreadsB / 4;                 // 256 rows, four lanes each
+constexpr int kChunksB = kRowsB * (kRowBytes / 16) / kThreadsB;  // 2
 constexpr int kTableCols = 2 * kMaxPos + 1;  // +f (0..11), -f (12..23), 0 (24)
 
 // LDS: per sequence row, bf16 K and V plus an fp32 copy of K for the query
 // and dQ passes, later overlaid by fp32 Q and dO rows for the key passes;
-// then the (P, dS) table with one row per lane pair (kMaxRows), so lanes past
+// then the (P, dS) table with one row per lane group (kRowsB), so lanes past
 // the last sequence row own private rows.
 constexpr int kLdsPerRow = 2 * kBf16Stride + kF32Stride;  // >= 2 * kF32Stride
-constexpr int kTableBytes = kMaxRows * kTableCols * 8;
+constexpr int kTableBytes = kRowsB * kTableCols * 8;
 constexpr int kLdsMax = 160 * 1024;
 constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 201
 
@@ -58,18 +72,76 @@ struct Args {
   u32x4 rec[MH];
 };
 
+// Sum of x over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float quad_sum(float x) {
+  const float y = pair_sum(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// This lane's quarter (16 bf16 = 32 bytes) of a bf16 LDS row.
+__device__ __forceinline__ void load_bf16_q(const char* base, int r, int part, u32x4 (&f)[2]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kBf16Stride) + part * 32);
+  f[0] = p[0];
+  f[1] = p[1];
+}
+
+// This lane's quarter (16 fp32 = 64 bytes) of an fp32 LDS row.
+__device__ __forceinline__ void load_f32_q(const char* base, int r, int part, u32x4 (&f)[4]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kF32Stride) + part * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) f[t] = p[t];
+}
+
+// Full 64-element dot product of two bf16 rows split over the row's four
+// lanes, accumulated in fp32.
+__device__ __forceinline__ float dot_q(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
+  float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
+                  dot2_first(a[3], b[0].w)};
+  const uint32_t bw[4] = {b[1].x, b[1].y, b[1].z, b[1].w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[4 + u]),
+                                             __builtin_bit_cast(bf16x2_t, bw[u]), acc[u], false);
+  return quad_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
+// acc += p * x for this lane's 16 fp32 elements.
+__device__ __forceinline__ void axpy_q(float (&acc)[16], float p, const u32x4 (&x)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc[4 * t + 0] = __builtin_fmaf(p, __uint_as_float(x[t].x), acc[4 * t + 0]);
+    acc[4 * t + 1] = __builtin_fmaf(p, __uint_as_float(x[t].y), acc[4 * t + 1]);
+    acc[4 * t + 2] = __builtin_fmaf(p, __uint_as_float(x[t].z), acc[4 * t + 2]);
+    acc[4 * t + 3] = __builtin_fmaf(p, __uint_as_float(x[t].w), acc[4 * t + 3]);
+  }
+}
+
+// Writes this lane's 16 bf16 elements (packed in w) as fp32 to an LDS row.
+__device__ __forceinline__ void store_f32_q_lds(char* base, int r, int part,
+                                                const uint32_t (&w)[8]) {
+  u32x4* p = reinterpret_cast<u32x4*>(base + r * kF32Stride + part * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    p[t] = u32x4{w[2 * t] << 16, w[2 * t] & 0xffff0000u, w[2 * t + 1] << 16,
+                 w[2 * t + 1] & 0xffff0000u};
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 struct Prefetch {
-  u32x4 k[kChunksPerThread];
-  u32x4 v[kChunksPerThread];
-  u32x4 q[4];
-  u32x4 dout[4];
+  u32x4 k[kChunksB];
+  u32x4 v[kChunksB];
+  u32x2 q[4];     // this lane's element groups of its Q row, 8 bytes each
+  u32x2 dout[4];
   float lse;
 };
 
 // Loads are unconditional (indices clamped into the slab) so every prefetch
-// register is overwritten each time; only the LDS commit is masked.
-// With `idle` set (no next slab) every address collapses onto the slab's
-// first row, so the loads still retire in order but cost no HBM traffic.
+// register is overwritten each time; only the LDS commit is masked.  With
+// `idle` set (no next slab) every address collapses onto the slab's first
+// row, so the loads still retire in order but cost no HBM traffic.
 template <typename A>
 __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, int tid, int row,
                                                int part, bool idle, Prefetch& pf) {
@@ -78,20 +150,20 @@ __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, i
   const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
   const int last = idle ? 0 : N * (kRowBytes / 16) - 1;
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    int idx = tid + c * kThreads;
+  for (int c = 0; c < kChunksB; ++c) {
+    int idx = tid + c * kThreadsB;
     idx = idx < last ? idx : last;
     pf.k[c] = __builtin_nontemporal_load(ks + idx);
     pf.v[c] = __builtin_nontemporal_load(vs + idx);
   }
   const int r = idle ? 0 : (row < N ? row : N - 1);
-  const size_t off = base + static_cast<size_t>(r) * kRowBytes + part * 64;
-  const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + off);
-  const u32x4* ds = reinterpret_cast<const u32x4*>(a.dout + off);
+  const size_t off = base + static_cast<size_t>(r) * kRowBytes + part * 8;
+  const u32x2* qs = reinterpret_cast<const u32x2*>(a.q + off);
+  const u32x2* ds = reinterpret_cast<const u32x2*>(a.dout + off);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    pf.q[t] = __builtin_nontemporal_load(qs + t);
-    pf.dout[t] = __builtin_nontemporal_load(ds + t);
+  for (int m = 0; m < 4; ++m) {  // group part + 4 m sits at byte 8 part + 32 m
+    pf.q[m] = __builtin_nontemporal_load(qs + 4 * m);
+    pf.dout[m] = __builtin_nontemporal_load(ds + 4 * m);
   }
   pf.lse = __builtin_nontemporal_load(a.lse + slab * static_cast<size_t>(N) + r);
 }
@@ -99,9 +171,9 @@ __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, i
 // Makes the compiler wait here for every prefetch register.
 __device__ __forceinline__ void settle(const Prefetch& pf) {
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) asm volatile("" ::"v"(pf.k[c]), "v"(pf.v[c]));
+  for (int c = 0; c < kChunksB; ++c) asm volatile("" ::"v"(pf.k[c]), "v"(pf.v[c]));
 #pragma unroll
-  for (int t = 0; t < 4; ++t) asm volatile("" ::"v"(pf.q[t]), "v"(pf.dout[t]));
+  for (int m = 0; m < 4; ++m) asm volatile("" ::"v"(pf.q[m]), "v"(pf.dout[m]));
   asm volatile("" ::"v"(pf.lse));
 }
 
@@ -109,54 +181,59 @@ __device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, char* lds_kf
                                           const Prefetch& pf) {
   const int chunks = N * (kRowBytes / 16);
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    const int idx = tid + c * kThreads;
+  for (int c = 0; c < kChunksB; ++c) {
+    const int idx = tid + c * kThreadsB;
     if (idx < chunks) {
-      const int off = (idx >> 3) * kBf16Stride + (idx & 7) * 16;
-      *reinterpret_cast<u32x4*>(lds_k + off) = pf.k[c];
-      *reinterpret_cast<u32x4*>(lds_v + off) = pf.v[c];
-      const u32x4 x = pf.k[c];
-      char* kf = lds_kf + (idx >> 3) * kF32Stride + (idx & 7) * 32;
-      *reinterpret_cast<u32x4*>(kf) = u32x4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
-      *reinterpret_cast<u32x4*>(kf + 16) =
-          u32x4{x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
+      // Chunk ch of row r holds element groups 2 ch and 2 ch + 1; group g goes
+      // to lane part g % 4, slot g / 4 of the permuted row.
+      const int r = idx >> 3, ch = idx & 7;
+      const int g0 = 2 * ch, g1 = 2 * ch + 1;
+      const int b0 = r * kBf16Stride + (g0 & 3) * 32 + (g0 >> 2) * 8;
+      const int b1 = r * kBf16Stride + (g1 & 3) * 32 + (g1 >> 2) * 8;
+      const u32x4 xk = pf.k[c], xv = pf.v[c];
+      *reinterpret_cast<uint2*>(lds_k + b0) = make_uint2(xk.x, xk.y);
+      *reinterpret_cast<uint2*>(lds_k + b1) = make_uint2(xk.z, xk.w);
+      *reinterpret_cast<uint2*>(lds_v + b0) = make_uint2(xv.x, xv.y);
+      *reinterpret_cast<uint2*>(lds_v + b1) = make_uint2(xv.z, xv.w);
+      char* f0 = lds_kf + r * kF32Stride + (g0 & 3) * 64 + (g0 >> 2) * 16;
+      char* f1 = lds_kf + r * kF32Stride + (g1 & 3) * 64 + (g1 >> 2) * 16;
+      *reinterpret_cast<u32x4*>(f0) =
+          u32x4{xk.x << 16, xk.x & 0xffff0000u, xk.y << 16, xk.y & 0xffff0000u};
+      *reinterpret_cast<u32x4*>(f1) =
+          u32x4{xk.z << 16, xk.z & 0xffff0000u, xk.w << 16, xk.w & 0xffff0000u};
     }
   }
 }
 
-// A finished fp32 half-row waiting to be written: its eight 16-byte chunks
-// are stored one per step of a later pass instead of in one burst, so the
-// stores of all waves trickle out while they compute.
+// A finished fp32 row fragment waiting to be written: its four 16-byte
+// groups (64 bytes apart in the row) are stored one per step of a later pass
+// instead of in one burst, so the stores of all waves trickle out while they
+// compute.
 struct Pending {
   float4* dst;
-  const float (&x)[32];
+  const float (&x)[16];
   float scale;
   int next;
   __device__ __forceinline__ void store(int t) {
     switch (t) {
-#define FIBATT_CHUNK(T)                                                                      \
-  case T:                                                                                    \
-    dst[T] = make_float4(x[4 * T] * scale, x[4 * T + 1] * scale, x[4 * T + 2] * scale,        \
-                         x[4 * T + 3] * scale);                                             \
+#define FIBATT_CHUNK(T)                                                               \
+  case T:                                                                             \
+    dst[4 * T] = make_float4(x[4 * T] * scale, x[4 * T + 1] * scale, x[4 * T + 2] * scale, \
+                         x[4 * T + 3] * scale);                                      \
     break;
       FIBATT_CHUNK(0) FIBATT_CHUNK(1) FIBATT_CHUNK(2) FIBATT_CHUNK(3)
-      FIBATT_CHUNK(4) FIBATT_CHUNK(5) FIBATT_CHUNK(6) FIBATT_CHUNK(7)
 #undef FIBATT_CHUNK
       default:
         break;
     }
   }
   __device__ __forceinline__ void tick() {
-    if (next < 8) store(next);
+    if (next < 4) store(next);
     ++next;
   }
   __device__ __forceinline__ void flush() {
-    for (; next < 8; ++next) store(next);
+    for (; next < 4; ++next) store(next);
   }
-};
-
-struct NoTick {
-  __device__ __forceinline__ void tick() {}
 };
 
 // Ascending positive distances of a head, one byte each in three words
@@ -171,25 +248,24 @@ struct Dist {
 
 // Query pass for displacements SGN * f_i, i < n (wave-uniform n) of data row
 // `row`: P (0 where the key is out of range) and dP go to table row trow,
-// column base + i (written by the pair's first lane, wr), and sum P dP is
-// added to d.  Two steps per
-// trip, so one step's K and V fragments are in flight during the other's
-// arithmetic.
+// column base + i (written by the group's first lane, wr), and sum P dP is
+// added to d.  The next step's K and V fragments are requested before the
+// current step's arithmetic.
 template <int SGN>
 __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v, float2* tbl,
                                            Dist dist, int n, int row, int trow, int N, int part,
-                                           const uint32_t (&qw)[16], const uint32_t (&dw)[16],
+                                           const uint32_t (&qw)[8], const uint32_t (&dw)[8],
                                            float c, float lse2, int base, bool wr, float& d) {
-  u32x4 ka[4], va[4], kb[4], vb[4];
-  auto load = [&](int i, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
+  u32x4 ka[2], va[2], kb[2], vb[2];
+  auto load = [&](int i, u32x4 (&kf)[2], u32x4 (&vf)[2]) {
     const int r = clamp_row(row + SGN * dist.at(i), N);
-    load_bf16_half(lds_k, r, part, kf);
-    load_bf16_half(lds_v, r, part, vf);
+    load_bf16_q(lds_k, r, part, kf);
+    load_bf16_q(lds_v, r, part, vf);
   };
-  auto step = [&](int i, const u32x4 (&kf)[4], const u32x4 (&vf)[4]) {
+  auto step = [&](int i, const u32x4 (&kf)[2], const u32x4 (&vf)[2]) {
     const int kk = row + SGN * dist.at(i);
-    const float s = dot_bf16(qw, kf);
-    const float dp = dot_bf16(dw, vf);
+    const float s = dot_q(qw, kf);
+    const float dp = dot_q(dw, vf);
     const bool ok = static_cast<unsigned>(kk) < static_cast<unsigned>(N);
     const float p = ok ? fast_exp2(__builtin_fmaf(s, c, -lse2)) : 0.f;
     if (wr) tbl[trow * kTableCols + base + i] = make_float2(p, dp);
@@ -211,74 +287,47 @@ __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v,
 template <int SGN>
 __device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist dist, int n, int row,
                                         int trow, int N, int part, float d, float scale, int base,
-                                        bool wr, float (&acc)[32]) {
-  // The step's table entry is fetched with its fp32 K fragment, one step
-  // ahead.
-  u32x4 ka[8], kb[8];
-  float2 ea, eb;
+                                        bool wr, float (&acc)[16]) {
   float2* e0 = tbl + trow * kTableCols + base;
-  auto load = [&](int i, u32x4 (&kf)[8], float2& e) {
-    load_f32_half(lds_kf, clamp_row(row + SGN * dist.at(i), N), part, kf);
-    e = e0[i];
-  };
-  auto step = [&](int i, const u32x4 (&kf)[8], const float2& e) {
+  for (int i = 0; i < n; ++i) {
+    u32x4 kf[4];
+    load_f32_q(lds_kf, clamp_row(row + SGN * dist.at(i), N), part, kf);
+    const float2 e = e0[i];
     const float ds = e.x * (e.y - d);
-    axpy_f32(acc, ds, kf);
+    axpy_q(acc, ds, kf);
     if (wr) e0[i] = make_float2(e.x, ds * scale);
-  };
-  if (n > 0) load(0, ka, ea);
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(i + 1, kb, eb);
-    step(i, ka, ea);
-    if (i + 1 < n) {
-      if (i + 2 < n) load(i + 2, ka, ea);
-      step(i + 1, kb, eb);
-    }
   }
 }
 
 // Key pass for key row k over displacements SGN * f_i: the queries
 // j = k - SGN * f_i contribute w_j * X_j, where w_j is component C of their
-// table entry (P for dV, dS / sqrt(d) for dK) and X_j their fp32 row.
+// table entry (P for dV, dS / sqrt(d) for dK) and X_j their fp32 row (the
+// other waves of the SIMD cover the LDS latency of each step).
 template <int SGN, int C, typename Tick>
 __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, Dist dist, int n,
-                                         int k, int N, int part, int base, float (&acc)[32],
+                                         int k, int N, int part, int base, float (&acc)[16],
                                          Tick& tk) {
-  // Row and weight of a step are fetched together, one step ahead.
-  u32x4 xa[8], xb[8];
-  float wa, wb;
-  auto load = [&](int i, u32x4 (&xf)[8], float& w) {
+  for (int i = 0; i < n; ++i) {
     const int j = k - SGN * dist.at(i);
     const int jc = clamp_row(j, N);
-    load_f32_half(lds_x, jc, part, xf);
+    u32x4 xf[4];
+    load_f32_q(lds_x, jc, part, xf);
     const float2 t = tbl[jc * kTableCols + base + i];
     const bool ok = static_cast<unsigned>(j) < static_cast<unsigned>(N);
-    w = ok ? (C == 0 ? t.x : t.y) : 0.f;
-  };
-  auto step = [&](const u32x4 (&xf)[8], float w) {
     tk.tick();
-    axpy_f32(acc, w, xf);
-  };
-  if (n > 0) load(0, xa, wa);
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(i + 1, xb, wb);
-    step(xa, wa);
-    if (i + 1 < n) {
-      if (i + 2 < n) load(i + 2, xa, wa);
-      step(xb, wb);
-    }
+    axpy_q(acc, ok ? (C == 0 ? t.x : t.y) : 0.f, xf);
   }
 }
 
 template <int MH>
-__global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
+__global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int row0 = 32 * wave + (lane & 31);
-  const int part0 = lane >> 5;
-  const int r0 = 32 * wave;
+  const int row0 = 16 * wave + (lane & 15);
+  const int part0 = lane >> 4;
+  const int r0 = 16 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are
   // completed before the loop so that the loop's first trip and later trips
@@ -289,15 +338,13 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
   issue_prefetch(a, a.N, slab, tid, row0, part0, false, pf);
   settle(pf);
   for (; slab < a.slabs; slab += gridDim.x) {
-    // An opaque per-slab copy of N keeps row-address arithmetic inside the
-    // loop instead of hoisted into registers for its whole duration.
+    // Opaque per-slab copies of N and of the lane's row and part keep the
+    // address arithmetic inside the loop instead of hoisted into registers.
     int N = a.N;
     asm volatile("" : "+s"(N));
-    int row = row0, part = part0;  // likewise for per-lane offsets
+    int row = row0, part = part0;
     asm volatile("" : "+v"(row), "+v"(part));
     __syncthreads();  // the previous slab is no longer read from LDS
-    // Passes 1-2: K, V in bf16.  Passes 3-4: Q, dO in fp32 over the same
-    // bytes.  Then the (P, dS) table, row-major with kTableCols entries.
     char* lds_k = smem;
     char* lds_v = smem + N * kBf16Stride;
     char* lds_kf = smem + 2 * N * kBf16Stride;
@@ -310,18 +357,20 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
     // counter then tracks stores exactly and never has to drain them early.
     const bool mine = row < N;
     const int rr = mine ? row : N - 1;
-    const int w0 = r0 < N ? r0 : N - 1;                 // this wave's rows: [w0, wl]
-    const int wl = (r0 + 31 < N ? r0 + 31 : N - 1);
+    const int w0 = r0 < N ? r0 : N - 1;  // this wave's rows: [w0, wl]
+    const int wl = (r0 + 15 < N ? r0 + 15 : N - 1);
     commit_kv(lds_k, lds_v, lds_kf, N, tid, pf);
-    uint32_t qw[16], dw[16];
-    unpack_words(pf.q, qw);
-    unpack_words(pf.dout, dw);
+    uint32_t qw[8], dw[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      qw[2 * m] = pf.q[m].x;
+      qw[2 * m + 1] = pf.q[m].y;
+      dw[2 * m] = pf.dout[m].x;
+      dw[2 * m + 1] = pf.dout[m].y;
+    }
     const float lse2 = pf.lse * kLog2e;
     __syncthreads();
     // Start the next slab's loads; they land while this slab is computed.
-    // The wait counter retires memory operations in issue order, and every
-    // store of this slab is issued after these loads, so the commit at the
-    // next slab never waits for those stores.
     const int next = slab + gridDim.x;
     issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
     const size_t grow = static_cast<size_t>(slab) * N + rr;
@@ -339,34 +388,33 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
       n_dn += (f <= wl) ? 1 : 0;
     }
     constexpr int z = 2 * kMaxPos;  // table column of distance 0
-    const bool wr = part == 0;  // table rows: row (private per lane pair)
-    float dqa[32];
+    const bool wr = part == 0;      // table rows: row (private per lane group)
+    float dqa[16];
     {
       float d = 0.f;
       query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, row, N, part, qw, dw, a.c, lse2, 0, wr, d);
       query_pass<-1>(lds_k, lds_v, tbl, dist, n_dn, rr, row, N, part, qw, dw, a.c, lse2, kMaxPos,
                      wr, d);
       if (has0) {
-        u32x4 kb[4], vb[4];
-        load_bf16_half(lds_k, rr, part, kb);
-        load_bf16_half(lds_v, rr, part, vb);
-        const float s = dot_bf16(qw, kb);
-        const float dp = dot_bf16(dw, vb);
+        u32x4 kb[2], vb[2];
+        load_bf16_q(lds_k, rr, part, kb);
+        load_bf16_q(lds_v, rr, part, vb);
+        const float s = dot_q(qw, kb);
+        const float dp = dot_q(dw, vb);
         const float p = fast_exp2(__builtin_fmaf(s, a.c, -lse2));
         if (wr) tbl[row * kTableCols + z] = make_float2(p, dp);
         d = __builtin_fmaf(p, dp, d);
       }
-      float (&acc)[32] = dqa;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-      dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, acc);
-      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, acc);
+      for (int e = 0; e < 16; ++e) dqa[e] = 0.f;
+      dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, dqa);
+      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, dqa);
       if (has0) {
-        u32x4 kb[4];
-        load_bf16_half(lds_k, rr, part, kb);
+        u32x4 kf[4];
+        load_f32_q(lds_kf, rr, part, kf);
         const float2 e = tbl[row * kTableCols + z];
         const float ds = e.x * (e.y - d);
-        axpy_bf16(acc, ds, kb);
+        axpy_q(dqa, ds, kf);
         if (wr) tbl[row * kTableCols + z] = make_float2(e.x, ds * a.scale);
       }
     }
@@ -376,39 +424,42 @@ __global__ void __launch_bounds__(kThreads) bwd_slab_bf16_kernel(Args<MH> a) {
     settle(pf);
     __syncthreads();  // K and V are no longer read; the table is complete
     if (mine) {
-      store_f32_half_from_bf16(lds_q, row, part, qw);
-      store_f32_half_from_bf16(lds_do, row, part, dw);
+      store_f32_q_lds(lds_q, row, part, qw);
+      store_f32_q_lds(lds_do, row, part, dw);
     }
     __syncthreads();
     {
       // Key k, displacement +f: query k - f exists while k >= f (f <= wl for
       // some key of the wave); displacement -f: query k + f < N.
       // dQ is written during the dV pass and dV during the dK pass.
-      Pending pq{reinterpret_cast<float4*>(a.dq + grow * 64) + part * 8, dqa, a.scale, 0};
-      float acc[32];
+      Pending pq{reinterpret_cast<float4*>(a.dq + grow * 64) + part, dqa, a.scale, 0};
+      float acc[16];
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
       key_pass<+1, 0>(lds_do, tbl, dist, n_dn, rr, N, part, 0, acc, pq);
       key_pass<-1, 0>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, pq);
       if (has0) {
-        u32x4 xb[8];
-        load_f32_half(lds_do, rr, part, xb);
-        axpy_f32(acc, tbl[rr * kTableCols + z].x, xb);
+        u32x4 xb[4];
+        load_f32_q(lds_do, rr, part, xb);
+        axpy_q(acc, tbl[rr * kTableCols + z].x, xb);
       }
       pq.flush();
-      Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part * 8, acc, 1.0f, 0};
-      float acc2[32];
+      Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part, acc, 1.0f, 0};
+      float acc2[16];
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc2[e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc2[e] = 0.f;
       key_pass<+1, 1>(lds_q, tbl, dist, n_dn, rr, N, part, 0, acc2, pv);
       key_pass<-1, 1>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, pv);
       if (has0) {
-        u32x4 xb[8];
-        load_f32_half(lds_q, rr, part, xb);
-        axpy_f32(acc2, tbl[rr * kTableCols + z].y, xb);
+        u32x4 xb[4];
+        load_f32_q(lds_q, rr, part, xb);
+        axpy_q(acc2, tbl[rr * kTableCols + z].y, xb);
       }
       pv.flush();
-      store_f32_half_global(a.dk + grow * 64, part, acc2, 1.0f);
+      float4* dk = reinterpret_cast<float4*>(a.dk + grow * 64) + part;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dk[4 * t] = make_float4(acc2[4 * t], acc2[4 * t + 1], acc2[4 * t + 2], acc2[4 * t + 3]);
     }
   }
 }
@@ -440,7 +491,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   if (attr != hipSuccess) return attr;
   const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsB), lds, stream, a);
   return hipGetLastError();
 }
 

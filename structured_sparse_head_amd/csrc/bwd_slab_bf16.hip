@@ -72,52 +72,6 @@ struct Args {
   u32x4 rec[MH];
 };
 
-// Sum of x over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48).
-__device__ __forceinline__ float quad_sum(float x) {
-  const float y = pair_sum(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// This lane's quarter (16 bf16 = 32 bytes) of a bf16 LDS row.
-__device__ __forceinline__ void load_bf16_q(const char* base, int r, int part, u32x4 (&f)[2]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kBf16Stride) + part * 32);
-  f[0] = p[0];
-  f[1] = p[1];
-}
-
-// This lane's quarter (16 fp32 = 64 bytes) of an fp32 LDS row.
-__device__ __forceinline__ void load_f32_q(const char* base, int r, int part, u32x4 (&f)[4]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kF32Stride) + part * 64);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) f[t] = p[t];
-}
-
-// Full 64-element dot product of two bf16 rows split over the row's four
-// lanes, accumulated in fp32.
-__device__ __forceinline__ float dot_q(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
-  float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
-                  dot2_first(a[3], b[0].w)};
-  const uint32_t bw[4] = {b[1].x, b[1].y, b[1].z, b[1].w};
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[4 + u]),
-                                             __builtin_bit_cast(bf16x2_t, bw[u]), acc[u], false);
-  return quad_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-}
-
-// acc += p * x for this lane's 16 fp32 elements.
-__device__ __forceinline__ void axpy_q(float (&acc)[16], float p, const u32x4 (&x)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    acc[4 * t + 0] = __builtin_fmaf(p, __uint_as_float(x[t].x), acc[4 * t + 0]);
-    acc[4 * t + 1] = __builtin_fmaf(p, __uint_as_float(x[t].y), acc[4 * t + 1]);
-    acc[4 * t + 2] = __builtin_fmaf(p, __uint_as_float(x[t].z), acc[4 * t + 2]);
-    acc[4 * t + 3] = __builtin_fmaf(p, __uint_as_float(x[t].w), acc[4 * t + 3]);
-  }
-}
-
 // Writes this lane's 16 bf16 elements (packed in w) as fp32 to an LDS row.
 __device__ __forceinline__ void store_f32_q_lds(char* base, int r, int part,
                                                 const uint32_t (&w)[8]) {
@@ -233,16 +187,6 @@ struct Pending {
   }
   __device__ __forceinline__ void flush() {
     for (; next < 4; ++next) store(next);
-  }
-};
-
-// Ascending positive distances of a head, one byte each in three words
-// (wave-uniform, so extraction is scalar arithmetic).
-struct Dist {
-  uint32_t w0, w1, w2;
-  __device__ __forceinline__ int at(int i) const {
-    const uint32_t w = i < 4 ? w0 : (i < 8 ? w1 : w2);
-    return static_cast<int>((w >> (8 * (i & 3))) & 0xffu);
   }
 };
 

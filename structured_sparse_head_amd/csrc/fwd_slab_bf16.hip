@@ -7,27 +7,38 @@
 // section, eq. (1) and (3); README Algorithm 3): scores Q_j . K_k / sqrt(d)
 // on the head's support, a row softmax, P V.  Design points:
 //
-//  * Lanes and LDS strides as in slab_bf16_common.h.  K rows are kept in
-//    bf16 and V rows in fp32 (converted once while staging), so P V needs
-//    no conversions.
+//  * Lanes.  1024 threads (16 waves, four per SIMD so that LDS and
+//    arithmetic latency is hidden by other waves); four lanes own a row:
+//    lane l of wave w works on row 16 w + (l % 16) and, with p = l / 16, on
+//    the 8-element groups p and p + 4.  The four lanes of a row thus cover
+//    each 64-byte half of the bf16 output row together, so every store
+//    instruction writes whole 64-byte pieces.  LDS rows are kept permuted
+//    (each lane's 16 elements contiguous) so a lane reads its fragment with
+//    consecutive 16-byte loads.  K rows stay bf16 and V rows are widened to
+//    fp32 while staging, so P V needs no conversions.
 //  * Softmax.  All scores of a row (at most 12 distances, each signed, plus
 //    0, for N <= 256) stay in registers: one pass forms them, the row
 //    maximum is taken once, a second pass exponentiates and accumulates P V
 //    in fp32.  No rescaling of the accumulator is needed.  Each pass walks
-//    the +f and -f displacements separately: for a wave's 32 rows the useful
+//    the +f and -f displacements separately: for a wave's 16 rows the useful
 //    ones are a prefix of the ascending distances in each direction, so the
 //    trip counts are wave-uniform and whole-wave misses are skipped.  Reads
-//    are branch-free (out-of-range keys use a clamped row and score -inf) and
-//    double-buffered so the next fragment is in flight during the arithmetic.
+//    are branch-free (out-of-range keys use a clamped row and score -inf);
+//    key fragments are double-buffered.
 //  * Overlap.  While a slab is computed from LDS, each thread already holds
-//    the next slab's K, V chunks and its own Q fragment in flight in
-//    registers; they are committed to LDS after the next barrier.
+//    chunks of the next slab's Q, K and V in flight in registers; they are
+//    committed to LDS after the next barrier (Q too, so that no prefetch
+//    register is carried across the loop).
 #include "slab_bf16_common.h"
 
 namespace fibatt {
 namespace {
 
 using namespace slab;
+
+constexpr int kThreadsF = 1024;                                  // 16 waves
+constexpr int kRowsF = kThreadsF / 4;                            // 256 rows
+constexpr int kChunksF = kRowsF * (kRowBytes / 16) / kThreadsF;  // 2
 
 // Per-head record: bytes 0..11 the ascending positive distances, byte 12
 // their count, byte 13 whether 0 is a distance.  Built on the host; with at
@@ -47,206 +58,232 @@ struct Args {
 };
 
 struct Prefetch {
-  u32x4 k[kChunksPerThread];
-  u32x4 v[kChunksPerThread];
-  u32x4 q[4];
+  u32x4 k[kChunksF];
+  u32x4 v[kChunksF];
+  u32x4 q[kChunksF];
 };
 
 // Loads are unconditional (indices clamped into the slab) so that every
 // prefetch register is overwritten each time; only the LDS commit is masked.
+// With `idle` set (no next slab) every address collapses onto the slab's
+// first row, so the loads cost no HBM traffic.
 template <typename A>
-__device__ __forceinline__ void issue_prefetch(const A& a, size_t slab, int tid, int row,
-                                               int part, Prefetch& pf) {
-  const size_t base = slab * static_cast<size_t>(a.N) * kRowBytes;
+__device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, int tid, int row,
+                                               int part, bool idle, Prefetch& pf) {
+  const size_t base = slab * static_cast<size_t>(N) * kRowBytes;
   const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
   const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
-  const int last = a.N * (kRowBytes / 16) - 1;
+  const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + base);
+  const int last = idle ? 0 : N * (kRowBytes / 16) - 1;
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    int idx = tid + c * kThreads;
+  for (int c = 0; c < kChunksF; ++c) {
+    int idx = tid + c * kThreadsF;
     idx = idx < last ? idx : last;
     pf.k[c] = __builtin_nontemporal_load(ks + idx);
     pf.v[c] = __builtin_nontemporal_load(vs + idx);
+    pf.q[c] = __builtin_nontemporal_load(qs + idx);
   }
-  const int r = row < a.N ? row : a.N - 1;
-  const u32x4* qs =
-      reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(r) * kRowBytes + part * 64);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pf.q[t] = __builtin_nontemporal_load(qs + t);
 }
 
-__device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, int N, int tid,
-                                                const Prefetch& pf) {
+// Makes the compiler wait here for every prefetch register.
+__device__ __forceinline__ void settle(const Prefetch& pf) {
+#pragma unroll
+  for (int c = 0; c < kChunksF; ++c) asm volatile("" ::"v"(pf.k[c]), "v"(pf.v[c]), "v"(pf.q[c]));
+}
+
+// Chunk ch (8 elements) of row r is element group ch: it goes to lane part
+// ch % 4, slot ch / 4 of the permuted row; V is widened to fp32.
+__device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, char* lds_q, int N,
+                                                int tid, const Prefetch& pf) {
   const int chunks = N * (kRowBytes / 16);
 #pragma unroll
-  for (int c = 0; c < kChunksPerThread; ++c) {
-    const int idx = tid + c * kThreads;
+  for (int c = 0; c < kChunksF; ++c) {
+    const int idx = tid + c * kThreadsF;
     if (idx < chunks) {
       const int r = idx >> 3;
       const int ch = idx & 7;
-      *reinterpret_cast<u32x4*>(lds_k + r * kBf16Stride + ch * 16) = pf.k[c];
+      const int kb = r * kBf16Stride + (ch & 3) * 32 + (ch >> 2) * 16;
+      *reinterpret_cast<u32x4*>(lds_k + kb) = pf.k[c];
+      *reinterpret_cast<u32x4*>(lds_q + kb) = pf.q[c];
       const u32x4 x = pf.v[c];
-      const u32x4 lo = {x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
-      const u32x4 hi = {x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
-      *reinterpret_cast<u32x4*>(lds_v + r * kF32Stride + ch * 32) = lo;
-      *reinterpret_cast<u32x4*>(lds_v + r * kF32Stride + ch * 32 + 16) = hi;
+      char* vp = lds_v + r * kF32Stride + (ch & 3) * 64 + (ch >> 2) * 32;
+      *reinterpret_cast<u32x4*>(vp) = u32x4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
+      *reinterpret_cast<u32x4*>(vp + 16) =
+          u32x4{x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
     }
   }
 }
 
-
-// Scores for displacements sgn * pos[i], i < n (wave-uniform n).  Out-of-range
+// Scores for displacements SGN * f_i, i < n (wave-uniform n).  Out-of-range
 // keys are read from a clamped row and scored -inf.  The next key fragment is
 // requested before the current dot product so LDS latency overlaps arithmetic.
 template <int SGN>
-__device__ __forceinline__ void scores_dir(const char* lds_k, const int (&pos)[kMaxPos], int n,
-                                           int row, int part, int N, const uint32_t (&qw)[16],
-                                           float (&s)[kMaxPos]) {
-  u32x4 kb[2][4];
-  if (n > 0) load_bf16_half(lds_k, clamp_row(row + SGN * pos[0], N), part, kb[0]);
+__device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, int row, int part,
+                                           int N, const uint32_t (&qw)[8], float (&s)[kMaxPos]) {
+  u32x4 ka[2], kb[2];
 #pragma unroll
-  for (int i = 0; i < kMaxPos; ++i) {
-    s[i] = -INFINITY;
+  for (int i = 0; i < kMaxPos; ++i) s[i] = -INFINITY;
+  if (n > 0) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(0), N), part, ka);
+#pragma unroll
+  for (int i = 0; i < kMaxPos; i += 2) {
     if (i < n) {
-      if (i + 1 < kMaxPos && i + 1 < n)
-        load_bf16_half(lds_k, clamp_row(row + SGN * pos[i + 1 < kMaxPos ? i + 1 : i], N), part,
-               kb[(i + 1) & 1]);
-      const int kk = row + SGN * pos[i];
-      const float d = dot_bf16(qw, kb[i & 1]);
-      s[i] = (static_cast<unsigned>(kk) < static_cast<unsigned>(N)) ? d : -INFINITY;
+      if (i + 1 < n) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(i + 1), N), part, kb);
+      const int k0 = row + SGN * dist.at(i);
+      const float d0 = dot_q(qw, ka);
+      s[i] = (static_cast<unsigned>(k0) < static_cast<unsigned>(N)) ? d0 : -INFINITY;
+      if (i + 1 < n) {
+        if (i + 2 < n) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(i + 2), N), part, ka);
+        const int k1 = row + SGN * dist.at(i + 1);
+        const float d1 = dot_q(qw, kb);
+        s[i + 1] = (static_cast<unsigned>(k1) < static_cast<unsigned>(N)) ? d1 : -INFINITY;
+      }
     }
   }
 }
 
 template <int SGN>
-__device__ __forceinline__ void accumulate_dir(const char* lds_v, const int (&pos)[kMaxPos],
-                                               int n, int row, int part, int N, float c, float mc,
+__device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int n, int row,
+                                               int part, int N, float c, float mc,
                                                const float (&s)[kMaxPos], float& l,
-                                               float (&o)[32]) {
-  u32x4 vb[2][8];
-  if (n > 0) load_f32_half(lds_v, clamp_row(row + SGN * pos[0], N), part, vb[0]);
-#pragma unroll
-  for (int i = 0; i < kMaxPos; ++i) {
-    if (i < n) {
-      if (i + 1 < kMaxPos && i + 1 < n)
-        load_f32_half(lds_v, clamp_row(row + SGN * pos[i + 1 < kMaxPos ? i + 1 : i], N), part,
-               vb[(i + 1) & 1]);
-      const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
-      l += p;
-      axpy_f32(o, p, vb[i & 1]);
-    }
+                                               float (&o)[16]) {
+  // Single-buffered: the other waves of the SIMD cover each step's LDS
+  // latency.
+  for (int i = 0; i < n; ++i) {
+    u32x4 vf[4];
+    load_f32_q(lds_v, clamp_row(row + SGN * dist.at(i), N), part, vf);
+    const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
+    l += p;
+    axpy_q(o, p, vf);
   }
 }
 
+// One slab for an active wave (its first row is < N).  Lanes past the last
+// row repeat row N - 1 and store the same values, so the stores need no
+// branch and the memory wait counter stays exact around the loop.
 template <typename A>
-__device__ __forceinline__ void attend_row(const A& a, size_t slab, int row, int part,
-                                           const char* lds_k, const char* lds_v,
-                                           const int (&pos)[kMaxPos], int n_plus, int n_minus,
-                                           bool has0, const u32x4 (&q)[4]) {
-  const int N = a.N;
-  uint32_t qw[16];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    qw[4 * t + 0] = q[t].x;
-    qw[4 * t + 1] = q[t].y;
-    qw[4 * t + 2] = q[t].z;
-    qw[4 * t + 3] = q[t].w;
+__device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row, int part, int r0,
+                                            const char* lds_k, const char* lds_v,
+                                            const char* lds_q, Prefetch& pf) {
+  const u32x4 rec = a.rec[slab % a.H];
+  const Dist dist{rec.x, rec.y, rec.z};
+  const int npos = static_cast<int>(rec.w & 0xffu);
+  const bool has0 = ((rec.w >> 8) & 0xffu) != 0;
+  const int rr = row < N ? row : N - 1;
+  uint32_t qw[8];
+  {
+    u32x4 qf[2];
+    load_bf16_q(lds_q, rr, part, qf);
+    qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
+    qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
+  }
+  // Displacements +f are useful to this wave while r0 + f < N, and -f
+  // while f <= rl; both are prefixes of the ascending distance list.
+  const int rl = (r0 + 15 < N ? r0 + 15 : N - 1);
+  int n_plus = 0, n_minus = 0;
+  for (int i = 0; i < npos; ++i) {
+    const int f = dist.at(i);
+    n_plus += (r0 + f < N) ? 1 : 0;
+    n_minus += (f <= rl) ? 1 : 0;
   }
   // Pass 1: raw scores Q_j . K_k for every signed displacement.
   float sp[kMaxPos], sm[kMaxPos];
-  scores_dir<+1>(lds_k, pos, n_plus, row, part, N, qw, sp);
-  scores_dir<-1>(lds_k, pos, n_minus, row, part, N, qw, sm);
+  scores_dir<+1>(lds_k, dist, n_plus, rr, part, N, qw, sp);
+  scores_dir<-1>(lds_k, dist, n_minus, rr, part, N, qw, sm);
   float s0 = -INFINITY;
   if (has0) {
-    u32x4 kf[4];
-    load_bf16_half(lds_k, row, part, kf);
-    s0 = dot_bf16(qw, kf);
+    u32x4 kf[2];
+    load_bf16_q(lds_k, rr, part, kf);
+    s0 = dot_q(qw, kf);
   }
   float m = s0;
 #pragma unroll
   for (int i = 0; i < kMaxPos; ++i) m = fmaxf(m, fmaxf(sp[i], sm[i]));
-
-  const size_t grow = slab * static_cast<size_t>(N) + row;
-  u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes + part * 64);
-  if (m == -INFINITY) {  // no key in the support of this row
-#pragma unroll
-    for (int t = 0; t < 4; ++t) orow[t] = u32x4{0u, 0u, 0u, 0u};
-    if (part == 0) a.lse[grow] = -INFINITY;
-    return;
-  }
-  // Pass 2: P = exp(scale (s - m)), accumulate P V in fp32.
+  // Pass 2: P = exp(scale (s - m)), accumulate P V in fp32.  A row with no
+  // key in its support keeps l = 0 and is written as O = 0, LSE = -inf.
+  const bool any = m != -INFINITY;
   const float c = a.scale_log2;
-  const float mc = m * c;
+  const float mc = any ? m * c : 0.f;
   float l = 0.f;
-  float o[32];
+  float o[16];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) o[e] = 0.f;
-  accumulate_dir<+1>(lds_v, pos, n_plus, row, part, N, c, mc, sp, l, o);
-  accumulate_dir<-1>(lds_v, pos, n_minus, row, part, N, c, mc, sm, l, o);
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  accumulate_dir<+1>(lds_v, dist, n_plus, rr, part, N, c, mc, sp, l, o);
+  accumulate_dir<-1>(lds_v, dist, n_minus, rr, part, N, c, mc, sm, l, o);
   if (has0) {
-    u32x4 vf[8];
-    load_f32_half(lds_v, row, part, vf);
+    u32x4 vf[4];
+    load_f32_q(lds_v, rr, part, vf);
     const float p = fast_exp2(__builtin_fmaf(s0, c, -mc));
     l += p;
-    axpy_f32(o, p, vf);
+    axpy_q(o, p, vf);
   }
-  const float inv = 1.0f / l;
+  const float inv = any ? 1.0f / l : 0.f;
+  uint32_t w[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const __bf16 lo = static_cast<__bf16>(o[8 * t + 2 * u] * inv);
-      const __bf16 hi = static_cast<__bf16>(o[8 * t + 2 * u + 1] * inv);
-      w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-    }
-    orow[t] = u32x4{w[0], w[1], w[2], w[3]};
+  for (int u = 0; u < 8; ++u) {
+    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
+    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
+    w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
-  if (part == 0) a.lse[grow] = (mc + fast_log2(l)) * kLn2;
+  const float lse = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
+  // The next slab's loads complete before any store of this slab, so the
+  // commit after the next barrier waits for nothing.
+  settle(pf);
+  const size_t grow = static_cast<size_t>(slab) * N + rr;
+  u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes);
+  orow[part] = u32x4{w[0], w[1], w[2], w[3]};
+  orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
+  a.lse[grow] = lse;  // the row's four lanes write the same value
 }
 
 template <int MH>
-__global__ void __launch_bounds__(kThreads) fwd_slab_bf16_kernel(Args<MH> a) {
+__global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int row = 32 * wave + (lane & 31);
-  const int part = lane >> 5;
-  const int N = a.N;
-  char* lds_k = smem;
-  char* lds_v = smem + N * kBf16Stride;
-  // Rows of this wave: [32 w, min(32 w + 32, N)).
-  const int r0 = 32 * wave;
-  const int rl = (r0 + 31 < N ? r0 + 31 : N - 1);
+  const int row0 = 16 * wave + (lane & 15);
+  const int part0 = lane >> 4;
+  const int r0 = 16 * wave;
 
+  // The grid never exceeds the slab count.  The first slab's loads are
+  // completed before the loop, so the loop's first trip and later trips see
+  // the same pending memory operations.
   Prefetch pf;
   int slab = blockIdx.x;
-  if (slab < a.slabs) issue_prefetch(a, slab, tid, row, part, pf);
-  for (; slab < a.slabs; slab += gridDim.x) {
-    __syncthreads();  // the previous slab is no longer read from LDS
-    commit_prefetch(lds_k, lds_v, N, tid, pf);
-    u32x4 q[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) q[t] = pf.q[t];
-    __syncthreads();
-    const int next = slab + gridDim.x;
-    if (next < a.slabs) issue_prefetch(a, next, tid, row, part, pf);
-    if (r0 < N) {
-      const HeadRecord hr = unpack_record(a.rec[slab % a.H]);
-      // Displacements +f are useful to this wave while r0 + f < N, and -f
-      // while f <= rl; both are prefixes of the ascending distance list.
-      int n_plus = 0, n_minus = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxPos; ++i) {
-        if (i < hr.npos) {
-          n_plus += (r0 + hr.pos[i] < N) ? 1 : 0;
-          n_minus += (hr.pos[i] <= rl) ? 1 : 0;
-        }
-      }
-      if (row < N)
-        attend_row(a, slab, row, part, lds_k, lds_v, hr.pos, n_plus, n_minus, hr.has0, q);
+  issue_prefetch(a, a.N, slab, tid, row0, part0, false, pf);
+  settle(pf);
+  // Waves whose rows all lie past the sequence only help stage the slabs;
+  // they run a loop of their own (same barriers) so that the loop of the
+  // working waves has no store-free path.
+  if (r0 < a.N) {
+    for (; slab < a.slabs; slab += gridDim.x) {
+      // Opaque per-slab copies of N and of the lane's row and part keep the
+      // address arithmetic inside the loop instead of hoisted into registers.
+      int N = a.N;
+      asm volatile("" : "+s"(N));
+      int row = row0, part = part0;
+      asm volatile("" : "+v"(row), "+v"(part));
+      char* lds_k = smem;
+      char* lds_v = smem + N * kBf16Stride;
+      char* lds_q = smem + N * (kBf16Stride + kF32Stride);
+      __syncthreads();  // the previous slab is no longer read from LDS
+      commit_prefetch(lds_k, lds_v, lds_q, N, tid, pf);
+      __syncthreads();
+      const int next = slab + gridDim.x;
+      issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
+      attend_slab(a, slab, N, row, part, r0, lds_k, lds_v, lds_q, pf);
+    }
+  } else {
+    for (; slab < a.slabs; slab += gridDim.x) {
+      int N = a.N;
+      asm volatile("" : "+s"(N));
+      __syncthreads();
+      commit_prefetch(smem, smem + N * kBf16Stride, smem + N * (kBf16Stride + kF32Stride), N, tid,
+                      pf);
+      __syncthreads();
+      const int next = slab + gridDim.x;
+      issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
     }
   }
 }
@@ -265,22 +302,23 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.slabs = p.B * p.H;
   a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
-  const size_t lds = static_cast<size_t>(p.N) * (kBf16Stride + kF32Stride);
+  const size_t lds = static_cast<size_t>(p.N) * (2 * kBf16Stride + kF32Stride);
   auto kern = fwd_slab_bf16_kernel<MH>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kMaxRows * (kBf16Stride + kF32Stride));
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kRowsF * (2 * kBf16Stride + kF32Stride));
   if (attr != hipSuccess) return attr;
   const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsF), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool fwd_slab_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kMaxRows && records_fit(p);
+  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kRowsF && records_fit(p);
 }
 
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,

@@ -281,6 +281,23 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   int slab = blockIdx.x;
   issue_prefetch(a, a.N, slab, tid, row0, part0, false, pf);
   settle(pf);
+  // Waves whose rows all lie past the sequence only help stage the slabs;
+  // they run a loop of their own with the same barriers.
+  if (r0 >= a.N) {
+    for (; slab < a.slabs; slab += gridDim.x) {
+      int N = a.N;
+      asm volatile("" : "+s"(N));
+      __syncthreads();
+      commit_kv(smem, smem + N * kBf16Stride, smem + 2 * N * kBf16Stride, N, tid, pf);
+      __syncthreads();
+      const int next = slab + gridDim.x;
+      issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
+      settle(pf);
+      __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
   for (; slab < a.slabs; slab += gridDim.x) {
     // Opaque per-slab copies of N and of the lane's row and part keep the
     // address arithmetic inside the loop instead of hoisted into registers.

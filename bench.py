@@ -54,8 +54,8 @@ def _bytes(wl, esize):
 # Dominant kernel on this workload for each pass, and the source files whose
 # hash identifies the build its HBM counters were taken on.
 KERNELS = {
-    "fwd": ("fwd_slab_bf16_kernel", ["fwd_slab_bf16.hip"]),
-    "bwd": ("bwd_slab_kernel", ["bwd.hip"]),
+    "fwd": ("fwd_slab_bf16_kernel", ["fwd_slab_bf16.hip", "slab_bf16_common.h"]),
+    "bwd": ("bwd_slab_bf16_kernel", ["bwd_slab_bf16.hip", "slab_bf16_common.h"]),
 }
 
 

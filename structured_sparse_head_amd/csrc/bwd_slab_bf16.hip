@@ -12,8 +12,9 @@
 //
 // Lanes.  1024 threads (16 waves, four per SIMD so that LDS and arithmetic
 // latency is hidden by other waves); four lanes own a row: lane l of wave w
-// works on row 16 w + (l % 16) and, with p = l / 16, on the element groups
-// {4 g .. 4 g + 3} for g = p, p + 4, p + 8, p + 12.  The four lanes of a row
+// works on row 16 w + (l % 16) and, with p = (l / 16 + (l % 16) / 4) mod 4
+// (see slab_bf16_common.h), on the element groups {4 g .. 4 g + 3} for
+// g = p, p + 4, p + 8, p + 12.  The four lanes of a row
 // therefore cover each 64-byte span of an fp32 output row together, so every
 // global store instruction writes whole 64-byte pieces.  LDS rows are kept
 // permuted (each lane's 16 elements contiguous, in that group order) so a
@@ -72,14 +73,16 @@ struct Args {
   u32x4 rec[MH];
 };
 
-// Writes this lane's 16 bf16 elements (packed in w) as fp32 to an LDS row.
+// Writes this lane's 16 bf16 elements (packed in w, groups p, p + 4, p + 8,
+// p + 12) as fp32 to logical chunks 4 p .. 4 p + 3 of an LDS row.
 __device__ __forceinline__ void store_f32_q_lds(char* base, int r, int part,
                                                 const uint32_t (&w)[8]) {
-  u32x4* p = reinterpret_cast<u32x4*>(base + r * kF32Stride + part * 64);
+  const int o = f32_chunk(r, 4 * part);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    p[t] = u32x4{w[2 * t] << 16, w[2 * t] & 0xffff0000u, w[2 * t + 1] << 16,
-                 w[2 * t + 1] & 0xffff0000u};
+    *reinterpret_cast<u32x4*>(base + o + (t << 4)) =
+        u32x4{w[2 * t] << 16, w[2 * t] & 0xffff0000u, w[2 * t + 1] << 16,
+              w[2 * t + 1] & 0xffff0000u};
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -138,19 +141,21 @@ __device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, char* lds_kf
   for (int c = 0; c < kChunksB; ++c) {
     const int idx = tid + c * kThreadsB;
     if (idx < chunks) {
-      // Chunk ch of row r holds element groups 2 ch and 2 ch + 1; group g goes
-      // to lane part g % 4, slot g / 4 of the permuted row.
+      // Chunk ch of row r holds element groups 2 ch and 2 ch + 1 (4 elements
+      // each).  Group g belongs to lane part g % 4, slot m = g / 4: in bf16
+      // it is half m % 2 of logical chunk 2 (g % 4) + m / 2, in fp32 logical
+      // chunk 4 (g % 4) + m.
       const int r = idx >> 3, ch = idx & 7;
       const int g0 = 2 * ch, g1 = 2 * ch + 1;
-      const int b0 = r * kBf16Stride + (g0 & 3) * 32 + (g0 >> 2) * 8;
-      const int b1 = r * kBf16Stride + (g1 & 3) * 32 + (g1 >> 2) * 8;
+      const int b0 = b16_chunk(r, 2 * (g0 & 3) + (g0 >> 3)) + ((g0 >> 2) & 1) * 8;
+      const int b1 = b16_chunk(r, 2 * (g1 & 3) + (g1 >> 3)) + ((g1 >> 2) & 1) * 8;
       const u32x4 xk = pf.k[c], xv = pf.v[c];
       *reinterpret_cast<uint2*>(lds_k + b0) = make_uint2(xk.x, xk.y);
       *reinterpret_cast<uint2*>(lds_k + b1) = make_uint2(xk.z, xk.w);
       *reinterpret_cast<uint2*>(lds_v + b0) = make_uint2(xv.x, xv.y);
       *reinterpret_cast<uint2*>(lds_v + b1) = make_uint2(xv.z, xv.w);
-      char* f0 = lds_kf + r * kF32Stride + (g0 & 3) * 64 + (g0 >> 2) * 16;
-      char* f1 = lds_kf + r * kF32Stride + (g1 & 3) * 64 + (g1 >> 2) * 16;
+      char* f0 = lds_kf + f32_chunk(r, 4 * (g0 & 3) + (g0 >> 2));
+      char* f1 = lds_kf + f32_chunk(r, 4 * (g1 & 3) + (g1 >> 2));
       *reinterpret_cast<u32x4*>(f0) =
           u32x4{xk.x << 16, xk.x & 0xffff0000u, xk.y << 16, xk.y & 0xffff0000u};
       *reinterpret_cast<u32x4*>(f1) =
@@ -270,7 +275,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int row0 = 16 * wave + (lane & 15);
-  const int part0 = lane >> 4;
+  const int part0 = lane_part(lane);
   const int r0 = 16 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are

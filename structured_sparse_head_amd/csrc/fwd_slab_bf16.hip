@@ -9,8 +9,9 @@
 //
 //  * Lanes.  1024 threads (16 waves, four per SIMD so that LDS and
 //    arithmetic latency is hidden by other waves); four lanes own a row:
-//    lane l of wave w works on row 16 w + (l % 16) and, with p = l / 16, on
-//    the 8-element groups p and p + 4.  The four lanes of a row thus cover
+//    lane l of wave w works on row 16 w + (l % 16) and, with
+//    p = (l / 16 + (l % 16) / 4) mod 4 (see slab_bf16_common.h), on the
+//    8-element groups p and p + 4.  The four lanes of a row thus cover
 //    each 64-byte half of the bf16 output row together, so every store
 //    instruction writes whole 64-byte pieces.  LDS rows are kept permuted
 //    (each lane's 16 elements contiguous) so a lane reads its fragment with
@@ -91,8 +92,9 @@ __device__ __forceinline__ void settle(const Prefetch& pf) {
   for (int c = 0; c < kChunksF; ++c) asm volatile("" ::"v"(pf.k[c]), "v"(pf.v[c]), "v"(pf.q[c]));
 }
 
-// Chunk ch (8 elements) of row r is element group ch: it goes to lane part
-// ch % 4, slot ch / 4 of the permuted row; V is widened to fp32.
+// Chunk ch (8 elements) of row r is element group ch: it becomes logical
+// chunk 2 (ch % 4) + ch / 4 of the permuted bf16 row (lane part ch % 4); in
+// fp32 it takes logical chunks 4 (ch % 4) + 2 (ch / 4) and the next one.
 __device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, char* lds_q, int N,
                                                 int tid, const Prefetch& pf) {
   const int chunks = N * (kRowBytes / 16);
@@ -102,13 +104,14 @@ __device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, char* 
     if (idx < chunks) {
       const int r = idx >> 3;
       const int ch = idx & 7;
-      const int kb = r * kBf16Stride + (ch & 3) * 32 + (ch >> 2) * 16;
+      const int kb = b16_chunk(r, 2 * (ch & 3) + (ch >> 2));
       *reinterpret_cast<u32x4*>(lds_k + kb) = pf.k[c];
       *reinterpret_cast<u32x4*>(lds_q + kb) = pf.q[c];
       const u32x4 x = pf.v[c];
-      char* vp = lds_v + r * kF32Stride + (ch & 3) * 64 + (ch >> 2) * 32;
-      *reinterpret_cast<u32x4*>(vp) = u32x4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
-      *reinterpret_cast<u32x4*>(vp + 16) =
+      const int vb = f32_chunk(r, 4 * (ch & 3) + 2 * (ch >> 2));
+      *reinterpret_cast<u32x4*>(lds_v + vb) =
+          u32x4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
+      *reinterpret_cast<u32x4*>(lds_v + (vb + 16)) =
           u32x4{x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
     }
   }
@@ -243,7 +246,7 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int row0 = 16 * wave + (lane & 15);
-  const int part0 = lane >> 4;
+  const int part0 = lane_part(lane);
   const int r0 = 16 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are

@@ -1,19 +1,22 @@
 // Pieces shared by the persistent slab kernels for bf16, d_h = 64 and short
-// sequences (N <= 256): lane layout, LDS row strides, fragment loads, the
-// two-lane dot product and the per-head distance records.
+// sequences (N <= 256): LDS row layout, fragment loads, the four-lane dot
+// product and the per-head distance records.
 //
-// Lanes.  Two lanes own a row, each holding 32 of its 64 elements: lanes
-// 0-31 of a wave take the first halves of 32 consecutive rows and lanes
-// 32-63 the second halves, so one v_permlane32_swap plus one add completes a
-// dot product.
+// Lanes.  Four lanes own a row (lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave);
+// each holds 16 of its 64 elements, so v_permlane32_swap and
+// v_permlane16_swap sums complete a dot product.
 //
-// LDS strides.  bf16 rows use 144 bytes and fp32 rows 272 bytes, both an odd
-// number of 16-byte units.  Measured on gfx950 (64 banks), a ds_read_b128
-// serves the two 32-lane halves of a wave separately and, within a half, the
-// lane quads whose index has even popcount ({0-3, 12-15, 20-23, 24-27})
-// together and the odd ones together.  Each such group reads 16 rows that
-// are distinct modulo 16, and an odd stride maps them to 16 distinct 16-byte
-// bank groups: no conflicts.
+// LDS rows.  bf16 rows take 144 bytes and fp32 rows 272 bytes (an odd
+// number of 16-byte units); a lane's 16 elements are chunks 2 p, 2 p + 1
+// (bf16) or 4 p .. 4 p + 3 (fp32) of its row for lane part p.  Measured on
+// gfx950 (64 banks), a ds_read_b128 serves the two 32-lane halves of a wave
+// separately and, within a half, the lane quads whose index has even
+// popcount ({0-3, 12-15, 20-23, 24-27}) together and the odd ones together.
+// With part = (l / 16 + (l % 16) / 4) mod 4 for lane l (the row's four lanes
+// still hold four different parts), every such group of an fp32 read hits 16
+// distinct 16-byte bank groups for any first row: no conflicts, found by
+// exhaustive search.  No part assignment makes the bf16 reads conflict-free
+// as well; they keep two-way conflicts on half the traffic.
 #pragma once
 
 #include "fib_offsets.h"
@@ -23,13 +26,18 @@
 namespace fibatt {
 namespace slab {
 
-constexpr int kThreads = 512;        // 8 waves; 256 rows at 2 lanes per row
-constexpr int kMaxRows = kThreads / 2;
+constexpr int kMaxRows = 256;        // rows a workgroup covers (16 waves x 16)
 constexpr int kMaxPos = 12;          // positive distances below 256: at most 1,2,3,5,...,233
 constexpr int kBf16Stride = 144;     // bytes per bf16 row of 64 in LDS (128 + 16)
 constexpr int kF32Stride = 272;      // bytes per fp32 row of 64 in LDS (256 + 16)
 constexpr int kRowBytes = 128;       // bf16 row of 64 elements in HBM
-constexpr int kChunksPerThread = kMaxRows * (kRowBytes / 16) / kThreads;  // 4
+
+// Byte offset of 16-byte chunk c of LDS row r.
+__device__ __forceinline__ int b16_chunk(int r, int c) { return __umul24(r, kBf16Stride) + c * 16; }
+__device__ __forceinline__ int f32_chunk(int r, int c) { return __umul24(r, kF32Stride) + c * 16; }
+
+// Part (which 16 of the 64 elements) lane l of a wave works on.
+__device__ __forceinline__ int lane_part(int lane) { return ((lane >> 4) + ((lane & 15) >> 2)) & 3; }
 
 // Sum of x over the lane pair (l, l ^ 32).
 __device__ __forceinline__ float pair_sum(float x) {
@@ -40,97 +48,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ int clamp_row(int r, int N) { return r < 0 ? 0 : (r >= N ? N - 1 : r); }
 
-// This lane's half (32 bf16 = 64 bytes) of LDS row r.
-__device__ __forceinline__ void load_bf16_half(const char* base, int r, int part, u32x4 (&f)[4]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kBf16Stride) + part * 64);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) f[t] = p[t];
-}
-
-// This lane's half (32 fp32 = 128 bytes) of LDS row r.
-__device__ __forceinline__ void load_f32_half(const char* base, int r, int part, u32x4 (&f)[8]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kF32Stride) + part * 128);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) f[t] = p[t];
-}
-
-__device__ __forceinline__ void unpack_words(const u32x4 (&x)[4], uint32_t (&w)[16]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    w[4 * t + 0] = x[t].x;
-    w[4 * t + 1] = x[t].y;
-    w[4 * t + 2] = x[t].z;
-    w[4 * t + 3] = x[t].w;
-  }
-}
-
 // First product of an accumulation chain: v_dot2_f32_bf16 with an inline
 // zero addend (the builtin with a literal 0 would add a register move).
 __device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
   float r;
   asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
   return r;
-}
-
-// Full 64-element dot product of two bf16 rows split over the lane pair,
-// accumulated in fp32.
-__device__ __forceinline__ float dot_bf16(const uint32_t (&a)[16], const u32x4 (&b)[4]) {
-  float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
-                  dot2_first(a[3], b[0].w)};
-#pragma unroll
-  for (int t = 1; t < 4; ++t) {
-    const uint32_t bw[4] = {b[t].x, b[t].y, b[t].z, b[t].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[4 * t + u]),
-                                               __builtin_bit_cast(bf16x2_t, bw[u]), acc[u], false);
-  }
-  return pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-}
-
-// acc += p * x for this lane's 32 fp32 elements.
-__device__ __forceinline__ void axpy_f32(float (&acc)[32], float p, const u32x4 (&x)[8]) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    acc[4 * t + 0] = __builtin_fmaf(p, __uint_as_float(x[t].x), acc[4 * t + 0]);
-    acc[4 * t + 1] = __builtin_fmaf(p, __uint_as_float(x[t].y), acc[4 * t + 1]);
-    acc[4 * t + 2] = __builtin_fmaf(p, __uint_as_float(x[t].z), acc[4 * t + 2]);
-    acc[4 * t + 3] = __builtin_fmaf(p, __uint_as_float(x[t].w), acc[4 * t + 3]);
-  }
-}
-
-// acc += p * x for this lane's 32 bf16 elements (widened exactly to fp32).
-__device__ __forceinline__ void axpy_bf16(float (&acc)[32], float p, const u32x4 (&x)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t w[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[8 * t + 2 * u] = __builtin_fmaf(p, __uint_as_float(w[u] << 16), acc[8 * t + 2 * u]);
-      acc[8 * t + 2 * u + 1] =
-          __builtin_fmaf(p, __uint_as_float(w[u] & 0xffff0000u), acc[8 * t + 2 * u + 1]);
-    }
-  }
-}
-
-// Writes this lane's 32 bf16 elements (packed in w) as fp32 to an LDS row.
-__device__ __forceinline__ void store_f32_half_from_bf16(char* base, int r, int part,
-                                                         const uint32_t (&w)[16]) {
-  u32x4* p = reinterpret_cast<u32x4*>(base + r * kF32Stride + part * 128);
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    p[t] = u32x4{w[2 * t] << 16, w[2 * t] & 0xffff0000u, w[2 * t + 1] << 16,
-                 w[2 * t + 1] & 0xffff0000u};
-}
-
-// Writes this lane's 32 fp32 elements times `scale` to a global row.
-__device__ __forceinline__ void store_f32_half_global(float* row, int part, const float (&x)[32],
-                                                      float scale) {
-  float4* p = reinterpret_cast<float4*>(row) + part * 8;
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    p[t] = make_float4(x[4 * t] * scale, x[4 * t + 1] * scale, x[4 * t + 2] * scale,
-                       x[4 * t + 3] * scale);
 }
 
 // ---- Four lanes per row (1024-thread kernels) ----------------------------
@@ -143,18 +66,20 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// This lane's quarter (16 bf16 = 32 bytes) of a bf16 LDS row.
+// This lane's quarter (16 bf16 = 32 bytes, chunks 2 p and 2 p + 1) of a bf16
+// LDS row.
 __device__ __forceinline__ void load_bf16_q(const char* base, int r, int part, u32x4 (&f)[2]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kBf16Stride) + part * 32);
-  f[0] = p[0];
-  f[1] = p[1];
+  const u32x4* q = reinterpret_cast<const u32x4*>(base + b16_chunk(r, 2 * part));
+  f[0] = q[0];
+  f[1] = q[1];
 }
 
-// This lane's quarter (16 fp32 = 64 bytes) of an fp32 LDS row.
+// This lane's quarter (16 fp32 = 64 bytes, chunks 4 p .. 4 p + 3) of an fp32
+// LDS row.
 __device__ __forceinline__ void load_f32_q(const char* base, int r, int part, u32x4 (&f)[4]) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + __umul24(r, kF32Stride) + part * 64);
+  const u32x4* q = reinterpret_cast<const u32x4*>(base + f32_chunk(r, 4 * part));
 #pragma unroll
-  for (int t = 0; t < 4; ++t) f[t] = p[t];
+  for (int t = 0; t < 4; ++t) f[t] = q[t];
 }
 
 // Full 64-element dot product of two bf16 rows split over the row's four
@@ -194,22 +119,6 @@ struct Dist {
 // Per-head record handed to the kernels in their arguments: bytes 0..11 are
 // the ascending positive distances, byte 12 their count, byte 13 whether 0
 // is a distance.  Sixteen bytes per head.
-struct HeadRecord {
-  int pos[kMaxPos];
-  int npos;
-  bool has0;
-};
-
-__device__ __forceinline__ HeadRecord unpack_record(const u32x4& rec) {
-  HeadRecord r;
-  const uint32_t w[4] = {rec.x, rec.y, rec.z, rec.w};
-  r.npos = static_cast<int>(w[3] & 0xffu);
-  r.has0 = ((w[3] >> 8) & 0xffu) != 0;
-#pragma unroll
-  for (int i = 0; i < kMaxPos; ++i) r.pos[i] = static_cast<int>((w[i >> 2] >> (8 * (i & 3))) & 0xffu);
-  return r;
-}
-
 // Host: the record of every head h < H (zero for h >= H, up to MH).  Returns
 // false when a head has more positive distances than kMaxPos (or N > 256).
 inline bool pack_records(const Problem& p, u32x4* rec, int MH) {

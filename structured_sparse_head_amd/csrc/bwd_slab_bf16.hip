@@ -208,8 +208,8 @@ __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v,
   u32x4 ka[2], va[2], kb[2], vb[2];
   auto load = [&](int i, u32x4 (&kf)[2], u32x4 (&vf)[2]) {
     const int r = clamp_row(row + SGN * dist.at(i), N);
-    load_bf16_q(lds_k, r, part, kf);
-    load_bf16_q(lds_v, r, part, vf);
+    load_bf16_q(lds_k + part * 32, r, kf);
+    load_bf16_q(lds_v + part * 32, r, vf);
   };
   auto step = [&](int i, const u32x4 (&kf)[2], const u32x4 (&vf)[2]) {
     const int kk = row + SGN * dist.at(i);
@@ -240,7 +240,7 @@ __device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist di
   float2* e0 = tbl + trow * kTableCols + base;
   for (int i = 0; i < n; ++i) {
     u32x4 kf[4];
-    load_f32_q(lds_kf, clamp_row(row + SGN * dist.at(i), N), part, kf);
+    load_f32_q(lds_kf + part * 64, clamp_row(row + SGN * dist.at(i), N), kf);
     const float2 e = e0[i];
     const float ds = e.x * (e.y - d);
     axpy_q(acc, ds, kf);
@@ -260,7 +260,7 @@ __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, D
     const int j = k - SGN * dist.at(i);
     const int jc = clamp_row(j, N);
     u32x4 xf[4];
-    load_f32_q(lds_x, jc, part, xf);
+    load_f32_q(lds_x + part * 64, jc, xf);
     const float2 t = tbl[jc * kTableCols + base + i];
     const bool ok = static_cast<unsigned>(j) < static_cast<unsigned>(N);
     tk.tick();
@@ -363,8 +363,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
                      wr, d);
       if (has0) {
         u32x4 kb[2], vb[2];
-        load_bf16_q(lds_k, rr, part, kb);
-        load_bf16_q(lds_v, rr, part, vb);
+        load_bf16_q(lds_k + part * 32, rr, kb);
+        load_bf16_q(lds_v + part * 32, rr, vb);
         const float s = dot_q(qw, kb);
         const float dp = dot_q(dw, vb);
         const float p = fast_exp2(__builtin_fmaf(s, a.c, -lse2));
@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, dqa);
       if (has0) {
         u32x4 kf[4];
-        load_f32_q(lds_kf, rr, part, kf);
+        load_f32_q(lds_kf + part * 64, rr, kf);
         const float2 e = tbl[row * kTableCols + z];
         const float ds = e.x * (e.y - d);
         axpy_q(dqa, ds, kf);
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       key_pass<-1, 0>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, pq);
       if (has0) {
         u32x4 xb[4];
-        load_f32_q(lds_do, rr, part, xb);
+        load_f32_q(lds_do + part * 64, rr, xb);
         axpy_q(acc, tbl[rr * kTableCols + z].x, xb);
       }
       pq.flush();
@@ -418,7 +418,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       key_pass<-1, 1>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, pv);
       if (has0) {
         u32x4 xb[4];
-        load_f32_q(lds_q, rr, part, xb);
+        load_f32_q(lds_q + part * 64, rr, xb);
         axpy_q(acc2, tbl[rr * kTableCols + z].y, xb);
       }
       pv.flush();

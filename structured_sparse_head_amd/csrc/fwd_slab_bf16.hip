@@ -126,16 +126,16 @@ __device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, 
   u32x4 ka[2], kb[2];
 #pragma unroll
   for (int i = 0; i < kMaxPos; ++i) s[i] = -INFINITY;
-  if (n > 0) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(0), N), part, ka);
+  if (n > 0) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(0), N), ka);
 #pragma unroll
   for (int i = 0; i < kMaxPos; i += 2) {
     if (i < n) {
-      if (i + 1 < n) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(i + 1), N), part, kb);
+      if (i + 1 < n) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 1), N), kb);
       const int k0 = row + SGN * dist.at(i);
       const float d0 = dot_q(qw, ka);
       s[i] = (static_cast<unsigned>(k0) < static_cast<unsigned>(N)) ? d0 : -INFINITY;
       if (i + 1 < n) {
-        if (i + 2 < n) load_bf16_q(lds_k, clamp_row(row + SGN * dist.at(i + 2), N), part, ka);
+        if (i + 2 < n) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 2), N), ka);
         const int k1 = row + SGN * dist.at(i + 1);
         const float d1 = dot_q(qw, kb);
         s[i + 1] = (static_cast<unsigned>(k1) < static_cast<unsigned>(N)) ? d1 : -INFINITY;
@@ -153,7 +153,7 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int
   // latency.
   for (int i = 0; i < n; ++i) {
     u32x4 vf[4];
-    load_f32_q(lds_v, clamp_row(row + SGN * dist.at(i), N), part, vf);
+    load_f32_q(lds_v + part * 64, clamp_row(row + SGN * dist.at(i), N), vf);
     const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
     l += p;
     axpy_q(o, p, vf);
@@ -175,7 +175,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   uint32_t qw[8];
   {
     u32x4 qf[2];
-    load_bf16_q(lds_q, rr, part, qf);
+    load_bf16_q(lds_q + part * 32, rr, qf);
     qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
     qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
@@ -195,7 +195,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   float s0 = -INFINITY;
   if (has0) {
     u32x4 kf[2];
-    load_bf16_q(lds_k, rr, part, kf);
+    load_bf16_q(lds_k + part * 32, rr, kf);
     s0 = dot_q(qw, kf);
   }
   float m = s0;
@@ -214,7 +214,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   accumulate_dir<-1>(lds_v, dist, n_minus, rr, part, N, c, mc, sm, l, o);
   if (has0) {
     u32x4 vf[4];
-    load_f32_q(lds_v, rr, part, vf);
+    load_f32_q(lds_v + part * 64, rr, vf);
     const float p = fast_exp2(__builtin_fmaf(s0, c, -mc));
     l += p;
     axpy_q(o, p, vf);

@@ -46,7 +46,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ int clamp_row(int r, int N) { return r < 0 ? 0 : (r >= N ? N - 1 : r); }
+// Row r clamped into [0, N - 1] (one v_med3_i32; the compiler would emit a
+// max and a min).
+__device__ __forceinline__ int clamp_row(int r, int N) {
+  int c;
+  asm("v_med3_i32 %0, %1, 0, %2" : "=v"(c) : "v"(r), "s"(N - 1));
+  return c;
+}
 
 // First product of an accumulation chain: v_dot2_f32_bf16 with an inline
 // zero addend (the builtin with a literal 0 would add a register move).
@@ -66,18 +72,18 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// This lane's quarter (16 bf16 = 32 bytes, chunks 2 p and 2 p + 1) of a bf16
-// LDS row.
-__device__ __forceinline__ void load_bf16_q(const char* base, int r, int part, u32x4 (&f)[2]) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(base + b16_chunk(r, 2 * part));
+// This lane's quarter (16 bf16 = 32 bytes) of bf16 LDS row r; `base` already
+// points at the lane's part of row 0 (array base + 32 p).
+__device__ __forceinline__ void load_bf16_q(const char* base, int r, u32x4 (&f)[2]) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(base + __umul24(r, kBf16Stride));
   f[0] = q[0];
   f[1] = q[1];
 }
 
-// This lane's quarter (16 fp32 = 64 bytes, chunks 4 p .. 4 p + 3) of an fp32
-// LDS row.
-__device__ __forceinline__ void load_f32_q(const char* base, int r, int part, u32x4 (&f)[4]) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(base + f32_chunk(r, 4 * part));
+// This lane's quarter (16 fp32 = 64 bytes) of fp32 LDS row r; `base` already
+// points at the lane's part of row 0 (array base + 64 p).
+__device__ __forceinline__ void load_f32_q(const char* base, int r, u32x4 (&f)[4]) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(base + __umul24(r, kF32Stride));
 #pragma unroll
   for (int t = 0; t < 4; ++t) f[t] = q[t];
 }

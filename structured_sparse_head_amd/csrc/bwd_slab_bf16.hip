@@ -12,7 +12,8 @@
 //
 // Lanes.  1024 threads (16 waves, four per SIMD so that LDS and arithmetic
 // latency is hidden by other waves); four lanes own a row: lane l of wave w
-// works on row 16 w + (l % 16) and, with p = (l / 16 + (l % 16) / 4) mod 4
+// works on row 16 b_w + (l % 16), b_w the wave's row block (plan_blocks),
+// and, with p = (l / 16 + (l % 16) / 4) mod 4
 // (see slab_bf16_common.h), on the element groups {4 g .. 4 g + 3} for
 // g = p, p + 4, p + 8, p + 12.  The four lanes of a row
 // therefore cover each 64-byte span of an fp32 output row together, so every
@@ -70,6 +71,7 @@ struct Args {
   int slabs;
   float c;      // log2(e) / sqrt(64)
   float scale;  // 1 / sqrt(64)
+  uint64_t blocks;  // row block of wave w in bits 4 w .. 4 w + 3
   u32x4 rec[MH];
 };
 
@@ -274,9 +276,9 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int row0 = 16 * wave + (lane & 15);
+  const int r0 = 16 * static_cast<int>((a.blocks >> (4 * wave)) & 15u);
+  const int row0 = r0 + (lane & 15);
   const int part0 = lane_part(lane);
-  const int r0 = 16 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are
   // completed before the loop so that the loop's first trip and later trips
@@ -449,6 +451,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.scale = 0.125f;  // 1 / sqrt(64)
   a.c = kLog2e * 0.125f;
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
+  a.blocks = plan_blocks(p.N, p.H, a.rec);
   const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes;
   auto kern = bwd_slab_bf16_kernel<MH>;
   static const hipError_t attr = hipFuncSetAttribute(

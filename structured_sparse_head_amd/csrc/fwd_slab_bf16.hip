@@ -9,7 +9,8 @@
 //
 //  * Lanes.  1024 threads (16 waves, four per SIMD so that LDS and
 //    arithmetic latency is hidden by other waves); four lanes own a row:
-//    lane l of wave w works on row 16 w + (l % 16) and, with
+//    lane l of wave w works on row 16 b_w + (l % 16), where b_w is the
+//    wave's row block (plan_blocks), and, with
 //    p = (l / 16 + (l % 16) / 4) mod 4 (see slab_bf16_common.h), on the
 //    8-element groups p and p + 4.  The four lanes of a row thus cover
 //    each 64-byte half of the bf16 output row together, so every store
@@ -55,6 +56,7 @@ struct Args {
   int N;
   int slabs;
   float scale_log2;
+  uint64_t blocks;  // row block of wave w in bits 4 w .. 4 w + 3
   u32x4 rec[MH];
 };
 
@@ -245,9 +247,9 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int row0 = 16 * wave + (lane & 15);
+  const int r0 = 16 * static_cast<int>((a.blocks >> (4 * wave)) & 15u);
+  const int row0 = r0 + (lane & 15);
   const int part0 = lane_part(lane);
-  const int r0 = 16 * wave;
 
   // The grid never exceeds the slab count.  The first slab's loads are
   // completed before the loop, so the loop's first trip and later trips see
@@ -305,6 +307,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.slabs = p.B * p.H;
   a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
+  a.blocks = plan_blocks(p.N, p.H, a.rec);
   const size_t lds = static_cast<size_t>(p.N) * (2 * kBf16Stride + kF32Stride);
   auto kern = fwd_slab_bf16_kernel<MH>;
   static const hipError_t attr =

@@ -23,6 +23,9 @@
 #include "kernel_common.h"
 #include "launch.h"
 
+#include <algorithm>
+#include <cstring>
+
 namespace fibatt {
 namespace slab {
 
@@ -156,6 +159,132 @@ inline bool pack_records(const Problem& p, u32x4* rec, int MH) {
 inline bool records_fit(const Problem& p) {
   u32x4 tmp[kMaxHeads];
   return p.H <= kMaxHeads && pack_records(p, tmp, p.H);
+}
+
+// Row blocks.  A workgroup's 16 waves each take one block of 16 rows, and
+// wave w runs on SIMD w mod 4, so the four SIMDs share the rows of a slab.
+// Blocks near either end of the sequence have fewer in-range distances than
+// the middle ones; with 13 blocks (N = 197), say, one SIMD gets four of them
+// and the other three get three.  plan_blocks picks which block each wave
+// takes so that, summed over the heads, the busiest SIMD has as little work
+// as a move-and-swap local search finds (from the plain block = wave
+// assignment and from a greedy largest-first one).  Four bits per wave;
+// blocks past the sequence mark idle waves.
+namespace plan_detail {
+constexpr int kBlocks = 16;
+constexpr int kSimds = 4;
+constexpr int kBlockFixed = 3;  // per-block work besides the distances, in distance steps
+
+struct Plan {
+  int n[kSimds];
+  int8_t b[kSimds][4];
+};
+
+inline long plan_score(const Plan& g, const int (*cost)[kBlocks], int H) {
+  long s = 0;
+  for (int h = 0; h < H; ++h) {
+    int m = 0;
+    for (int i = 0; i < kSimds; ++i) {
+      int l = 0;
+      for (int j = 0; j < g.n[i]; ++j) l += cost[h][g.b[i][j]];
+      m = l > m ? l : m;
+    }
+    s += m;
+  }
+  return s;
+}
+
+// Moves of one block to another SIMD and swaps of two blocks, while any
+// lowers the score.
+inline long plan_improve(Plan& g, const int (*cost)[kBlocks], int H) {
+  long best = plan_score(g, cost, H);
+  for (bool changed = true; changed;) {
+    changed = false;
+    for (int s1 = 0; s1 < kSimds; ++s1)
+      for (int s2 = 0; s2 < kSimds; ++s2) {
+        if (s1 == s2) continue;
+        for (int i = 0; i < g.n[s1]; ++i)
+          for (int j = 0; j <= g.n[s2]; ++j) {
+            Plan t = g;
+            if (j < g.n[s2]) {  // swap
+              const int8_t x = t.b[s1][i];
+              t.b[s1][i] = t.b[s2][j];
+              t.b[s2][j] = x;
+            } else {  // move
+              if (t.n[s2] == 4) continue;
+              t.b[s2][t.n[s2]++] = t.b[s1][i];
+              t.b[s1][i] = t.b[s1][--t.n[s1]];
+            }
+            const long sc = plan_score(t, cost, H);
+            if (sc < best) {
+              best = sc;
+              g = t;
+              changed = true;
+            }
+          }
+      }
+  }
+  return best;
+}
+}  // namespace plan_detail
+
+inline uint64_t plan_blocks(int N, int H, const u32x4* rec) {
+  using namespace plan_detail;
+  const int nb = (N + 15) / 16;
+  static thread_local int last_n = -1, last_h = -1;
+  static thread_local u32x4 last_rec[kMaxHeads];
+  static thread_local uint64_t last_plan = 0;
+  if (N == last_n && H == last_h && memcmp(rec, last_rec, sizeof(u32x4) * H) == 0)
+    return last_plan;
+
+  int cost[kMaxHeads][kBlocks] = {};
+  for (int h = 0; h < H; ++h) {
+    const int cnt = static_cast<int>(rec[h].w & 0xffu);
+    const uint32_t w[3] = {rec[h].x, rec[h].y, rec[h].z};
+    for (int b = 0; b < nb; ++b) {
+      const int r0 = 16 * b, rl = r0 + 15 < N ? r0 + 15 : N - 1;
+      int c = kBlockFixed;
+      for (int i = 0; i < cnt; ++i) {
+        const int f = static_cast<int>((w[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        c += (r0 + f < N ? 1 : 0) + (f <= rl ? 1 : 0);
+      }
+      cost[h][b] = c;
+    }
+  }
+  Plan plain = {}, greedy = {};
+  for (int b = 0; b < nb; ++b) plain.b[b % kSimds][plain.n[b % kSimds]++] = static_cast<int8_t>(b);
+  {
+    long tot[kBlocks] = {}, load[kSimds] = {};
+    int order[kBlocks];
+    for (int b = 0; b < nb; ++b) {
+      for (int h = 0; h < H; ++h) tot[b] += cost[h][b];
+      order[b] = b;
+    }
+    std::stable_sort(order, order + nb, [&](int x, int y) { return tot[x] > tot[y]; });
+    for (int k = 0; k < nb; ++k) {
+      int s = -1;
+      for (int i = 0; i < kSimds; ++i)
+        if (greedy.n[i] < 4 && (s < 0 || load[i] < load[s])) s = i;
+      greedy.b[s][greedy.n[s]++] = static_cast<int8_t>(order[k]);
+      load[s] += tot[order[k]];
+    }
+  }
+  const long sp = plan_improve(plain, cost, H);
+  const long sg = plan_improve(greedy, cost, H);
+  const Plan& g = sg < sp ? greedy : plain;
+
+  uint64_t plan = 0;
+  int idle = nb;
+  for (int w = 0; w < kBlocks; ++w) {
+    const int s = w % kSimds, slot = w / kSimds;
+    const int b = slot < g.n[s] ? g.b[s][slot] : idle++;
+    plan |= static_cast<uint64_t>(b) << (4 * w);
+  }
+  last_n = N;
+  last_h = H;
+  memcpy(last_rec, rec, sizeof(u32x4) * H);
+  last_plan = plan;
+  return plan;
 }
 
 // Compute units of the current device (cached per process).

@@ -41,6 +41,7 @@ using namespace slab;
 constexpr int kThreadsF = 1024;                                  // 16 waves
 constexpr int kRowsF = kThreadsF / 4;                            // 256 rows
 constexpr int kChunksF = kRowsF * (kRowBytes / 16) / kThreadsF;  // 2
+constexpr int kGroups = (kMaxPos + 3) / 4;                       // distance groups of four
 
 // Per-head record: bytes 0..11 the ascending positive distances, byte 12
 // their count, byte 13 whether 0 is a distance.  Built on the host; with at
@@ -119,46 +120,72 @@ __device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, char* 
   }
 }
 
-// Scores for displacements SGN * f_i, i < n (wave-uniform n).  Out-of-range
-// keys are read from a clamped row and scored -inf.  The next key fragment is
-// requested before the current dot product so LDS latency overlaps arithmetic.
+// Scores for displacements SGN * f_i, i < n (wave-uniform n), four
+// distances per group: each lane forms its partial dot products for the
+// group's four keys and one transposed reduction leaves the full score of
+// distance 4 g + slot in the lane of that slot (slot = (lane / 16) % 4).
+// Out-of-range keys and i >= n score -inf.  The next key fragment is
+// requested before the current dot product so LDS latency overlaps
+// arithmetic.
 template <int SGN>
 __device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, int row, int part,
-                                           int N, const uint32_t (&qw)[8], float (&s)[kMaxPos]) {
-  u32x4 ka[2], kb[2];
+                                           int slot, int N, const uint32_t (&qw)[8],
+                                           float (&s)[kGroups]) {
+  // One fragment variable per distance (not a two-entry ring): a fragment
+  // loaded under a condition then merges with nothing, so the compiler
+  // needs no register copies at the branch joins.
+  u32x4 kf[kMaxPos][2];
 #pragma unroll
-  for (int i = 0; i < kMaxPos; ++i) s[i] = -INFINITY;
-  if (n > 0) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(0), N), ka);
+  for (int g = 0; g < kGroups; ++g) s[g] = -INFINITY;
+  if (n > 0) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(0), N), kf[0]);
 #pragma unroll
-  for (int i = 0; i < kMaxPos; i += 2) {
-    if (i < n) {
-      if (i + 1 < n) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 1), N), kb);
-      const int k0 = row + SGN * dist.at(i);
-      const float d0 = dot_q(qw, ka);
-      s[i] = (static_cast<unsigned>(k0) < static_cast<unsigned>(N)) ? d0 : -INFINITY;
-      if (i + 1 < n) {
-        if (i + 2 < n) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 2), N), ka);
-        const int k1 = row + SGN * dist.at(i + 1);
-        const float d1 = dot_q(qw, kb);
-        s[i + 1] = (static_cast<unsigned>(k1) < static_cast<unsigned>(N)) ? d1 : -INFINITY;
+  for (int g = 0; g < kGroups; ++g) {
+    if (4 * g < n) {
+      float pd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        pd[j] = 0.f;
+        if (i < n) {
+          if (i + 1 < n)
+            load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 1), N), kf[i + 1]);
+          pd[j] = dot_part(qw, kf[i]);
+        }
       }
+      const float t = reduce4(pd);
+      const uint32_t w = g == 0 ? dist.w0 : (g == 1 ? dist.w1 : dist.w2);
+      const int k = row + SGN * static_cast<int>(__builtin_amdgcn_ubfe(w, 8 * slot, 8));
+      const bool ok = 4 * g + slot < n && static_cast<unsigned>(k) < static_cast<unsigned>(N);
+      s[g] = ok ? t : -INFINITY;
     }
   }
 }
 
+// P V for displacements SGN * f_i, i < n: each lane turns its own score of
+// a group into a probability, then the group's four are gathered to every
+// lane of the row.  l collects this lane's own probabilities only.
 template <int SGN>
 __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int n, int row,
                                                int part, int N, float c, float mc,
-                                               const float (&s)[kMaxPos], float& l,
+                                               const float (&s)[kGroups], float& l,
                                                float (&o)[16]) {
-  // Single-buffered: the other waves of the SIMD cover each step's LDS
-  // latency.
-  for (int i = 0; i < n; ++i) {
-    u32x4 vf[4];
-    load_f32_q(lds_v + part * 64, clamp_row(row + SGN * dist.at(i), N), vf);
-    const float p = fast_exp2(__builtin_fmaf(s[i], c, -mc));  // 0 for s = -inf
-    l += p;
-    axpy_q(o, p, vf);
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    if (4 * g < n) {
+      const float pown = fast_exp2(__builtin_fmaf(s[g], c, -mc));  // 0 for s = -inf
+      l += pown;
+      float p[4];
+      gather4(pown, p);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        if (i < n) {
+          u32x4 vf[4];
+          load_f32_q(lds_v + part * 64, clamp_row(row + SGN * dist.at(i), N), vf);
+          axpy_q(o, p[j], vf);
+        }
+      }
+    }
   }
 }
 
@@ -166,7 +193,8 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int
 // row repeat row N - 1 and store the same values, so the stores need no
 // branch and the memory wait counter stays exact around the loop.
 template <typename A>
-__device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row, int part, int r0,
+__device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row, int part, int slot,
+                                            int r0,
                                             const char* lds_k, const char* lds_v,
                                             const char* lds_q, Prefetch& pf) {
   const u32x4 rec = a.rec[slab % a.H];
@@ -190,19 +218,20 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
     n_plus += (r0 + f < N) ? 1 : 0;
     n_minus += (f <= rl) ? 1 : 0;
   }
-  // Pass 1: raw scores Q_j . K_k for every signed displacement.
-  float sp[kMaxPos], sm[kMaxPos];
-  scores_dir<+1>(lds_k, dist, n_plus, rr, part, N, qw, sp);
-  scores_dir<-1>(lds_k, dist, n_minus, rr, part, N, qw, sm);
+  // Pass 1: raw scores Q_j . K_k for every signed displacement (one per
+  // lane and group of four distances; the diagonal in every lane).
+  float sp[kGroups], sm[kGroups];
+  scores_dir<+1>(lds_k, dist, n_plus, rr, part, slot, N, qw, sp);
+  scores_dir<-1>(lds_k, dist, n_minus, rr, part, slot, N, qw, sm);
   float s0 = -INFINITY;
   if (has0) {
     u32x4 kf[2];
     load_bf16_q(lds_k + part * 32, rr, kf);
     s0 = dot_q(qw, kf);
   }
-  float m = s0;
-#pragma unroll
-  for (int i = 0; i < kMaxPos; ++i) m = fmaxf(m, fmaxf(sp[i], sm[i]));
+  float m = fmaxf(fmaxf(sp[0], sm[0]), fmaxf(sp[1], sm[1]));
+  m = quad_max(fmaxf(m, fmaxf(sp[2], sm[2])));
+  m = fmaxf(m, s0);
   // Pass 2: P = exp(scale (s - m)), accumulate P V in fp32.  A row with no
   // key in its support keeps l = 0 and is written as O = 0, LSE = -inf.
   const bool any = m != -INFINITY;
@@ -214,6 +243,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
   accumulate_dir<+1>(lds_v, dist, n_plus, rr, part, N, c, mc, sp, l, o);
   accumulate_dir<-1>(lds_v, dist, n_minus, rr, part, N, c, mc, sm, l, o);
+  l = quad_sum(l);
   if (has0) {
     u32x4 vf[4];
     load_f32_q(lds_v + part * 64, rr, vf);
@@ -250,6 +280,7 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   const int r0 = 16 * static_cast<int>((a.blocks >> (4 * wave)) & 15u);
   const int row0 = r0 + (lane & 15);
   const int part0 = lane_part(lane);
+  const int slot0 = quad_slot(lane);
 
   // The grid never exceeds the slab count.  The first slab's loads are
   // completed before the loop, so the loop's first trip and later trips see
@@ -267,8 +298,8 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
       // address arithmetic inside the loop instead of hoisted into registers.
       int N = a.N;
       asm volatile("" : "+s"(N));
-      int row = row0, part = part0;
-      asm volatile("" : "+v"(row), "+v"(part));
+      int row = row0, part = part0, slot = slot0;
+      asm volatile("" : "+v"(row), "+v"(part), "+v"(slot));
       char* lds_k = smem;
       char* lds_v = smem + N * kBf16Stride;
       char* lds_q = smem + N * (kBf16Stride + kF32Stride);
@@ -277,7 +308,7 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
       __syncthreads();
       const int next = slab + gridDim.x;
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
-      attend_slab(a, slab, N, row, part, r0, lds_k, lds_v, lds_q, pf);
+      attend_slab(a, slab, N, row, part, slot, r0, lds_k, lds_v, lds_q, pf);
     }
   } else {
     for (; slab < a.slabs; slab += gridDim.x) {

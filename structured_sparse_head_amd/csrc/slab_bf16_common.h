@@ -91,9 +91,9 @@ __device__ __forceinline__ void load_f32_q(const char* base, int r, u32x4 (&f)[4
   for (int t = 0; t < 4; ++t) f[t] = q[t];
 }
 
-// Full 64-element dot product of two bf16 rows split over the row's four
-// lanes, accumulated in fp32.
-__device__ __forceinline__ float dot_q(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
+// This lane's part of the dot product of two bf16 rows (16 elements),
+// accumulated in fp32.
+__device__ __forceinline__ float dot_part(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
   float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
                   dot2_first(a[3], b[0].w)};
   const uint32_t bw[4] = {b[1].x, b[1].y, b[1].z, b[1].w};
@@ -101,7 +101,57 @@ __device__ __forceinline__ float dot_q(const uint32_t (&a)[8], const u32x4 (&b)[
   for (int u = 0; u < 4; ++u)
     acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[4 + u]),
                                              __builtin_bit_cast(bf16x2_t, bw[u]), acc[u], false);
-  return quad_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Full 64-element dot product of two bf16 rows split over the row's four
+// lanes, accumulated in fp32.
+__device__ __forceinline__ float dot_q(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
+  return quad_sum(dot_part(a, b));
+}
+
+// Transposed reduction over the row's four lanes: x[j] holds this lane's
+// partial sum of quantity j; the result is the full sum of quantity
+// slot = (lane / 16) % 4.  Three swaps and three adds reduce four
+// quantities (a plain quad_sum per quantity would take eight of each).
+__device__ __forceinline__ int quad_slot(int lane) { return (lane >> 4) & 3; }
+
+__device__ __forceinline__ float reduce4(const float (&x)[4]) {
+  // Across lane halves: the low half keeps quantities 0 and 1, the high
+  // half 2 and 3.
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]),
+                                                  false, false);
+  const float t0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float t1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  // Across 16-lane rows: even rows keep t0, odd rows t1.
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(t0), __float_as_uint(t1), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// The inverse gather: x is this lane's value of quantity quad_slot(lane);
+// afterwards every lane of the row holds all four (y[j] = quantity j).
+__device__ __forceinline__ void gather4(float x, float (&y)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);  // a[0]: slots 0/1, a[1]: slots 2/3
+  const auto lo = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+  y[0] = __uint_as_float(lo[0]);
+  y[1] = __uint_as_float(lo[1]);
+  y[2] = __uint_as_float(hi[0]);
+  y[3] = __uint_as_float(hi[1]);
+}
+
+// Maximum of x over the four lanes of a row.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // acc += p * x for this lane's 16 fp32 elements.

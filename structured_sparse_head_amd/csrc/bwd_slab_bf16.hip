@@ -46,6 +46,7 @@ constexpr int kThreadsB = 1024;                       // 16 waves
 constexpr int kRowsB = kThreadsB / 4;                 // 256 rows, four lanes each
 constexpr int kChunksB = kRowsB * (kRowBytes / 16) / kThreadsB;  // 2
 constexpr int kTableCols = 2 * kMaxPos + 1;  // +f (0..11), -f (12..23), 0 (24)
+constexpr int kGroups = (kMaxPos + 3) / 4;   // distance groups of four in the query pass
 
 // LDS: per sequence row, bf16 K and V plus an fp32 copy of K for the query
 // and dQ passes, later overlaid by fp32 Q and dO rows for the key passes;
@@ -198,37 +199,52 @@ struct Pending {
 };
 
 // Query pass for displacements SGN * f_i, i < n (wave-uniform n) of data row
-// `row`: P (0 where the key is out of range) and dP go to table row trow,
-// column base + i (written by the group's first lane, wr), and sum P dP is
-// added to d.  The next step's K and V fragments are requested before the
-// current step's arithmetic.
+// `row`, four distances per group: each lane forms its partial Q.K and dO.V
+// products for the group's four keys, and two transposed reductions leave
+// the scores of distance 4 g + slot in the lane of that slot.  That lane
+// writes P (0 where the key is out of range) and dP to table row trow,
+// column base + i, and adds P dP to its partial d.  One fragment variable
+// per distance, requested a step ahead: loads under a condition then merge
+// with nothing, so the compiler needs no register copies at branch joins.
 template <int SGN>
 __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v, float2* tbl,
                                            Dist dist, int n, int row, int trow, int N, int part,
-                                           const uint32_t (&qw)[8], const uint32_t (&dw)[8],
-                                           float c, float lse2, int base, bool wr, float& d) {
-  u32x4 ka[2], va[2], kb[2], vb[2];
-  auto load = [&](int i, u32x4 (&kf)[2], u32x4 (&vf)[2]) {
+                                           int slot, const uint32_t (&qw)[8],
+                                           const uint32_t (&dw)[8], float c, float lse2, int base,
+                                           float& d) {
+  u32x4 kf[kMaxPos][2], vf[kMaxPos][2];
+  auto load = [&](int i) {
     const int r = clamp_row(row + SGN * dist.at(i), N);
-    load_bf16_q(lds_k + part * 32, r, kf);
-    load_bf16_q(lds_v + part * 32, r, vf);
+    load_bf16_q(lds_k + part * 32, r, kf[i]);
+    load_bf16_q(lds_v + part * 32, r, vf[i]);
   };
-  auto step = [&](int i, const u32x4 (&kf)[2], const u32x4 (&vf)[2]) {
-    const int kk = row + SGN * dist.at(i);
-    const float s = dot_q(qw, kf);
-    const float dp = dot_q(dw, vf);
-    const bool ok = static_cast<unsigned>(kk) < static_cast<unsigned>(N);
-    const float p = ok ? fast_exp2(__builtin_fmaf(s, c, -lse2)) : 0.f;
-    if (wr) tbl[trow * kTableCols + base + i] = make_float2(p, dp);
-    d = __builtin_fmaf(p, dp, d);
-  };
-  if (n > 0) load(0, ka, va);
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load(i + 1, kb, vb);
-    step(i, ka, va);
-    if (i + 1 < n) {
-      if (i + 2 < n) load(i + 2, ka, va);
-      step(i + 1, kb, vb);
+  if (n > 0) load(0);
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    if (4 * g < n) {
+      float ps[4], pp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        ps[j] = 0.f;
+        pp[j] = 0.f;
+        if (i < n) {
+          if (i + 1 < n) load(i + 1);
+          ps[j] = dot_part(qw, kf[i]);
+          pp[j] = dot_part(dw, vf[i]);
+        }
+      }
+      const float sc = reduce4(ps);
+      const float dp = reduce4(pp);
+      const uint32_t w = g == 0 ? dist.w0 : (g == 1 ? dist.w1 : dist.w2);
+      const int kk = row + SGN * static_cast<int>(__builtin_amdgcn_ubfe(w, 8 * slot, 8));
+      const int i = 4 * g + slot;
+      const bool ok = static_cast<unsigned>(kk) < static_cast<unsigned>(N);
+      const float p = ok ? fast_exp2(__builtin_fmaf(sc, c, -lse2)) : 0.f;
+      if (i < n) {
+        tbl[trow * kTableCols + base + i] = make_float2(p, dp);
+        d = __builtin_fmaf(p, dp, d);
+      }
     }
   }
 }
@@ -279,6 +295,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   const int r0 = 16 * static_cast<int>((a.blocks >> (4 * wave)) & 15u);
   const int row0 = r0 + (lane & 15);
   const int part0 = lane_part(lane);
+  const int slot0 = quad_slot(lane);
 
   // The grid never exceeds the slab count.  The first slab's loads are
   // completed before the loop so that the loop's first trip and later trips
@@ -310,8 +327,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     // address arithmetic inside the loop instead of hoisted into registers.
     int N = a.N;
     asm volatile("" : "+s"(N));
-    int row = row0, part = part0;
-    asm volatile("" : "+v"(row), "+v"(part));
+    int row = row0, part = part0, slot = slot0;
+    asm volatile("" : "+v"(row), "+v"(part), "+v"(slot));
     __syncthreads();  // the previous slab is no longer read from LDS
     char* lds_k = smem;
     char* lds_v = smem + N * kBf16Stride;
@@ -360,9 +377,11 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     float dqa[16];
     {
       float d = 0.f;
-      query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, row, N, part, qw, dw, a.c, lse2, 0, wr, d);
-      query_pass<-1>(lds_k, lds_v, tbl, dist, n_dn, rr, row, N, part, qw, dw, a.c, lse2, kMaxPos,
-                     wr, d);
+      query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, row, N, part, slot, qw, dw, a.c, lse2, 0,
+                     d);
+      query_pass<-1>(lds_k, lds_v, tbl, dist, n_dn, rr, row, N, part, slot, qw, dw, a.c, lse2,
+                     kMaxPos, d);
+      d = quad_sum(d);
       if (has0) {
         u32x4 kb[2], vb[2];
         load_bf16_q(lds_k + part * 32, rr, kb);

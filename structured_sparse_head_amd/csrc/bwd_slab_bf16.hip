@@ -168,33 +168,18 @@ __device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, char* lds_kf
 }
 
 // A finished fp32 row fragment waiting to be written: its four 16-byte
-// groups (64 bytes apart in the row) are stored one per step of a later pass
-// instead of in one burst, so the stores of all waves trickle out while they
-// compute.
+// groups (64 bytes apart in the row) are stored one per step of the first
+// steps of a later pass instead of in one burst, so the stores of all waves
+// trickle out while they compute.  Chunk indices are compile-time constants
+// so that every store is one 16-byte store at a fixed offset.
 struct Pending {
   float4* dst;
   const float (&x)[16];
   float scale;
-  int next;
-  __device__ __forceinline__ void store(int t) {
-    switch (t) {
-#define FIBATT_CHUNK(T)                                                               \
-  case T:                                                                             \
-    dst[4 * T] = make_float4(x[4 * T] * scale, x[4 * T + 1] * scale, x[4 * T + 2] * scale, \
-                         x[4 * T + 3] * scale);                                      \
-    break;
-      FIBATT_CHUNK(0) FIBATT_CHUNK(1) FIBATT_CHUNK(2) FIBATT_CHUNK(3)
-#undef FIBATT_CHUNK
-      default:
-        break;
-    }
-  }
-  __device__ __forceinline__ void tick() {
-    if (next < 4) store(next);
-    ++next;
-  }
-  __device__ __forceinline__ void flush() {
-    for (; next < 4; ++next) store(next);
+  template <int T>
+  __device__ __forceinline__ void store() const {
+    dst[4 * T] = make_float4(x[4 * T] * scale, x[4 * T + 1] * scale, x[4 * T + 2] * scale,
+                             x[4 * T + 3] * scale);
   }
 };
 
@@ -269,21 +254,34 @@ __device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist di
 // Key pass for key row k over displacements SGN * f_i: the queries
 // j = k - SGN * f_i contribute w_j * X_j, where w_j is component C of their
 // table entry (P for dV, dS / sqrt(d) for dK) and X_j their fp32 row (the
-// other waves of the SIMD cover the LDS latency of each step).
-template <int SGN, int C, typename Tick>
+// other waves of the SIMD cover the LDS latency of each step).  With a
+// pending fragment, its chunk t is stored after step t of the first four.
+template <int SGN, int C>
 __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, Dist dist, int n,
                                          int k, int N, int part, int base, float (&acc)[16],
-                                         Tick& tk) {
-  for (int i = 0; i < n; ++i) {
+                                         const Pending* pend) {
+  auto step = [&](int i) {
     const int j = k - SGN * dist.at(i);
     const int jc = clamp_row(j, N);
     u32x4 xf[4];
     load_f32_q(lds_x + part * 64, jc, xf);
     const float2 t = tbl[jc * kTableCols + base + i];
     const bool ok = static_cast<unsigned>(j) < static_cast<unsigned>(N);
-    tk.tick();
     axpy_q(acc, ok ? (C == 0 ? t.x : t.y) : 0.f, xf);
+  };
+  int i = 0;
+  if (pend) {
+    if (0 < n) step(0);
+    pend->store<0>();
+    if (1 < n) step(1);
+    pend->store<1>();
+    if (2 < n) step(2);
+    pend->store<2>();
+    if (3 < n) step(3);
+    pend->store<3>();
+    i = 4;
   }
+  for (; i < n; ++i) step(i);
 }
 
 template <int MH>
@@ -419,30 +417,28 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       // Key k, displacement +f: query k - f exists while k >= f (f <= wl for
       // some key of the wave); displacement -f: query k + f < N.
       // dQ is written during the dV pass and dV during the dK pass.
-      Pending pq{reinterpret_cast<float4*>(a.dq + grow * 64) + part, dqa, a.scale, 0};
+      const Pending pq{reinterpret_cast<float4*>(a.dq + grow * 64) + part, dqa, a.scale};
       float acc[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      key_pass<+1, 0>(lds_do, tbl, dist, n_dn, rr, N, part, 0, acc, pq);
-      key_pass<-1, 0>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, pq);
+      key_pass<+1, 0>(lds_do, tbl, dist, n_dn, rr, N, part, 0, acc, &pq);
+      key_pass<-1, 0>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, nullptr);
       if (has0) {
         u32x4 xb[4];
         load_f32_q(lds_do + part * 64, rr, xb);
         axpy_q(acc, tbl[rr * kTableCols + z].x, xb);
       }
-      pq.flush();
-      Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part, acc, 1.0f, 0};
+      const Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part, acc, 1.0f};
       float acc2[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc2[e] = 0.f;
-      key_pass<+1, 1>(lds_q, tbl, dist, n_dn, rr, N, part, 0, acc2, pv);
-      key_pass<-1, 1>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, pv);
+      key_pass<+1, 1>(lds_q, tbl, dist, n_dn, rr, N, part, 0, acc2, &pv);
+      key_pass<-1, 1>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, nullptr);
       if (has0) {
         u32x4 xb[4];
         load_f32_q(lds_q + part * 64, rr, xb);
         axpy_q(acc2, tbl[rr * kTableCols + z].y, xb);
       }
-      pv.flush();
       float4* dk = reinterpret_cast<float4*>(a.dk + grow * 64) + part;
 #pragma unroll
       for (int t = 0; t < 4; ++t)

@@ -168,9 +168,9 @@ __device__ __forceinline__ void commit_kv(char* lds_k, char* lds_v, char* lds_kf
 }
 
 // A finished fp32 row fragment waiting to be written: its four 16-byte
-// groups (64 bytes apart in the row) are stored one per step of the first
-// steps of a later pass instead of in one burst, so the stores of all waves
-// trickle out while they compute.  Chunk indices are compile-time constants
+// groups (64 bytes apart in the row) are stored a few steps apart during
+// later passes instead of in one burst, so the stores of all waves trickle
+// out while they compute.  Chunk indices are compile-time constants
 // so that every store is one 16-byte store at a fixed offset.
 struct Pending {
   float4* dst;
@@ -255,8 +255,9 @@ __device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist di
 // j = k - SGN * f_i contribute w_j * X_j, where w_j is component C of their
 // table entry (P for dV, dS / sqrt(d) for dK) and X_j their fp32 row (the
 // other waves of the SIMD cover the LDS latency of each step).  With a
-// pending fragment, its chunk t is stored after step t of the first four.
-template <int SGN, int C>
+// pending fragment, its chunks T0 and T0 + 1 are stored after steps 0 and 4:
+// the two passes of a kind spread a fragment's four stores over their steps.
+template <int SGN, int C, int T0>
 __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, Dist dist, int n,
                                          int k, int N, int part, int base, float (&acc)[16],
                                          const Pending* pend) {
@@ -272,14 +273,13 @@ __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, D
   int i = 0;
   if (pend) {
     if (0 < n) step(0);
-    pend->store<0>();
+    pend->store<T0>();
     if (1 < n) step(1);
-    pend->store<1>();
     if (2 < n) step(2);
-    pend->store<2>();
     if (3 < n) step(3);
-    pend->store<3>();
-    i = 4;
+    if (4 < n) step(4);
+    pend->store<T0 + 1>();
+    i = 5;
   }
   for (; i < n; ++i) step(i);
 }
@@ -421,8 +421,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       float acc[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      key_pass<+1, 0>(lds_do, tbl, dist, n_dn, rr, N, part, 0, acc, &pq);
-      key_pass<-1, 0>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, nullptr);
+      key_pass<+1, 0, 0>(lds_do, tbl, dist, n_dn, rr, N, part, 0, acc, &pq);
+      key_pass<-1, 0, 2>(lds_do, tbl, dist, n_up, rr, N, part, kMaxPos, acc, &pq);
       if (has0) {
         u32x4 xb[4];
         load_f32_q(lds_do + part * 64, rr, xb);
@@ -432,8 +432,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       float acc2[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc2[e] = 0.f;
-      key_pass<+1, 1>(lds_q, tbl, dist, n_dn, rr, N, part, 0, acc2, &pv);
-      key_pass<-1, 1>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, nullptr);
+      key_pass<+1, 1, 0>(lds_q, tbl, dist, n_dn, rr, N, part, 0, acc2, &pv);
+      key_pass<-1, 1, 2>(lds_q, tbl, dist, n_up, rr, N, part, kMaxPos, acc2, &pv);
       if (has0) {
         u32x4 xb[4];
         load_f32_q(lds_q + part * 64, rr, xb);

@@ -1,0 +1,255 @@
+// Forward for long sequences, bf16, d_h = 64: sparse Fibottention attention
+// O = softmax_Omega(Q K^T / sqrt(d)) V on query tiles read straight from
+// global memory.
+//
+// Fibottention paper (arXiv 2406.19391), method section, eq. (1) and (3):
+// query row j only meets keys j + delta for the head's signed displacements
+// delta (+f and -f for every f in Fib(a_i, b_i) within the window, and 0 when
+// 0 is a distance).  For a fixed delta the keys of consecutive queries are
+// consecutive rows, so each load instruction of a wave (16 query rows) reads
+// 16 consecutive K or V rows: coalesced, and the rows come from L2 because
+// the neighbouring tiles of the slab read the same rows for other
+// displacements.
+//
+// Design points:
+//  * Lanes.  Four adjacent lanes own a query row: lane l of a wave works on
+//    row r0 + l / 4 and, with p = l % 4, on the 8-element groups p and p + 4
+//    of Q, K, V and O.  A lane quad then reads or writes 64 contiguous bytes
+//    per instruction, which the cache front end serves as one access (with
+//    the four lanes of a row 16 lanes apart every lane was an access of its
+//    own, and that access rate bounded the kernel).  Sums over a row use DPP
+//    quad permutations.
+//  * Work.  A workgroup (4 waves, 64 rows) takes one query tile.  Tiles are
+//    numbered slab by slab and dealt to the XCDs in contiguous ranges
+//    (workgroup b runs on XCD b mod 8), so the tiles of a slab share an L2.
+//  * Two passes instead of an online softmax.  Pass 1 forms every score of
+//    the row in groups of four displacements; a transposed reduction over the
+//    quad leaves one full score per lane (displacement 4 g + p in lane p), so
+//    a lane keeps ceil(n / 4) scores.  The row maximum is one quad max.
+//    Pass 2 turns each lane's own scores into probabilities, broadcasts a
+//    group's four within the quad and accumulates P V in fp32.
+//  * Lanes past the last row repeat row N - 1 and write identical values.
+#include "slab_bf16_common.h"
+
+namespace fibatt {
+namespace {
+
+using slab::clamp_row;
+using slab::dot_part;
+
+// DPP quad permutations: lane i of each quad reads lane P[i].
+constexpr int kSwap1 = 0xB1;  // [1, 0, 3, 2]
+constexpr int kSwap2 = 0x4E;  // [2, 3, 0, 1]
+
+template <int CTRL>
+__device__ __forceinline__ float qperm(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum and maximum of x over the lane quad.
+__device__ __forceinline__ float quad_sum4(float x) {
+  x += qperm<kSwap1>(x);
+  return x + qperm<kSwap2>(x);
+}
+__device__ __forceinline__ float quad_max4(float x) {
+  x = fmaxf(x, qperm<kSwap1>(x));
+  return fmaxf(x, qperm<kSwap2>(x));
+}
+
+// Transposed reduction over the quad: x[j] is this lane's partial sum of
+// quantity j; the result is the full sum of quantity lane % 4.  Each round
+// keeps half of the quantities and sends the other half to the partner lane.
+__device__ __forceinline__ float reduce4q(const float (&x)[4], bool b0, bool b1) {
+  const float u0 = (b0 ? x[1] : x[0]) + qperm<kSwap1>(b0 ? x[0] : x[1]);
+  const float u1 = (b0 ? x[3] : x[2]) + qperm<kSwap1>(b0 ? x[2] : x[3]);
+  return (b1 ? u1 : u0) + qperm<kSwap2>(b1 ? u0 : u1);
+}
+
+// y[j] = x of lane j of the quad.
+__device__ __forceinline__ void gather4q(float x, float (&y)[4]) {
+  y[0] = qperm<0x00>(x);
+  y[1] = qperm<0x55>(x);
+  y[2] = qperm<0xAA>(x);
+  y[3] = qperm<0xFF>(x);
+}
+
+constexpr int kTileThreads = 256;              // 4 waves
+constexpr int kTileRows = kTileThreads / 4;    // 64 query rows
+constexpr int kRowB = 128;                     // bf16 row of 64
+constexpr int kGroupsT = (kMaxSigned + 3) / 4; // displacement groups of four
+constexpr int kXcds = 8;
+
+template <int MH>
+struct TileArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;
+  int H;
+  int N;
+  int tiles;    // query tiles per slab
+  int work;     // slabs * tiles
+  int per_xcd;  // ceil(work / 8)
+  float scale_log2;
+  HeadTableT<MH> ht;
+};
+
+// This lane's 16 elements (groups p and p + 4) of bf16 row r.
+__device__ __forceinline__ void load_row_q(const char* rowp, u32x4 (&f)[2]) {
+  f[0] = *reinterpret_cast<const u32x4*>(rowp);
+  f[1] = *reinterpret_cast<const u32x4*>(rowp + 64);
+}
+
+template <int MH>
+__global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH> a) {
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
+  __shared__ int s_nd;
+  const int w = (blockIdx.x % kXcds) * a.per_xcd + static_cast<int>(blockIdx.x / kXcds);
+  if (w >= a.work) return;  // whole workgroup, before any barrier
+  const int slab = w / a.tiles;
+  const int tile = w - slab * a.tiles;
+  const int h = slab % a.H;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;  // a whole last group
+  }
+  __syncthreads();
+  const int nd = s_nd;
+  const int N = a.N;
+  const int lane = tid & 63;
+  const int part = lane & 3;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int row = tile * kTileRows + (tid >> 2);
+  const int rr = row < N ? row : N - 1;
+  const size_t base = static_cast<size_t>(slab) * N * kRowB;
+  const char* kbase = a.k + base + part * 16;
+  const char* vbase = a.v + base + part * 16;
+
+  uint32_t qw[8];
+  {
+    u32x4 qf[2];
+    qf[0] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(rr) * kRowB + part * 16));
+    qf[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        a.q + base + static_cast<size_t>(rr) * kRowB + part * 16 + 64));
+    qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
+    qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
+  }
+
+  // Pass 1: scores, one per lane and group of four displacements.
+  float s[kGroupsT];
+#pragma unroll
+  for (int g = 0; g < kGroupsT; ++g) {
+    s[g] = -INFINITY;
+    if (4 * g < nd) {
+      const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
+      const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
+                        __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
+      u32x4 kf[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf[j]);
+      float pd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pd[j] = dot_part(qw, kf[j]);
+      const float t = reduce4q(pd, b0, b1);
+      const int kk = rr + s_deltas[4 * g + part];
+      const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
+      s[g] = ok ? t : -INFINITY;
+    }
+  }
+  float m = s[0];
+#pragma unroll
+  for (int g = 1; g < kGroupsT; ++g) m = fmaxf(m, s[g]);
+  m = quad_max4(m);
+
+  // Pass 2: P = exp(scale (s - m)), P V in fp32.  A row with no key in its
+  // support keeps l = 0 and is written as O = 0, LSE = -inf.
+  const bool any = m != -INFINITY;
+  const float c = a.scale_log2;
+  const float mc = any ? m * c : 0.f;
+  float l = 0.f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int g = 0; g < kGroupsT; ++g) {
+    if (4 * g < nd) {
+      const float pown = fast_exp2(__builtin_fmaf(s[g], c, -mc));  // 0 for s = -inf
+      l += pown;
+      float p[4];
+      gather4q(pown, p);
+      const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
+      const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
+                        __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * g + j < nd) {
+          u32x4 vf[2];
+          load_row_q(vbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, vf);
+          const uint32_t x[8] = {vf[0].x, vf[0].y, vf[0].z, vf[0].w,
+                                 vf[1].x, vf[1].y, vf[1].z, vf[1].w};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            o[2 * u] = __builtin_fmaf(p[j], __uint_as_float(x[u] << 16), o[2 * u]);
+            o[2 * u + 1] = __builtin_fmaf(p[j], __uint_as_float(x[u] & 0xffff0000u), o[2 * u + 1]);
+          }
+        }
+      }
+    }
+  }
+  l = quad_sum4(l);
+  const float inv = any ? 1.0f / l : 0.f;
+  uint32_t ow[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
+    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
+    ow[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  char* orow = a.o + base + static_cast<size_t>(rr) * kRowB + part * 16;
+  *reinterpret_cast<u32x4*>(orow) = u32x4{ow[0], ow[1], ow[2], ow[3]};
+  *reinterpret_cast<u32x4*>(orow + 64) = u32x4{ow[4], ow[5], ow[6], ow[7]};
+  if (part == 0)
+    a.lse[static_cast<size_t>(slab) * N + rr] = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
+template <int MH>
+hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, hipStream_t stream) {
+  TileArgs<MH> a;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.o = static_cast<char*>(o);
+  a.lse = lse;
+  a.H = p.H;
+  a.N = p.N;
+  a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
+  a.ht = shrink_heads<MH>(p.heads, p.H);
+  const long long slabs = static_cast<long long>(p.B) * p.H;
+  a.tiles = (p.N + kTileRows - 1) / kTileRows;
+  const long long work = slabs * a.tiles;
+  if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
+  a.work = static_cast<int>(work);
+  a.per_xcd = (a.work + kXcds - 1) / kXcds;
+  const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
+  hipLaunchKernelGGL(fwd_tile_bf16_kernel<MH>, dim3(grid), dim3(kTileThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_tile_bf16_fits(const Problem& p) { return p.dtype == DType::kBF16 && p.D == 64; }
+
+hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream) {
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads>(p, q, k, v, o, lse, stream);
+}
+
+}  // namespace fibatt

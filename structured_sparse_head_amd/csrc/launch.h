@@ -38,6 +38,11 @@ bool fwd_slab_fits(const Problem& p);
 bool fwd_slab_bf16_fits(const Problem& p);
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream);
+// Forward for bf16, d_h = 64 and any N, query tiles read from global memory
+// (the default when the persistent kernel does not fit).
+bool fwd_tile_bf16_fits(const Problem& p);
+hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream);
 bool bwd_slab_fits(const Problem& p);
 
 // Persistent backward for bf16, d_h = 64, N <= 201 (the default when it fits).

@@ -1,0 +1,311 @@
+// Backward for long sequences, bf16, d_h = 64: exact gradients of the sparse
+// Fibottention attention on 64-row tiles read straight from global memory.
+//
+// The Fibottention paper (method section, eq. (1) and (3)) defines the
+// forward; the backward is its derivative.  With P the support-restricted
+// softmax recomputed from the forward's log-sum-exp, dP_jk = dO_j . V_k,
+//   D_j   = sum_k P_jk dP_jk,      dS_jk = P_jk (dP_jk - D_j),
+//   dQ_j  = sum_k dS_jk K_k / sqrt(d),
+//   dK_k  = sum_j dS_jk Q_j / sqrt(d),   dV_k = sum_j P_jk dO_j.
+// The support is symmetric (it is defined through |j - k|), so the queries
+// that see key k are k + delta for the same signed displacements: dK and dV
+// are gathered key by key, every output row has one writer and no atomics.
+//
+// Two launches on the caller's stream:
+//  * dq: per query row, pass 1 forms P and dP for every displacement (a
+//    transposed quad reduction leaves one (P, dP) pair per lane and group of
+//    four displacements) and D; pass 2 forms the lane's dS, broadcasts a
+//    group's four in the quad and accumulates dS K.  D goes to the workspace.
+//  * dkdv: per key row and group of four displacements, the queries' Q and dO
+//    rows are read once for both the recomputed scores and the accumulation
+//    of dV += P dO and dK += dS Q.
+// Lanes past the last row repeat row N - 1 and write identical values.
+#include "tile_bf16_common.h"
+
+namespace fibatt {
+namespace {
+
+using slab::clamp_row;
+using slab::dot_part;
+using namespace tile;
+
+template <int MH>
+struct BwdTileArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* ws;  // D per row
+  int H;
+  int N;
+  int tiles;
+  int work;
+  int per_xcd;
+  float c;      // log2(e) / sqrt(64)
+  float scale;  // 1 / sqrt(64)
+  HeadTableT<MH> ht;
+};
+
+// The head's signed displacements in LDS (thread 0 builds them), padded with
+// zeros to a whole last group; returns their count after a barrier.
+__device__ __forceinline__ int stage_deltas(int32_t a, int32_t b, int32_t lim, int* dist,
+                                            int* deltas, int* nd) {
+  if (threadIdx.x == 0) {
+    build_deltas(a, b, lim, dist, deltas, nd);
+    for (int i = 0; i < 4; ++i) deltas[*nd + i] = 0;
+  }
+  __syncthreads();
+  return *nd;
+}
+
+__device__ __forceinline__ void group_deltas(const int* deltas, int g, int (&d)[4]) {
+  const int4 d4 = *reinterpret_cast<const int4*>(&deltas[4 * g]);
+  d[0] = __builtin_amdgcn_readfirstlane(d4.x);
+  d[1] = __builtin_amdgcn_readfirstlane(d4.y);
+  d[2] = __builtin_amdgcn_readfirstlane(d4.z);
+  d[3] = __builtin_amdgcn_readfirstlane(d4.w);
+}
+
+// Stores this lane's 16 fp32 elements (groups p and p + 4) times `scale`.
+__device__ __forceinline__ void store_row_f32(float* row, int part, const float (&x)[16],
+                                              float scale) {
+  float4* a = reinterpret_cast<float4*>(row + 8 * part);
+  float4* b = reinterpret_cast<float4*>(row + 32 + 8 * part);
+  a[0] = make_float4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+  a[1] = make_float4(x[4] * scale, x[5] * scale, x[6] * scale, x[7] * scale);
+  b[0] = make_float4(x[8] * scale, x[9] * scale, x[10] * scale, x[11] * scale);
+  b[1] = make_float4(x[12] * scale, x[13] * scale, x[14] * scale, x[15] * scale);
+}
+
+__device__ __forceinline__ void frag_words(const u32x4 (&f)[2], uint32_t (&w)[8]) {
+  w[0] = f[0].x; w[1] = f[0].y; w[2] = f[0].z; w[3] = f[0].w;
+  w[4] = f[1].x; w[5] = f[1].y; w[6] = f[1].z; w[7] = f[1].w;
+}
+
+template <int MH, int KG>
+__global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<MH> a) {
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
+  __shared__ int s_nd;
+  const int w = tile_of_block(a.per_xcd);
+  if (w >= a.work) return;  // whole workgroup, before any barrier
+  const int slab = w / a.tiles;
+  const int tile = w - slab * a.tiles;
+  const int h = slab % a.H;
+  const int nd = stage_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  const int N = a.N;
+  const int lane = threadIdx.x & 63;
+  const int part = lane & 3;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int row = tile * kTileRows + (threadIdx.x >> 2);
+  const int rr = row < N ? row : N - 1;
+  const size_t base = static_cast<size_t>(slab) * N * kRowB;
+  const size_t rbase = static_cast<size_t>(slab) * N;
+  const char* kbase = a.k + base + part * 16;
+  const char* vbase = a.v + base + part * 16;
+
+  uint32_t qw[8], dw[8];
+  {
+    u32x4 f[2];
+    load_row_q(a.q + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    frag_words(f, qw);
+    load_row_q(a.dout + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    frag_words(f, dw);
+  }
+  const float lse2 = a.lse[rbase + rr] * kLog2e;
+
+  // Pass 1: P and dP, one pair per lane and group; D = sum P dP.
+  float pw[KG], dpw[KG];
+  float dl = 0.f;
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    pw[g] = 0.f;
+    dpw[g] = 0.f;
+    if (4 * g < nd) {
+      int d[4];
+      group_deltas(s_deltas, g, d);
+      u32x4 kf[4][2], vf[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t off = static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB;
+        load_row_q(kbase + off, kf[j]);
+        load_row_q(vbase + off, vf[j]);
+      }
+      float ps[4], pp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ps[j] = dot_part(qw, kf[j]);
+        pp[j] = dot_part(dw, vf[j]);
+      }
+      const float sc = reduce4q(ps, b0, b1);
+      const float dp = reduce4q(pp, b0, b1);
+      const int kk = rr + s_deltas[4 * g + part];
+      const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
+      const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse2)) : 0.f;
+      pw[g] = p;
+      dpw[g] = dp;
+      dl = __builtin_fmaf(p, dp, dl);
+    }
+  }
+  const float dd = quad_sum4(dl);
+
+  // Pass 2: dQ = sum dS K / sqrt(d).
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    if (4 * g < nd) {
+      float ds[4];
+      gather4q(pw[g] * (dpw[g] - dd), ds);
+      int d[4];
+      group_deltas(s_deltas, g, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * g + j < nd) {
+          u32x4 kf[2];
+          load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf);
+          axpy_bf16(acc, ds[j], kf);
+        }
+      }
+    }
+  }
+  store_row_f32(a.dq + (rbase + rr) * 64, part, acc, a.scale);
+  if (part == 0) a.ws[rbase + rr] = dd;
+}
+
+template <int MH>
+__global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs<MH> a) {
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
+  __shared__ int s_nd;
+  const int w = tile_of_block(a.per_xcd);
+  if (w >= a.work) return;  // whole workgroup, before any barrier
+  const int slab = w / a.tiles;
+  const int tile = w - slab * a.tiles;
+  const int h = slab % a.H;
+  const int nd = stage_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  const int N = a.N;
+  const int lane = threadIdx.x & 63;
+  const int part = lane & 3;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int row = tile * kTileRows + (threadIdx.x >> 2);
+  const int rr = row < N ? row : N - 1;  // key row
+  const size_t base = static_cast<size_t>(slab) * N * kRowB;
+  const size_t rbase = static_cast<size_t>(slab) * N;
+  const char* qbase = a.q + base + part * 16;
+  const char* obase = a.dout + base + part * 16;
+
+  uint32_t kw[8], vw[8];
+  {
+    u32x4 f[2];
+    load_row_q(a.k + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    frag_words(f, kw);
+    load_row_q(a.v + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    frag_words(f, vw);
+  }
+  float dk[16], dv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    dk[e] = 0.f;
+    dv[e] = 0.f;
+  }
+  for (int g = 0; 4 * g < nd; ++g) {
+    int d[4];
+    group_deltas(s_deltas, g, d);
+    // This lane's query (slot p of the group) and its LSE and D, requested
+    // with the group's rows.
+    const int jj = rr + s_deltas[4 * g + part];
+    const bool ok = 4 * g + part < nd && static_cast<unsigned>(jj) < static_cast<unsigned>(N);
+    const int jc = clamp_row(jj, N);
+    const float lse_j = a.lse[rbase + jc];
+    const float d_j = a.ws[rbase + jc];
+    u32x4 qf[4][2], of[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t off = static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB;
+      load_row_q(qbase + off, qf[j]);
+      load_row_q(obase + off, of[j]);
+    }
+    float ps[4], pp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ps[j] = dot_part(kw, qf[j]);
+      pp[j] = dot_part(vw, of[j]);
+    }
+    const float sc = reduce4q(ps, b0, b1);
+    const float dp = reduce4q(pp, b0, b1);
+    const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse_j * kLog2e)) : 0.f;
+    float pg[4], dsg[4];
+    gather4q(p, pg);
+    gather4q(p * (dp - d_j), dsg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      axpy_bf16(dv, pg[j], of[j]);
+      axpy_bf16(dk, dsg[j], qf[j]);
+    }
+  }
+  store_row_f32(a.dk + (rbase + rr) * 64, part, dk, a.scale);
+  store_row_f32(a.dv + (rbase + rr) * 64, part, dv, 1.0f);
+}
+
+template <int MH, int KG>
+void launch_dq(const BwdTileArgs<MH>& a, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+}
+
+template <int MH>
+hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                    float* ws, hipStream_t stream) {
+  BwdTileArgs<MH> a;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.dout = static_cast<const char*>(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = ws;
+  a.H = p.H;
+  a.N = p.N;
+  a.scale = 0.125f;  // 1 / sqrt(64)
+  a.c = kLog2e * 0.125f;
+  a.ht = shrink_heads<MH>(p.heads, p.H);
+  const long long slabs = static_cast<long long>(p.B) * p.H;
+  a.tiles = (p.N + kTileRows - 1) / kTileRows;
+  const long long work = slabs * a.tiles;
+  if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
+  a.work = static_cast<int>(work);
+  a.per_xcd = (a.work + kXcds - 1) / kXcds;
+  const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
+  const int groups = (max_signed(p) + 3) / 4;
+  if (groups <= 4)
+    launch_dq<MH, 4>(a, grid, stream);
+  else if (groups <= 8)
+    launch_dq<MH, 8>(a, grid, stream);
+  else if (groups <= 12)
+    launch_dq<MH, 12>(a, grid, stream);
+  else
+    launch_dq<MH, (kMaxSigned + 3) / 4>(a, grid, stream);
+  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_tile_bf16_fits(const Problem& p) { return p.dtype == DType::kBF16 && p.D == 64; }
+
+hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const float* lse, const void* dout, float* dq, float* dk,
+                                float* dv, float* ws, hipStream_t stream) {
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  return launch_t<kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+}
+
+}  // namespace fibatt

@@ -29,55 +29,15 @@
 //    Pass 2 turns each lane's own scores into probabilities, broadcasts a
 //    group's four within the quad and accumulates P V in fp32.
 //  * Lanes past the last row repeat row N - 1 and write identical values.
-#include "slab_bf16_common.h"
+#include "tile_bf16_common.h"
 
 namespace fibatt {
 namespace {
 
 using slab::clamp_row;
 using slab::dot_part;
+using namespace tile;
 
-// DPP quad permutations: lane i of each quad reads lane P[i].
-constexpr int kSwap1 = 0xB1;  // [1, 0, 3, 2]
-constexpr int kSwap2 = 0x4E;  // [2, 3, 0, 1]
-
-template <int CTRL>
-__device__ __forceinline__ float qperm(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum and maximum of x over the lane quad.
-__device__ __forceinline__ float quad_sum4(float x) {
-  x += qperm<kSwap1>(x);
-  return x + qperm<kSwap2>(x);
-}
-__device__ __forceinline__ float quad_max4(float x) {
-  x = fmaxf(x, qperm<kSwap1>(x));
-  return fmaxf(x, qperm<kSwap2>(x));
-}
-
-// Transposed reduction over the quad: x[j] is this lane's partial sum of
-// quantity j; the result is the full sum of quantity lane % 4.  Each round
-// keeps half of the quantities and sends the other half to the partner lane.
-__device__ __forceinline__ float reduce4q(const float (&x)[4], bool b0, bool b1) {
-  const float u0 = (b0 ? x[1] : x[0]) + qperm<kSwap1>(b0 ? x[0] : x[1]);
-  const float u1 = (b0 ? x[3] : x[2]) + qperm<kSwap1>(b0 ? x[2] : x[3]);
-  return (b1 ? u1 : u0) + qperm<kSwap2>(b1 ? u0 : u1);
-}
-
-// y[j] = x of lane j of the quad.
-__device__ __forceinline__ void gather4q(float x, float (&y)[4]) {
-  y[0] = qperm<0x00>(x);
-  y[1] = qperm<0x55>(x);
-  y[2] = qperm<0xAA>(x);
-  y[3] = qperm<0xFF>(x);
-}
-
-constexpr int kTileThreads = 256;              // 4 waves
-constexpr int kTileRows = kTileThreads / 4;    // 64 query rows
-constexpr int kRowB = 128;                     // bf16 row of 64
-constexpr int kGroupsT = (kMaxSigned + 3) / 4; // displacement groups of four
-constexpr int kXcds = 8;
 
 template <int MH>
 struct TileArgs {
@@ -95,18 +55,14 @@ struct TileArgs {
   HeadTableT<MH> ht;
 };
 
-// This lane's 16 elements (groups p and p + 4) of bf16 row r.
-__device__ __forceinline__ void load_row_q(const char* rowp, u32x4 (&f)[2]) {
-  f[0] = *reinterpret_cast<const u32x4*>(rowp);
-  f[1] = *reinterpret_cast<const u32x4*>(rowp + 64);
-}
-
-template <int MH>
+// KG: displacement groups of four the kernel holds scores for (at least
+// the largest head's count); smaller instantiations keep fewer registers.
+template <int MH, int KG>
 __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH> a) {
   __shared__ int s_dist[kMaxOffsets];
   __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
   __shared__ int s_nd;
-  const int w = (blockIdx.x % kXcds) * a.per_xcd + static_cast<int>(blockIdx.x / kXcds);
+  const int w = tile_of_block(a.per_xcd);
   if (w >= a.work) return;  // whole workgroup, before any barrier
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
@@ -140,9 +96,9 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   }
 
   // Pass 1: scores, one per lane and group of four displacements.
-  float s[kGroupsT];
+  float s[KG];
 #pragma unroll
-  for (int g = 0; g < kGroupsT; ++g) {
+  for (int g = 0; g < KG; ++g) {
     s[g] = -INFINITY;
     if (4 * g < nd) {
       const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
@@ -163,7 +119,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   }
   float m = s[0];
 #pragma unroll
-  for (int g = 1; g < kGroupsT; ++g) m = fmaxf(m, s[g]);
+  for (int g = 1; g < KG; ++g) m = fmaxf(m, s[g]);
   m = quad_max4(m);
 
   // Pass 2: P = exp(scale (s - m)), P V in fp32.  A row with no key in its
@@ -176,7 +132,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
 #pragma unroll
-  for (int g = 0; g < kGroupsT; ++g) {
+  for (int g = 0; g < KG; ++g) {
     if (4 * g < nd) {
       const float pown = fast_exp2(__builtin_fmaf(s[g], c, -mc));  // 0 for s = -inf
       l += pown;
@@ -218,6 +174,11 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     a.lse[static_cast<size_t>(slab) * N + rr] = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
+template <int MH, int KG>
+void launch_kg(const TileArgs<MH>& a, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+}
+
 template <int MH>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                     float* lse, hipStream_t stream) {
@@ -238,7 +199,15 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.work = static_cast<int>(work);
   a.per_xcd = (a.work + kXcds - 1) / kXcds;
   const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
-  hipLaunchKernelGGL(fwd_tile_bf16_kernel<MH>, dim3(grid), dim3(kTileThreads), 0, stream, a);
+  const int groups = (max_signed(p) + 3) / 4;
+  if (groups <= 4)
+    launch_kg<MH, 4>(a, grid, stream);
+  else if (groups <= 8)
+    launch_kg<MH, 8>(a, grid, stream);
+  else if (groups <= 12)
+    launch_kg<MH, 12>(a, grid, stream);
+  else
+    launch_kg<MH, (kMaxSigned + 3) / 4>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -45,6 +45,14 @@ hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, 
                                 void* o, float* lse, hipStream_t stream);
 bool bwd_slab_fits(const Problem& p);
 
+// Backward for bf16, d_h = 64 and any N on 64-row tiles (two launches; D
+// goes through the workspace); the default when the persistent kernel does
+// not fit.
+bool bwd_tile_bf16_fits(const Problem& p);
+hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const float* lse, const void* dout, float* dq, float* dk,
+                                float* dv, float* ws, hipStream_t stream);
+
 // Persistent backward for bf16, d_h = 64, N <= 201 (the default when it fits).
 bool bwd_slab_bf16_fits(const Problem& p);
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,

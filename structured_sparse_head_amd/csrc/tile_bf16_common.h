@@ -1,0 +1,94 @@
+// Pieces shared by the long-sequence tile kernels (bf16, d_h = 64): four
+// adjacent lanes own a row (lane l works on row l / 4 of its wave's 16 and,
+// with p = l % 4, on the 8-element groups p and p + 4), so a lane quad reads
+// or writes 64 contiguous bytes per instruction.  Sums over a row use DPP
+// quad permutations.  Workgroups of 4 waves take 64-row tiles, numbered slab
+// by slab and dealt to the XCDs in contiguous ranges (workgroup b runs on XCD
+// b mod 8) so that the tiles of a slab share an L2.
+#pragma once
+
+#include "slab_bf16_common.h"
+
+namespace fibatt {
+namespace tile {
+
+constexpr int kTileThreads = 256;              // 4 waves
+constexpr int kTileRows = kTileThreads / 4;    // 64 query rows
+constexpr int kRowB = 128;                     // bf16 row of 64
+constexpr int kXcds = 8;
+
+// DPP quad permutations: lane i of each quad reads lane P[i].
+constexpr int kSwap1 = 0xB1;  // [1, 0, 3, 2]
+constexpr int kSwap2 = 0x4E;  // [2, 3, 0, 1]
+
+template <int CTRL>
+__device__ __forceinline__ float qperm(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum and maximum of x over the lane quad.
+__device__ __forceinline__ float quad_sum4(float x) {
+  x += qperm<kSwap1>(x);
+  return x + qperm<kSwap2>(x);
+}
+__device__ __forceinline__ float quad_max4(float x) {
+  x = fmaxf(x, qperm<kSwap1>(x));
+  return fmaxf(x, qperm<kSwap2>(x));
+}
+
+// Transposed reduction over the quad: x[j] is this lane's partial sum of
+// quantity j; the result is the full sum of quantity lane % 4.  Each round
+// keeps half of the quantities and sends the other half to the partner lane.
+__device__ __forceinline__ float reduce4q(const float (&x)[4], bool b0, bool b1) {
+  const float u0 = (b0 ? x[1] : x[0]) + qperm<kSwap1>(b0 ? x[0] : x[1]);
+  const float u1 = (b0 ? x[3] : x[2]) + qperm<kSwap1>(b0 ? x[2] : x[3]);
+  return (b1 ? u1 : u0) + qperm<kSwap2>(b1 ? u0 : u1);
+}
+
+// y[j] = x of lane j of the quad.
+__device__ __forceinline__ void gather4q(float x, float (&y)[4]) {
+  y[0] = qperm<0x00>(x);
+  y[1] = qperm<0x55>(x);
+  y[2] = qperm<0xAA>(x);
+  y[3] = qperm<0xFF>(x);
+}
+
+// This lane's 16 elements (groups p and p + 4) of a bf16 row; rowp already
+// points at byte 16 p of the row.
+__device__ __forceinline__ void load_row_q(const char* rowp, u32x4 (&f)[2]) {
+  f[0] = *reinterpret_cast<const u32x4*>(rowp);
+  f[1] = *reinterpret_cast<const u32x4*>(rowp + 64);
+}
+
+// acc += p * x for this lane's 16 bf16 elements (widened to fp32).
+__device__ __forceinline__ void axpy_bf16(float (&acc)[16], float p, const u32x4 (&x)[2]) {
+  const uint32_t w[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    acc[2 * u] = __builtin_fmaf(p, __uint_as_float(w[u] << 16), acc[2 * u]);
+    acc[2 * u + 1] = __builtin_fmaf(p, __uint_as_float(w[u] & 0xffff0000u), acc[2 * u + 1]);
+  }
+}
+
+// Workgroup b's tile index: XCD b mod 8 takes the contiguous range
+// [x * per_xcd, (x + 1) * per_xcd).
+__device__ __forceinline__ int tile_of_block(int per_xcd) {
+  return static_cast<int>(blockIdx.x % kXcds) * per_xcd + static_cast<int>(blockIdx.x / kXcds);
+}
+
+// Signed displacements of the head with the most (2 per positive distance,
+// 1 for distance 0).
+inline int max_signed(const Problem& p) {
+  int best = 0;
+  for (int h = 0; h < p.H; ++h) {
+    int32_t dist[kMaxOffsets];
+    const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], dist, kMaxOffsets);
+    int c = 0;
+    for (int i = 0; i < (n < kMaxOffsets ? n : kMaxOffsets); ++i) c += dist[i] == 0 ? 1 : 2;
+    best = c > best ? c : best;
+  }
+  return best;
+}
+
+}  // namespace tile
+}  // namespace fibatt

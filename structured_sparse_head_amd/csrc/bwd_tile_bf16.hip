@@ -1,5 +1,5 @@
-// Backward for long sequences, bf16, d_h = 64: exact gradients of the sparse
-// Fibottention attention on 64-row tiles read straight from global memory.
+// Backward for long sequences, bf16, d_h = 64 or 128: exact gradients of the
+// sparse Fibottention attention on tiles read straight from global memory.
 //
 // The Fibottention paper (method section, eq. (1) and (3)) defines the
 // forward; the backward is its derivative.  With P the support-restricted
@@ -45,8 +45,8 @@ struct BwdTileArgs {
   int tiles;
   int work;
   int per_xcd;
-  float c;      // log2(e) / sqrt(64)
-  float scale;  // 1 / sqrt(64)
+  float c;      // log2(e) / sqrt(d)
+  float scale;  // 1 / sqrt(d)
   HeadTableT<MH> ht;
 };
 
@@ -70,7 +70,8 @@ __device__ __forceinline__ void group_deltas(const int* deltas, int g, int (&d)[
   d[3] = __builtin_amdgcn_readfirstlane(d4.w);
 }
 
-// Stores this lane's 16 fp32 elements (groups p and p + 4) times `scale`.
+// Stores this lane's 16 fp32 elements (groups p and p + 4 of its 64-element
+// half) times `scale`; `row` already points at the half.
 __device__ __forceinline__ void store_row_f32(float* row, int part, const float (&x)[16],
                                               float scale) {
   float4* a = reinterpret_cast<float4*>(row + 8 * part);
@@ -86,8 +87,10 @@ __device__ __forceinline__ void frag_words(const u32x4 (&f)[2], uint32_t (&w)[8]
   w[4] = f[1].x; w[5] = f[1].y; w[6] = f[1].z; w[7] = f[1].w;
 }
 
-template <int MH, int KG>
+template <int MH, int KG, int NQ>
 __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<MH> a) {
+  using G = Geo<NQ>;
+  constexpr int kRowB = G::kRowB;
   __shared__ int s_dist[kMaxOffsets];
   __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
   __shared__ int s_nd;
@@ -101,19 +104,21 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;
   const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
-  const int row = tile * kTileRows + (threadIdx.x >> 2);
+  const int row = tile * G::kRows + tile_row<NQ>(threadIdx.x);
+  const int half = row_half<NQ>(threadIdx.x);
   const int rr = row < N ? row : N - 1;
   const size_t base = static_cast<size_t>(slab) * N * kRowB;
   const size_t rbase = static_cast<size_t>(slab) * N;
-  const char* kbase = a.k + base + part * 16;
-  const char* vbase = a.v + base + part * 16;
+  const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
+  const char* kbase = a.k + base + lofs;
+  const char* vbase = a.v + base + lofs;
 
   uint32_t qw[8], dw[8];
   {
     u32x4 f[2];
-    load_row_q(a.q + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    load_row_q(a.q + base + static_cast<size_t>(rr) * kRowB + lofs, f);
     frag_words(f, qw);
-    load_row_q(a.dout + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    load_row_q(a.dout + base + static_cast<size_t>(rr) * kRowB + lofs, f);
     frag_words(f, dw);
   }
   const float lse2 = a.lse[rbase + rr] * kLog2e;
@@ -141,8 +146,8 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
         ps[j] = dot_part(qw, kf[j]);
         pp[j] = dot_part(dw, vf[j]);
       }
-      const float sc = reduce4q(ps, b0, b1);
-      const float dp = reduce4q(pp, b0, b1);
+      const float sc = halves_sum<NQ>(reduce4q(ps, b0, b1));
+      const float dp = halves_sum<NQ>(reduce4q(pp, b0, b1));
       const int kk = rr + s_deltas[4 * g + part];
       const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
       const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse2)) : 0.f;
@@ -151,7 +156,7 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       dl = __builtin_fmaf(p, dp, dl);
     }
   }
-  const float dd = quad_sum4(dl);
+  const float dd = quad_sum4(dl);  // both halves of a row hold the same P, dP
 
   // Pass 2: dQ = sum dS K / sqrt(d).
   float acc[16];
@@ -174,12 +179,14 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       }
     }
   }
-  store_row_f32(a.dq + (rbase + rr) * 64, part, acc, a.scale);
-  if (part == 0) a.ws[rbase + rr] = dd;
+  store_row_f32(a.dq + (rbase + rr) * G::kD + 64 * half, part, acc, a.scale);
+  if (part == 0 && half == 0) a.ws[rbase + rr] = dd;
 }
 
-template <int MH>
+template <int MH, int NQ>
 __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs<MH> a) {
+  using G = Geo<NQ>;
+  constexpr int kRowB = G::kRowB;
   __shared__ int s_dist[kMaxOffsets];
   __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
   __shared__ int s_nd;
@@ -193,19 +200,21 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;
   const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
-  const int row = tile * kTileRows + (threadIdx.x >> 2);
+  const int row = tile * G::kRows + tile_row<NQ>(threadIdx.x);
+  const int half = row_half<NQ>(threadIdx.x);
   const int rr = row < N ? row : N - 1;  // key row
   const size_t base = static_cast<size_t>(slab) * N * kRowB;
   const size_t rbase = static_cast<size_t>(slab) * N;
-  const char* qbase = a.q + base + part * 16;
-  const char* obase = a.dout + base + part * 16;
+  const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
+  const char* qbase = a.q + base + lofs;
+  const char* obase = a.dout + base + lofs;
 
   uint32_t kw[8], vw[8];
   {
     u32x4 f[2];
-    load_row_q(a.k + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    load_row_q(a.k + base + static_cast<size_t>(rr) * kRowB + lofs, f);
     frag_words(f, kw);
-    load_row_q(a.v + base + static_cast<size_t>(rr) * kRowB + part * 16, f);
+    load_row_q(a.v + base + static_cast<size_t>(rr) * kRowB + lofs, f);
     frag_words(f, vw);
   }
   float dk[16], dv[16];
@@ -237,8 +246,8 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
       ps[j] = dot_part(kw, qf[j]);
       pp[j] = dot_part(vw, of[j]);
     }
-    const float sc = reduce4q(ps, b0, b1);
-    const float dp = reduce4q(pp, b0, b1);
+    const float sc = halves_sum<NQ>(reduce4q(ps, b0, b1));
+    const float dp = halves_sum<NQ>(reduce4q(pp, b0, b1));
     const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse_j * kLog2e)) : 0.f;
     float pg[4], dsg[4];
     gather4q(p, pg);
@@ -249,16 +258,17 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
       axpy_bf16(dk, dsg[j], qf[j]);
     }
   }
-  store_row_f32(a.dk + (rbase + rr) * 64, part, dk, a.scale);
-  store_row_f32(a.dv + (rbase + rr) * 64, part, dv, 1.0f);
+  store_row_f32(a.dk + (rbase + rr) * G::kD + 64 * half, part, dk, a.scale);
+  store_row_f32(a.dv + (rbase + rr) * G::kD + 64 * half, part, dv, 1.0f);
 }
 
-template <int MH, int KG>
+template <int MH, int KG, int NQ>
 void launch_dq(const BwdTileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ>), dim3(grid), dim3(kTileThreads), 0, stream,
+                     a);
 }
 
-template <int MH>
+template <int MH, int NQ>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
                     float* ws, hipStream_t stream) {
@@ -274,11 +284,11 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.ws = ws;
   a.H = p.H;
   a.N = p.N;
-  a.scale = 0.125f;  // 1 / sqrt(64)
-  a.c = kLog2e * 0.125f;
+  a.scale = 1.0f / sqrtf(static_cast<float>(Geo<NQ>::kD));
+  a.c = kLog2e * a.scale;
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const long long slabs = static_cast<long long>(p.B) * p.H;
-  a.tiles = (p.N + kTileRows - 1) / kTileRows;
+  a.tiles = (p.N + Geo<NQ>::kRows - 1) / Geo<NQ>::kRows;
   const long long work = slabs * a.tiles;
   if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
   a.work = static_cast<int>(work);
@@ -286,26 +296,34 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_dq<MH, 4>(a, grid, stream);
+    launch_dq<MH, 4, NQ>(a, grid, stream);
   else if (groups <= 8)
-    launch_dq<MH, 8>(a, grid, stream);
+    launch_dq<MH, 8, NQ>(a, grid, stream);
   else if (groups <= 12)
-    launch_dq<MH, 12>(a, grid, stream);
+    launch_dq<MH, 12, NQ>(a, grid, stream);
   else
-    launch_dq<MH, (kMaxSigned + 3) / 4>(a, grid, stream);
-  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+    launch_dq<MH, (kMaxSigned + 3) / 4, NQ>(a, grid, stream);
+  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ>), dim3(grid), dim3(kTileThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool bwd_tile_bf16_fits(const Problem& p) { return p.dtype == DType::kBF16 && p.D == 64; }
+bool bwd_tile_bf16_fits(const Problem& p) {
+  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
+}
 
 hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
                                 float* dv, float* ws, hipStream_t stream) {
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-  return launch_t<kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  if (p.D == 128) {
+    if (p.H <= kSmallHeads)
+      return launch_t<kSmallHeads, 2>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    return launch_t<kMaxHeads, 2>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  }
+  if (p.H <= kSmallHeads)
+    return launch_t<kSmallHeads, 1>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  return launch_t<kMaxHeads, 1>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
 }
 
 }  // namespace fibatt

@@ -1,4 +1,4 @@
-// Forward for long sequences, bf16, d_h = 64: sparse Fibottention attention
+// Forward for long sequences, bf16, d_h = 64 or 128: sparse Fibottention attention
 // O = softmax_Omega(Q K^T / sqrt(d)) V on query tiles read straight from
 // global memory.
 //
@@ -6,22 +6,22 @@
 // query row j only meets keys j + delta for the head's signed displacements
 // delta (+f and -f for every f in Fib(a_i, b_i) within the window, and 0 when
 // 0 is a distance).  For a fixed delta the keys of consecutive queries are
-// consecutive rows, so each load instruction of a wave (16 query rows) reads
-// 16 consecutive K or V rows: coalesced, and the rows come from L2 because
+// consecutive rows, so each load instruction of a wave (16 query rows, 8 for
+// d_h = 128) reads that many consecutive K or V rows: coalesced, and the rows come from L2 because
 // the neighbouring tiles of the slab read the same rows for other
 // displacements.
 //
 // Design points:
-//  * Lanes.  Four adjacent lanes own a query row: lane l of a wave works on
-//    row r0 + l / 4 and, with p = l % 4, on the 8-element groups p and p + 4
-//    of Q, K, V and O.  A lane quad then reads or writes 64 contiguous bytes
-//    per instruction, which the cache front end serves as one access (with
-//    the four lanes of a row 16 lanes apart every lane was an access of its
-//    own, and that access rate bounded the kernel).  Sums over a row use DPP
-//    quad permutations.
-//  * Work.  A workgroup (4 waves, 64 rows) takes one query tile.  Tiles are
-//    numbered slab by slab and dealt to the XCDs in contiguous ranges
-//    (workgroup b runs on XCD b mod 8), so the tiles of a slab share an L2.
+//  * Lanes.  A lane quad owns 64 elements of a query row (lane p of the quad:
+//    8-element groups p and p + 4 of Q, K, V and O), one quad per row for
+//    d_h = 64 and two for 128.  A quad then reads or writes 64 contiguous
+//    bytes per instruction, which the cache front end serves as one access
+//    (with the four lanes of a row 16 lanes apart every lane was an access of
+//    its own, and that access rate bounded the kernel).
+//  * Work.  A workgroup (4 waves) takes one query tile of 64 or 32 rows.
+//    Tiles are numbered slab by slab and dealt to the XCDs in contiguous
+//    ranges (workgroup b runs on XCD b mod 8), so the tiles of a slab share
+//    an L2.
 //  * Two passes instead of an online softmax.  Pass 1 forms every score of
 //    the row in groups of four displacements; a transposed reduction over the
 //    quad leaves one full score per lane (displacement 4 g + p in lane p), so
@@ -57,8 +57,10 @@ struct TileArgs {
 
 // KG: displacement groups of four the kernel holds scores for (at least
 // the largest head's count); smaller instantiations keep fewer registers.
-template <int MH, int KG>
+template <int MH, int KG, int NQ>
 __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH> a) {
+  using G = Geo<NQ>;
+  constexpr int kRowB = G::kRowB;
   __shared__ int s_dist[kMaxOffsets];
   __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
   __shared__ int s_nd;
@@ -78,19 +80,21 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   const int lane = tid & 63;
   const int part = lane & 3;
   const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
-  const int row = tile * kTileRows + (tid >> 2);
+  const int row = tile * G::kRows + tile_row<NQ>(tid);
+  const int half = row_half<NQ>(tid);
   const int rr = row < N ? row : N - 1;
   const size_t base = static_cast<size_t>(slab) * N * kRowB;
-  const char* kbase = a.k + base + part * 16;
-  const char* vbase = a.v + base + part * 16;
+  const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
+  const char* kbase = a.k + base + lofs;
+  const char* vbase = a.v + base + lofs;
 
   uint32_t qw[8];
   {
     u32x4 qf[2];
     qf[0] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(rr) * kRowB + part * 16));
+        reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(rr) * kRowB + lofs));
     qf[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        a.q + base + static_cast<size_t>(rr) * kRowB + part * 16 + 64));
+        a.q + base + static_cast<size_t>(rr) * kRowB + lofs + 64));
     qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
     qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
@@ -111,7 +115,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
       float pd[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) pd[j] = dot_part(qw, kf[j]);
-      const float t = reduce4q(pd, b0, b1);
+      const float t = halves_sum<NQ>(reduce4q(pd, b0, b1));
       const int kk = rr + s_deltas[4 * g + part];
       const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
       s[g] = ok ? t : -INFINITY;
@@ -120,7 +124,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   float m = s[0];
 #pragma unroll
   for (int g = 1; g < KG; ++g) m = fmaxf(m, s[g]);
-  m = quad_max4(m);
+  m = quad_max4(m);  // both halves of a row hold the same scores
 
   // Pass 2: P = exp(scale (s - m)), P V in fp32.  A row with no key in its
   // support keeps l = 0 and is written as O = 0, LSE = -inf.
@@ -157,7 +161,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
       }
     }
   }
-  l = quad_sum4(l);
+  l = quad_sum4(l);  // (the other half's l is the same)
   const float inv = any ? 1.0f / l : 0.f;
   uint32_t ow[8];
 #pragma unroll
@@ -167,19 +171,20 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     ow[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
-  char* orow = a.o + base + static_cast<size_t>(rr) * kRowB + part * 16;
+  char* orow = a.o + base + static_cast<size_t>(rr) * kRowB + lofs;
   *reinterpret_cast<u32x4*>(orow) = u32x4{ow[0], ow[1], ow[2], ow[3]};
   *reinterpret_cast<u32x4*>(orow + 64) = u32x4{ow[4], ow[5], ow[6], ow[7]};
-  if (part == 0)
+  if (part == 0 && half == 0)
     a.lse[static_cast<size_t>(slab) * N + rr] = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-template <int MH, int KG>
+template <int MH, int KG, int NQ>
 void launch_kg(const TileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ>), dim3(grid), dim3(kTileThreads), 0, stream,
+                     a);
 }
 
-template <int MH>
+template <int MH, int NQ>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                     float* lse, hipStream_t stream) {
   TileArgs<MH> a;
@@ -190,10 +195,10 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.lse = lse;
   a.H = p.H;
   a.N = p.N;
-  a.scale_log2 = kLog2e / 8.0f;  // 1 / sqrt(64)
+  a.scale_log2 = kLog2e / sqrtf(static_cast<float>(Geo<NQ>::kD));
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const long long slabs = static_cast<long long>(p.B) * p.H;
-  a.tiles = (p.N + kTileRows - 1) / kTileRows;
+  a.tiles = (p.N + Geo<NQ>::kRows - 1) / Geo<NQ>::kRows;
   const long long work = slabs * a.tiles;
   if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
   a.work = static_cast<int>(work);
@@ -201,24 +206,30 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_kg<MH, 4>(a, grid, stream);
+    launch_kg<MH, 4, NQ>(a, grid, stream);
   else if (groups <= 8)
-    launch_kg<MH, 8>(a, grid, stream);
+    launch_kg<MH, 8, NQ>(a, grid, stream);
   else if (groups <= 12)
-    launch_kg<MH, 12>(a, grid, stream);
+    launch_kg<MH, 12, NQ>(a, grid, stream);
   else
-    launch_kg<MH, (kMaxSigned + 3) / 4>(a, grid, stream);
+    launch_kg<MH, (kMaxSigned + 3) / 4, NQ>(a, grid, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool fwd_tile_bf16_fits(const Problem& p) { return p.dtype == DType::kBF16 && p.D == 64; }
+bool fwd_tile_bf16_fits(const Problem& p) {
+  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
+}
 
 hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream) {
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, o, lse, stream);
-  return launch_t<kMaxHeads>(p, q, k, v, o, lse, stream);
+  if (p.D == 128) {
+    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 2>(p, q, k, v, o, lse, stream);
+    return launch_t<kMaxHeads, 2>(p, q, k, v, o, lse, stream);
+  }
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 1>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads, 1>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace fibatt

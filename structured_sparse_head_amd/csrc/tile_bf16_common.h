@@ -1,10 +1,13 @@
-// Pieces shared by the long-sequence tile kernels (bf16, d_h = 64): four
-// adjacent lanes own a row (lane l works on row l / 4 of its wave's 16 and,
-// with p = l % 4, on the 8-element groups p and p + 4), so a lane quad reads
-// or writes 64 contiguous bytes per instruction.  Sums over a row use DPP
-// quad permutations.  Workgroups of 4 waves take 64-row tiles, numbered slab
-// by slab and dealt to the XCDs in contiguous ranges (workgroup b runs on XCD
-// b mod 8) so that the tiles of a slab share an L2.
+// Pieces shared by the long-sequence tile kernels (bf16, d_h = 64 or 128).
+// A lane quad owns 64 elements of a row: lane p of the quad works on the
+// 8-element groups p and p + 4 of them, so a quad reads or writes 64
+// contiguous bytes per instruction.  A row of d_h = 64 is one quad (16 rows
+// per wave); a row of 128 is two quads 32 lanes apart, one per half (8 rows
+// per wave).  Sums over a quad use DPP quad permutations, and the two halves
+// of a 128-wide row are joined with v_permlane32_swap.  Workgroups of 4 waves
+// take tiles of 64 or 32 rows, numbered slab by slab and dealt to the XCDs in
+// contiguous ranges (workgroup b runs on XCD b mod 8) so that the tiles of a
+// slab share an L2.
 #pragma once
 
 #include "slab_bf16_common.h"
@@ -12,10 +15,16 @@
 namespace fibatt {
 namespace tile {
 
-constexpr int kTileThreads = 256;              // 4 waves
-constexpr int kTileRows = kTileThreads / 4;    // 64 query rows
-constexpr int kRowB = 128;                     // bf16 row of 64
+constexpr int kTileThreads = 256;  // 4 waves
 constexpr int kXcds = 8;
+
+// NQ quads per row (d_h = 64 NQ).
+template <int NQ>
+struct Geo {
+  static constexpr int kRowB = 128 * NQ;              // bf16 row bytes
+  static constexpr int kRows = kTileThreads / 4 / NQ;  // rows per tile
+  static constexpr int kD = 64 * NQ;
+};
 
 // DPP quad permutations: lane i of each quad reads lane P[i].
 constexpr int kSwap1 = 0xB1;  // [1, 0, 3, 2]
@@ -43,6 +52,27 @@ __device__ __forceinline__ float reduce4q(const float (&x)[4], bool b0, bool b1)
   const float u0 = (b0 ? x[1] : x[0]) + qperm<kSwap1>(b0 ? x[0] : x[1]);
   const float u1 = (b0 ? x[3] : x[2]) + qperm<kSwap1>(b0 ? x[2] : x[3]);
   return (b1 ? u1 : u0) + qperm<kSwap2>(b1 ? u0 : u1);
+}
+
+// x summed with the other half of a 128-wide row, which sits 32 lanes away
+// (for partial dot products; values both halves already share need no join).
+template <int NQ>
+__device__ __forceinline__ float halves_sum(float x) {
+  if constexpr (NQ == 2) return slab::pair_sum(x);
+  return x;
+}
+// Row (within a tile) and half of lane `tid`: a wave holds 16 rows of
+// d_h = 64 (quad q = lane / 4 is row q), or 8 rows of d_h = 128 with the
+// first halves in lanes 0-31 and the second halves in lanes 32-63.
+template <int NQ>
+__device__ __forceinline__ int tile_row(int tid) {
+  if constexpr (NQ == 2) return (tid >> 6) * 8 + ((tid & 31) >> 2);
+  return tid >> 2;
+}
+template <int NQ>
+__device__ __forceinline__ int row_half(int tid) {
+  if constexpr (NQ == 2) return (tid >> 5) & 1;
+  return 0;
 }
 
 // y[j] = x of lane j of the quad.

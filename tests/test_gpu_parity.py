@@ -169,6 +169,10 @@ EDGE = [
     ("bf16 N256", 1, 4, 256, 64, torch.bfloat16, None, None),
     ("bf16 H20", 2, 20, 100, 64, torch.bfloat16, None, None),
     ("bf16 N33 tail", 3, 5, 33, 64, torch.bfloat16, None, None),
+    ("bf16 N300 diag windows", 2, 3, 300, 64, torch.bfloat16, ([0, 3, 5], [1, 3, 1]), [300, 50, 3]),
+    ("bf16 d128 N300 diag windows", 1, 3, 300, 128, torch.bfloat16, ([0, 3, 5], [1, 3, 1]),
+     [300, 50, 3]),
+    ("bf16 d128 N77 H20", 2, 20, 77, 128, torch.bfloat16, None, None),
 ]
 
 

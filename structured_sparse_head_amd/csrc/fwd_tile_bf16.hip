@@ -50,7 +50,8 @@ struct TileArgs {
   int N;
   int tiles;    // query tiles per slab
   int work;     // slabs * tiles
-  int per_xcd;  // ceil(work / 8)
+  int per_xcd;  // tile order: see tile_of_block
+  int chunk;
   float scale_log2;
   HeadTableT<MH> ht;
 };
@@ -64,8 +65,8 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   __shared__ int s_dist[kMaxOffsets];
   __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
   __shared__ int s_nd;
-  const int w = tile_of_block(a.per_xcd);
-  if (w >= a.work) return;  // whole workgroup, before any barrier
+  const int w = tile_of_block(a.per_xcd, a.chunk, a.tiles);
+  if (w < 0 || w >= a.work) return;  // whole workgroup, before any barrier
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
@@ -202,8 +203,10 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const long long work = slabs * a.tiles;
   if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
   a.work = static_cast<int>(work);
-  a.per_xcd = (a.work + kXcds - 1) / kXcds;
-  const unsigned grid = static_cast<unsigned>(a.per_xcd) * kXcds;
+  const long long grid_ll =
+      tile_grid(slabs, a.tiles, 2ll * p.N * Geo<NQ>::kRowB, a.per_xcd, a.chunk);
+  if (grid_ll > 0x7fffffffll) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
     launch_kg<MH, 4, NQ>(a, grid, stream);

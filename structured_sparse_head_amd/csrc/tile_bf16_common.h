@@ -100,10 +100,38 @@ __device__ __forceinline__ void axpy_bf16(float (&acc)[16], float p, const u32x4
   }
 }
 
-// Workgroup b's tile index: XCD b mod 8 takes the contiguous range
-// [x * per_xcd, (x + 1) * per_xcd).
-__device__ __forceinline__ int tile_of_block(int per_xcd) {
-  return static_cast<int>(blockIdx.x % kXcds) * per_xcd + static_cast<int>(blockIdx.x / kXcds);
+// Workgroup b's tile index (-1 for none), b running on XCD x = b mod 8.
+//  * Small slabs (per_xcd > 0): XCD x takes the contiguous range
+//    [x * per_xcd, (x + 1) * per_xcd) of all tiles, so a slab's tiles share
+//    one L2.
+//  * Large slabs (chunk > 0): every slab's tiles are cut into 8 contiguous
+//    chunks of `chunk` tiles; XCD x takes chunk x of slab 0, then of slab 1,
+//    and so on.  All XCDs work on one slab at a time (its K and V stay in the
+//    Infinity Cache) while each keeps its own row window in its L2.
+__device__ __forceinline__ int tile_of_block(int per_xcd, int chunk, int tiles) {
+  const int x = static_cast<int>(blockIdx.x % kXcds);
+  const int k = static_cast<int>(blockIdx.x / kXcds);
+  if (chunk == 0) return x * per_xcd + k;
+  const int slab = k / chunk;
+  const int t = x * chunk + (k - slab * chunk);
+  return t < tiles ? slab * tiles + t : -1;
+}
+
+// Launch shape for `slabs` slabs of `tiles` tiles whose K and V take
+// `slab_kv` bytes: the first order above while a slab's K and V fit in half
+// an L2 (4 MB per XCD), the second otherwise.  Returns the grid size.
+inline long long tile_grid(long long slabs, int tiles, long long slab_kv, int& per_xcd,
+                          int& chunk) {
+  constexpr long long kHalfL2 = 2ll << 20;
+  const long long work = slabs * tiles;
+  if (slab_kv <= kHalfL2) {
+    chunk = 0;
+    per_xcd = static_cast<int>((work + kXcds - 1) / kXcds);
+    return static_cast<long long>(per_xcd) * kXcds;
+  }
+  per_xcd = 0;
+  chunk = (tiles + kXcds - 1) / kXcds;
+  return slabs * chunk * kXcds;
 }
 
 // Signed displacements of the head with the most (2 per positive distance,

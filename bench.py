@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--modified", action="store_true",
+                    help="heads from README Algorithm 2's modified Wythoff pairs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 10 times "
                          "(scale reference for HBM byte counters), then exit")
@@ -151,7 +153,7 @@ def main():
 
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    a, b = fa.wythoff_rows(wl.H)
+    a, b = fa.wythoff_rows(wl.H, modified=args.modified)
     w = workloads.windows(wl)
     ptr, offs = fa.offsets(wl.N, a, b, w)
     F = [[int(f) for f in offs[ptr[h]:ptr[h + 1]]] for h in range(wl.H)]
@@ -237,7 +239,7 @@ def main():
             "workload": f"Fibottention attention, {wl.name} (ViT-B/16 224px tokens)"
             if args.workload == 2 else f"Fibottention attention, {wl.name}",
             "B": wl.B, "H": wl.H, "N": wl.N, "d_h": wl.d,
-            "heads": "Wythoff rows 1..H",
+            "heads": "modified Wythoff pairs, rows 1..H" if args.modified else "Wythoff rows 1..H",
             "pairs_per_pass": pairs_per_pass,
             "buffer_sets": R,
         },

@@ -84,6 +84,20 @@ typedef struct {
  * if *b would exceed INT32_MAX. */
 int fibatt_wythoff(int32_t i, int32_t* a, int32_t* b);
 
+/* The modified pair of README Algorithm 2 (its is_modified branch) for
+ * Wythoff row i >= 1: with (a, b) = fibatt_wythoff(i), *b = b - a and
+ * *a = a - (b - a), the Fibonacci recurrence run two steps back, so that
+ * Fib(*a, *b) = *a, *b, a, b, ...  For row 1 this is (0, 1): head 1 then
+ * attends distance 0 as well.  Errors as fibatt_wythoff. */
+int fibatt_wythoff_modified(int32_t i, int32_t* a, int32_t* b);
+
+/* Per-head windows interpolated between w_min and w_max (Fibottention paper,
+ * method section): w[i - 1] = w_min + floor((w_max - w_min)(i - 1)/(H - 1))
+ * for heads i = 1..H; a single head gets w_max (the formula is undefined
+ * for H = 1).  w is a host array of H int32.  Errors: E_INVAL for H < 1,
+ * w NULL, w_min < 1 or w_max < w_min. */
+int fibatt_windows(int32_t H, int32_t w_min, int32_t w_max, int32_t* w);
+
 /* Host-only offset table (no GPU involved).  For each head h, the distinct
  * distances f of Fib(a[h], b[h]) with f <= min(w[h], N - 1), ascending
  * (README Algorithm 1 generates the sequence; the paper's set definition

@@ -18,6 +18,7 @@ from .fibottention import (  # noqa: F401
     support_mask,
     window_sizes,
     wythoff_row,
+    wythoff_row_modified,
     wythoff_rows,
     zeckendorf,
 )

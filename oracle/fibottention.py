@@ -136,9 +136,20 @@ def _first_column(count: int) -> List[int]:
     return _FIRST_COLUMN
 
 
-def wythoff_rows(h: int) -> Tuple[np.ndarray, np.ndarray]:
-    """(a, b) int32 arrays for heads 1..h (R2)."""
-    pairs = [wythoff_row(i) for i in range(1, h + 1)]
+def wythoff_row_modified(i: int) -> Tuple[int, int]:
+    """README Algorithm 2, modified branch: from row i's (a, b) take
+    b_m = b - a and a_m = a - b_m, i.e. the recurrence run two steps back, so
+    Fib(a_m, b_m) = a_m, b_m, a, b, ...  (Head 1 then starts 0, 1.)"""
+    a, b = wythoff_row(i)
+    b_m = b - a
+    return a - b_m, b_m
+
+
+def wythoff_rows(h: int, modified: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """(a, b) int32 arrays for heads 1..h (R2); `modified` selects README
+    Algorithm 2's modified pairs."""
+    row = wythoff_row_modified if modified else wythoff_row
+    pairs = [row(i) for i in range(1, h + 1)]
     a = np.array([p[0] for p in pairs], dtype=np.int32)
     b = np.array([p[1] for p in pairs], dtype=np.int32)
     return a, b

@@ -22,6 +22,8 @@ from .fibatt import (  # noqa: F401
     forward,
     lib,
     offsets,
+    windows,
     wythoff,
+    wythoff_modified,
     wythoff_rows,
 )

@@ -122,6 +122,33 @@ int fibatt_wythoff(int32_t i, int32_t* a, int32_t* b) {
   return ok();
 }
 
+int fibatt_wythoff_modified(int32_t i, int32_t* a, int32_t* b) {
+  if (!a || !b) return fail(FIBATT_E_INVAL, "output pointers must be non-NULL");
+  if (i < 1) return fail(FIBATT_E_INVAL, "Wythoff rows are numbered from 1 (got %d)", i);
+  const uint64_t p = floor_n_phi(static_cast<uint64_t>(i));
+  const uint64_t av = floor_n_phi(p);
+  const uint64_t bv = av + p;
+  const uint64_t bm = bv - av;  // b_m = b - a
+  const uint64_t am = av - bm;  // a_m = a - b_m
+  if (bm > 0x7fffffffull) return fail(FIBATT_E_RANGE, "row %d does not fit int32", i);
+  *a = static_cast<int32_t>(am);
+  *b = static_cast<int32_t>(bm);
+  return ok();
+}
+
+int fibatt_windows(int32_t H, int32_t w_min, int32_t w_max, int32_t* w) {
+  if (H < 1 || !w) return fail(FIBATT_E_INVAL, "need H >= 1 and a non-NULL w");
+  if (w_min < 1 || w_max < w_min)
+    return fail(FIBATT_E_INVAL, "need 1 <= w_min <= w_max (got %d, %d)", w_min, w_max);
+  if (H == 1) {
+    w[0] = w_max;
+    return ok();
+  }
+  for (int32_t i = 1; i <= H; ++i)
+    w[i - 1] = w_min + static_cast<int32_t>(static_cast<int64_t>(w_max - w_min) * (i - 1) / (H - 1));
+  return ok();
+}
+
 int fibatt_offsets(int32_t H, int32_t N, const int32_t* a, const int32_t* b, const int32_t* w,
                    int32_t* head_ptr, int32_t* offs, int32_t offs_cap) {
   if (H < 1 || N < 1) return fail(FIBATT_E_INVAL, "H and N must be >= 1 (got %d, %d)", H, N);

@@ -22,8 +22,8 @@ OK, E_INVAL, E_RANGE, E_UNSUPPORTED, E_HIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 MAX_HEADS = 128
 
-EXPORTED = ("fibatt_wythoff", "fibatt_offsets", "fibatt_fwd", "fibatt_bwd",
-            "fibatt_bwd_workspace_floats", "fibatt_last_error")
+EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fibatt_offsets",
+            "fibatt_fwd", "fibatt_bwd", "fibatt_bwd_workspace_floats", "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     L.fibatt_wythoff.argtypes = [ctypes.c_int32, i32p, i32p]
     L.fibatt_wythoff.restype = ctypes.c_int
+    L.fibatt_wythoff_modified.argtypes = [ctypes.c_int32, i32p, i32p]
+    L.fibatt_wythoff_modified.restype = ctypes.c_int
+    L.fibatt_windows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]
+    L.fibatt_windows.restype = ctypes.c_int
     L.fibatt_offsets.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p, i32p, i32p,
                                  ctypes.c_int32]
     L.fibatt_offsets.restype = ctypes.c_int
@@ -97,10 +101,26 @@ def wythoff(i: int) -> Tuple[int, int]:
     return a.value, b.value
 
 
-def wythoff_rows(H: int) -> Tuple[np.ndarray, np.ndarray]:
-    """(a, b) int32 arrays for tensor heads 0..H-1 (Wythoff rows 1..H)."""
-    pairs = [wythoff(i) for i in range(1, H + 1)]
+def wythoff_modified(i: int) -> Tuple[int, int]:
+    """README Algorithm 2's modified pair for Wythoff row i >= 1."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().fibatt_wythoff_modified(i, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def wythoff_rows(H: int, modified: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """(a, b) int32 arrays for tensor heads 0..H-1 (Wythoff rows 1..H, or
+    their modified pairs)."""
+    row = wythoff_modified if modified else wythoff
+    pairs = [row(i) for i in range(1, H + 1)]
     return _i32([p[0] for p in pairs]), _i32([p[1] for p in pairs])
+
+
+def windows(H: int, w_min: int, w_max: int) -> np.ndarray:
+    """Per-head windows interpolated between w_min and w_max."""
+    w = np.zeros(H, dtype=np.int32)
+    _check(lib().fibatt_windows(H, w_min, w_max, _ptr(w)))
+    return w
 
 
 def offsets(N: int, a, b, w) -> Tuple[np.ndarray, np.ndarray]:

@@ -50,6 +50,31 @@ def test_wythoff_large_rows_match_decimal_closed_form():
             assert fa.wythoff(i) == (a, b), i
 
 
+def test_wythoff_modified_matches_oracle():
+    for i in range(1, 1001):
+        assert fa.wythoff_modified(i) == oracle.wythoff_row_modified(i), i
+    a, b = fa.wythoff_rows(12, modified=True)
+    oa, ob = oracle.wythoff_rows(12, modified=True)
+    assert np.array_equal(a, oa) and np.array_equal(b, ob)
+
+
+def test_wythoff_modified_rejects_bad_rows():
+    for i in (0, -5):
+        with pytest.raises(fa.FibattError) as ei:
+            fa.wythoff_modified(i)
+        assert ei.value.code == fa.E_INVAL
+
+
+def test_windows_match_oracle():
+    for H in (1, 2, 3, 12, 16, 100):
+        for w_min, w_max in ((1, 1), (5, 65), (49, 197), (1, 2 ** 31 - 1), (7, 8)):
+            assert list(fa.windows(H, w_min, w_max)) == oracle.window_sizes(H, w_min, w_max)
+    for H, lo, hi in ((0, 1, 2), (3, 0, 2), (3, 5, 4)):
+        with pytest.raises(fa.FibattError) as ei:
+            fa.windows(H, lo, hi)
+        assert ei.value.code == fa.E_INVAL
+
+
 def test_wythoff_rejects_bad_rows():
     for i in (0, -1, -(2 ** 31)):
         with pytest.raises(fa.FibattError) as ei:

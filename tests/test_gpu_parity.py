@@ -193,6 +193,29 @@ def test_edge_cases(case, path):
         _set_path(None)
 
 
+MODIFIED = [
+    # (name, B, H, N, d, dtype): heads from README Algorithm 2's modified pairs
+    ("vit N197", 2, 12, 197, 64, torch.bfloat16),
+    ("tile N700", 1, 12, 700, 64, torch.bfloat16),
+    ("tile d128 N300", 1, 6, 300, 128, torch.bfloat16),
+    ("fp32 N90", 2, 4, 90, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", MODIFIED, ids=[c[0] for c in MODIFIED])
+def test_modified_wythoff_heads(case):
+    name, B, H, N, d, dtype = case
+    _say(f"case: modified Wythoff heads {name} B={B} H={H} N={N} d={d} {dtype}")
+    ab = fa.wythoff_rows(H, modified=True)
+    oa, ob = oracle.wythoff_rows(H, modified=True)
+    assert np.array_equal(ab[0], oa) and np.array_equal(ab[1], ob)
+    a, b, w, F = _heads(H, N, ab=ab)
+    assert 0 in F[0]  # head 1 attends distance 0
+    inp = workloads.random_case(31 + N, B, H, N, d, dtype)
+    gpu = _gpu_run(inp, a, b, w)
+    _compare(gpu, inp, F, TOL[dtype])
+
+
 def test_empty_support_gives_zero_and_neg_inf():
     _say("case: all rows empty (N=4, heads 2..3 have no distance < 4)")
     inp = workloads.random_case(5, 1, 3, 4, 64, torch.float32)

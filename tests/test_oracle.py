@@ -183,6 +183,29 @@ def test_pages_two_percent_figure():
     assert all(s < 5 for s in shares)
 
 
+def test_wythoff_modified_is_extended_array_columns():
+    # The recurrence run two steps back from row i lands on columns -1 and 0
+    # of the extended Wythoff array: i - 1 and floor(i phi).  Checked against
+    # a decimal evaluation of floor(i phi), not against the oracle's Zeckendorf
+    # construction.
+    for i in range(1, 1501):
+        a_m, b_m = oracle.wythoff_row_modified(i)
+        assert a_m == i - 1, i
+        assert b_m == _floor_phi_decimal(i), i
+
+
+def test_wythoff_modified_offsets_extend_the_row():
+    N = 1000
+    for i in range(1, 13):
+        a, b = oracle.wythoff_row(i)
+        a_m, b_m = oracle.wythoff_row_modified(i)
+        plain = set(oracle.fib_offsets(a, b, N, N))
+        mod = set(oracle.fib_offsets(a_m, b_m, N, N))
+        assert plain <= mod and mod - plain == {a_m, b_m} - plain, i
+    # Head 1: 0, 1, 1, 2, 3, ... -> distance 0 joins the support.
+    assert oracle.fib_offsets(*oracle.wythoff_row_modified(1), 20, 21) == [0, 1, 2, 3, 5, 8, 13]
+
+
 def test_window_sizes_interpolate():
     assert oracle.window_sizes(12, 5, 65) == [5 + (60 * i) // 11 for i in range(12)]
     ws = oracle.window_sizes(12, 5, 65)

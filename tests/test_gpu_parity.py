@@ -173,6 +173,9 @@ EDGE = [
     ("bf16 d128 N300 diag windows", 1, 3, 300, 128, torch.bfloat16, ([0, 3, 5], [1, 3, 1]),
      [300, 50, 3]),
     ("bf16 d128 N77 H20", 2, 20, 77, 128, torch.bfloat16, None, None),
+    ("bf16 d128 N1", 2, 3, 1, 128, torch.bfloat16, None, None),
+    ("bf16 d128 N2 H17", 1, 17, 2, 128, torch.bfloat16, None, None),
+    ("bf16 N258 H17 w1", 1, 17, 258, 64, torch.bfloat16, None, [1] * 17),
 ]
 
 

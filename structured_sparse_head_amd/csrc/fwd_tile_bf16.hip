@@ -100,22 +100,28 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
 
-  // Pass 1: scores, one per lane and group of four displacements.
+  // Pass 1: scores, one per lane and group of four displacements.  The next
+  // group's rows are requested before this group's dot products; one
+  // fragment variable per group, so guarded loads merge with nothing.
   float s[KG];
+  u32x4 kf[KG][4][2];
+  auto load_k = [&](int g) {
+    const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
+    const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
+                      __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf[g][j]);
+  };
+  if (0 < nd) load_k(0);
 #pragma unroll
   for (int g = 0; g < KG; ++g) {
     s[g] = -INFINITY;
     if (4 * g < nd) {
-      const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
-      const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
-                        __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
-      u32x4 kf[4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf[j]);
+      if (g + 1 < KG && 4 * (g + 1) < nd) load_k(g + 1);
       float pd[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pd[j] = dot_part(qw, kf[j]);
+      for (int j = 0; j < 4; ++j) pd[j] = dot_part(qw, kf[g][j]);
       const float t = halves_sum<NQ>(reduce4q(pd, b0, b1));
       const int kk = rr + s_deltas[4 * g + part];
       const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
@@ -128,7 +134,9 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   m = quad_max4(m);  // both halves of a row hold the same scores
 
   // Pass 2: P = exp(scale (s - m)), P V in fp32.  A row with no key in its
-  // support keeps l = 0 and is written as O = 0, LSE = -inf.
+  // support keeps l = 0 and is written as O = 0, LSE = -inf.  A group's four
+  // V rows are requested together, a group ahead (slots past the end have
+  // P = 0 and read a valid row).
   const bool any = m != -INFINITY;
   const float c = a.scale_log2;
   const float mc = any ? m * c : 0.f;
@@ -136,30 +144,26 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   float o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  u32x4 vf[KG][4][2];
+  auto load_v = [&](int g) {
+    const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
+    const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
+                      __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      load_row_q(vbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, vf[g][j]);
+  };
+  if (0 < nd) load_v(0);
 #pragma unroll
   for (int g = 0; g < KG; ++g) {
     if (4 * g < nd) {
+      if (g + 1 < KG && 4 * (g + 1) < nd) load_v(g + 1);
       const float pown = fast_exp2(__builtin_fmaf(s[g], c, -mc));  // 0 for s = -inf
       l += pown;
       float p[4];
       gather4q(pown, p);
-      const int4 d4 = *reinterpret_cast<const int4*>(&s_deltas[4 * g]);
-      const int d[4] = {__builtin_amdgcn_readfirstlane(d4.x), __builtin_amdgcn_readfirstlane(d4.y),
-                        __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (4 * g + j < nd) {
-          u32x4 vf[2];
-          load_row_q(vbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, vf);
-          const uint32_t x[8] = {vf[0].x, vf[0].y, vf[0].z, vf[0].w,
-                                 vf[1].x, vf[1].y, vf[1].z, vf[1].w};
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            o[2 * u] = __builtin_fmaf(p[j], __uint_as_float(x[u] << 16), o[2 * u]);
-            o[2 * u + 1] = __builtin_fmaf(p[j], __uint_as_float(x[u] & 0xffff0000u), o[2 * u + 1]);
-          }
-        }
-      }
+      for (int j = 0; j < 4; ++j) axpy_bf16(o, p[j], vf[g][j]);
     }
   }
   l = quad_sum4(l);  // (the other half's l is the same)

@@ -13,7 +13,7 @@
 // Lanes.  1024 threads (16 waves, four per SIMD so that LDS and arithmetic
 // latency is hidden by other waves); four lanes own a row: lane l of wave w
 // works on row 16 b_w + (l % 16), b_w the wave's row block (plan_blocks),
-// and, with p = (l / 16 + (l % 16) / 4) mod 4
+// and, with p = (l / 16) xor parity((l % 16) / 4)
 // (see slab_bf16_common.h), on the element groups {4 g .. 4 g + 3} for
 // g = p, p + 4, p + 8, p + 12.  The four lanes of a row
 // therefore cover each 64-byte span of an fp32 output row together, so every

@@ -11,7 +11,7 @@
 //    arithmetic latency is hidden by other waves); four lanes own a row:
 //    lane l of wave w works on row 16 b_w + (l % 16), where b_w is the
 //    wave's row block (plan_blocks), and, with
-//    p = (l / 16 + (l % 16) / 4) mod 4 (see slab_bf16_common.h), on the
+//    p = (l / 16) xor parity((l % 16) / 4) (see slab_bf16_common.h), on the
 //    8-element groups p and p + 4.  The four lanes of a row thus cover
 //    each 64-byte half of the bf16 output row together, so every store
 //    instruction writes whole 64-byte pieces.  LDS rows are kept permuted

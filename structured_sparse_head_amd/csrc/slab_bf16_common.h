@@ -12,11 +12,10 @@
 // gfx950 (64 banks), a ds_read_b128 serves the two 32-lane halves of a wave
 // separately and, within a half, the lane quads whose index has even
 // popcount ({0-3, 12-15, 20-23, 24-27}) together and the odd ones together.
-// With part = (l / 16 + (l % 16) / 4) mod 4 for lane l (the row's four lanes
-// still hold four different parts), every such group of an fp32 read hits 16
-// distinct 16-byte bank groups for any first row: no conflicts, found by
-// exhaustive search.  No part assignment makes the bf16 reads conflict-free
-// as well; they keep two-way conflicts on half the traffic.
+// With part = (l / 16) xor parity((l % 16) / 4) for lane l (the row's four
+// lanes still hold four different parts), every such group of an fp32 read
+// and of a bf16 read hits 16 distinct 16-byte bank groups for any first row:
+// no conflicts for either stride, found by exhaustive search.
 #pragma once
 
 #include "fib_offsets.h"
@@ -40,7 +39,9 @@ __device__ __forceinline__ int b16_chunk(int r, int c) { return __umul24(r, kBf1
 __device__ __forceinline__ int f32_chunk(int r, int c) { return __umul24(r, kF32Stride) + c * 16; }
 
 // Part (which 16 of the 64 elements) lane l of a wave works on.
-__device__ __forceinline__ int lane_part(int lane) { return ((lane >> 4) + ((lane & 15) >> 2)) & 3; }
+__device__ __forceinline__ int lane_part(int lane) {
+  return ((lane >> 4) & 3) ^ (((lane >> 2) ^ (lane >> 3)) & 1);
+}
 
 // Sum of x over the lane pair (l, l ^ 32).
 __device__ __forceinline__ float pair_sum(float x) {

@@ -7,6 +7,7 @@ neither imports nor links anything from ``structured_sparse_head_amd``.
 
 from .fibottention import (  # noqa: F401
     backward,
+    cls_support_mask,
     dense_backward,
     dense_forward,
     fib_offsets,

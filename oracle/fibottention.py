@@ -52,6 +52,12 @@ R6  A query row with no key in the support gets O = 0, LSE = -inf and
     contributes nothing to any gradient.
 R7  An offset of 0 (only possible when a = 0) is the diagonal and counts once.
 R8  Token 0 (a CLS token) is an ordinary token: no dense row or column.
+    The other reading, README Algorithm 2's mask whose row and column 0 are
+    all ones (the class token attends every token and every token attends
+    it), is the ``cls=True`` variant of ``forward`` and ``backward``.  There
+    the pages index the N patch tokens 1..N behind the class token, so the
+    distances between two patches are the same as between their positions
+    here; pair (0, 0) is in the support as well.
 """
 
 from __future__ import annotations
@@ -212,6 +218,22 @@ def support_mask(n_tokens: int, offsets: Sequence[int]) -> np.ndarray:
     return m
 
 
+def cls_support_mask(n_tokens: int, offsets: Sequence[int]) -> np.ndarray:
+    """README Algorithm 2's class-token mask: Omega among tokens 1..N-1 and
+    ones in row 0 and column 0."""
+    m = support_mask(n_tokens, offsets)
+    m[0, :] = True
+    m[:, 0] = True
+    return m
+
+
+def _cls_extra_rows(n_tokens: int, offsets: Sequence[int]) -> np.ndarray:
+    """Rows j >= 1 that gain key 0 under the class-token mask: those whose
+    distance j to token 0 is not one of the head's offsets."""
+    dist = set(int(f) for f in offsets)
+    return np.array([j >= 1 and j not in dist for j in range(n_tokens)], dtype=bool)
+
+
 def signed_offsets(offsets: Sequence[int]) -> List[int]:
     """Key displacement k - j for every distance (0 once, f > 0 as -f and +f)."""
     out = []
@@ -255,12 +277,35 @@ def _head_probs(S):
     return P, lse
 
 
+def _cls_scores(q, k, extra):
+    """One extra score slot per row: Q_j . K_0 / sqrt(d) for the rows that
+    gain key 0 under the class-token mask, -inf elsewhere.  Shape [1, B, N]."""
+    B, N, d = q.shape
+    c = np.full((1, B, N), -np.inf)
+    c[0][:, extra] = (q[:, extra, :] * k[:, 0:1, :]).sum(-1) / math.sqrt(d)
+    return c
+
+
+def _dense_row0(q, k):
+    """Class-token row: scores of token 0 against every key and their
+    softmax.  Returns (P0 [B, N], lse0 [B])."""
+    s0 = (q[:, 0:1, :] * k).sum(-1) / math.sqrt(q.shape[-1])   # [B, N]
+    m = s0.max(axis=1)
+    e = np.exp(s0 - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m + np.log(l)
+
+
 def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-            offsets_per_head: Sequence[Sequence[int]]):
+            offsets_per_head: Sequence[Sequence[int]], cls: bool = False):
     """O and LSE (natural log) for q, k, v of shape [B, H, N, d] (fp64).
 
     Implementation: one pass per signed offset over contiguous slices, then a
     two-pass (max, then exp-sum) softmax.  Returns (o [B,H,N,d], lse [B,H,N]).
+
+    cls=True applies README Algorithm 2's class-token mask: each row j >= 1
+    whose distance to token 0 is not an offset gets key 0 as one more score
+    slot, and row 0 is a dense softmax over all N keys.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, N, d = q.shape
@@ -269,11 +314,19 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     for h in range(H):
         deltas = signed_offsets(offsets_per_head[h])
         S = _head_scores(q[:, h], k[:, h], deltas)
+        if cls:
+            extra = _cls_extra_rows(N, offsets_per_head[h])
+            S = np.concatenate([S, _cls_scores(q[:, h], k[:, h], extra)])
+            S[:, :, 0] = -np.inf        # row 0 is replaced by the dense row below
         P, lse[:, h] = _head_probs(S)
         for i, dl in enumerate(deltas):
             lo, hi = max(0, -dl), min(N, N - dl)
             if lo < hi:
                 o[:, h, lo:hi, :] += P[i, :, lo:hi, None] * v[:, h, lo + dl:hi + dl, :]
+        if cls:
+            o[:, h] += P[-1][:, :, None] * v[:, h, 0:1, :]
+            P0, lse[:, h, 0] = _dense_row0(q[:, h], k[:, h])
+            o[:, h, 0] = (P0[:, :, None] * v[:, h]).sum(axis=1)
     return o, lse
 
 
@@ -283,7 +336,7 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-             offsets_per_head: Sequence[Sequence[int]]):
+             offsets_per_head: Sequence[Sequence[int]], cls: bool = False):
     """dQ, dK, dV of sum(O * dO) for the forward above (fp64).
 
     With P the support-restricted softmax and dP_jk = dO_j . V_k:
@@ -293,7 +346,9 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
       dK_k  = sum_j dS_jk Q_j / sqrt(d)
       dV_k  = sum_j P_jk dO_j
     The key-side sums are accumulated query-centrically (a slice add per
-    signed offset), not key-centrically like the HIP kernels.
+    signed offset), not key-centrically like the HIP kernels.  cls=True is
+    the class-token mask of ``forward``: the extra key-0 slot of rows j >= 1
+    and the dense row 0 enter the same formulas.
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, H, N, d = q.shape
@@ -304,12 +359,18 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     for h in range(H):
         deltas = signed_offsets(offsets_per_head[h])
         S = _head_scores(q[:, h], k[:, h], deltas)
+        if cls:
+            extra = _cls_extra_rows(N, offsets_per_head[h])
+            S = np.concatenate([S, _cls_scores(q[:, h], k[:, h], extra)])
+            S[:, :, 0] = -np.inf
         P, _ = _head_probs(S)
         dP = np.zeros_like(P)
         for i, dl in enumerate(deltas):
             lo, hi = max(0, -dl), min(N, N - dl)
             if lo < hi:
                 dP[i, :, lo:hi] = (do[:, h, lo:hi, :] * v[:, h, lo + dl:hi + dl, :]).sum(-1)
+        if cls:
+            dP[-1] = (do[:, h] * v[:, h, 0:1, :]).sum(-1)
         D = (P * dP).sum(axis=0)
         dS = P * (dP - D[None])
         for i, dl in enumerate(deltas):
@@ -320,6 +381,19 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
             dq[:, h, lo:hi, :] += dS[i, :, lo:hi, None] * k[:, h, ks, :] * scale
             dk[:, h, ks, :] += dS[i, :, lo:hi, None] * q[:, h, lo:hi, :] * scale
             dv[:, h, ks, :] += P[i, :, lo:hi, None] * do[:, h, lo:hi, :]
+        if cls:
+            # extra key-0 slot of rows j >= 1
+            dq[:, h] += dS[-1][:, :, None] * k[:, h, 0:1, :] * scale
+            dk[:, h, 0] += (dS[-1][:, :, None] * q[:, h]).sum(axis=1) * scale
+            dv[:, h, 0] += (P[-1][:, :, None] * do[:, h]).sum(axis=1)
+            # dense row 0
+            P0, _ = _dense_row0(q[:, h], k[:, h])                    # [B, N]
+            dP0 = (do[:, h, 0:1, :] * v[:, h]).sum(-1)               # [B, N]
+            D0 = (P0 * dP0).sum(axis=1)
+            dS0 = P0 * (dP0 - D0[:, None])
+            dq[:, h, 0] += (dS0[:, :, None] * k[:, h]).sum(axis=1) * scale
+            dk[:, h] += dS0[:, :, None] * q[:, h, 0:1, :] * scale
+            dv[:, h] += P0[:, :, None] * do[:, h, 0:1, :]
     return dq, dk, dv
 
 

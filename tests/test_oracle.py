@@ -359,3 +359,107 @@ def test_backward_invariants():
     q, k, v, do, F, masks = _tiny_case(6, H=4, d=8, seed=2, wyt=False)
     dq, dk, dv = oracle.backward(q, k, v, do, F)
     assert (dq[:, 3] == 0).all() and (dk[:, 3] == 0).all() and (dv[:, 3] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# Class-token variant (README Algorithm 2: row and column 0 of the mask are
+# all ones)
+# --------------------------------------------------------------------------
+
+def _cls_case(N, B=2, d=8, seed=0):
+    """Wythoff heads 1..3 plus a head with the diagonal (a = 0) and one with
+    no distance below N (empty Fibonacci support)."""
+    q, k, v, do = (_rand((B, 5, N, d), seed + t) for t in range(4))
+    a, b = oracle.wythoff_rows(3)
+    F = [oracle.fib_offsets(int(a[h]), int(b[h]), N, N) for h in range(3)]
+    F.append(oracle.fib_offsets(0, 2, N, N))           # 0, 2, 4, 6, 10, ...
+    F.append([f for f in [N + 5] if f <= N - 1])       # nothing in range
+    masks = np.stack([oracle.cls_support_mask(N, f) for f in F])
+    return q, k, v, do, F, masks
+
+
+def _torch_masked_attention(q, k, v, masks):
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) / math.sqrt(q.shape[-1])
+    m = torch.from_numpy(masks)[None]
+    p = torch.softmax(s.masked_fill(~m, float("-inf")), -1)
+    return tq, tk, tv, torch.matmul(p, tv), torch.logsumexp(s.masked_fill(~m, float("-inf")), -1)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 13, 40])
+def test_cls_forward_matches_dense_brute_force(N):
+    q, k, v, do, F, masks = _cls_case(N, seed=N)
+    o, lse = oracle.forward(q, k, v, F, cls=True)
+    o2, lse2, P = oracle.dense_forward(q, k, v, masks)
+    assert np.isfinite(lse).all()           # every row sees at least key 0
+    np.testing.assert_allclose(o, o2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse2, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 13, 40])
+def test_cls_backward_matches_dense_brute_force(N):
+    q, k, v, do, F, masks = _cls_case(N, seed=100 + N)
+    g = oracle.backward(q, k, v, do, F, cls=True)
+    g2 = oracle.dense_backward(q, k, v, do, masks)
+    for x, y in zip(g, g2):
+        np.testing.assert_allclose(x, y, atol=1e-12, rtol=0)
+
+
+def test_cls_matches_torch_autograd_fp64():
+    N = 29
+    q, k, v, do, F, masks = _cls_case(N, d=16, seed=41)
+    tq, tk, tv, out, lse_t = _torch_masked_attention(q, k, v, masks)
+    out.backward(torch.from_numpy(do))
+    o, lse = oracle.forward(q, k, v, F, cls=True)
+    dq, dk, dv = oracle.backward(q, k, v, do, F, cls=True)
+    np.testing.assert_allclose(o, out.detach().numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_t.detach().numpy(), atol=1e-12, rtol=0)
+    for x, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(x, t.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def test_cls_with_every_distance_is_plain_attention():
+    # Fib(0, 1) = 0, 1, 1, 2, 3, 5, 8, ...: with N = 4 every distance 0..3 is
+    # a term, so both masks are all ones and the result is dense softmax
+    # attention (torch's scaled_dot_product_attention without a mask).
+    N = 4
+    q, k, v, do = (_rand((2, 1, N, 8), 60 + t) for t in range(4))
+    F = [oracle.fib_offsets(0, 1, N, N)]
+    assert F == [[0, 1, 2, 3]]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v))).numpy()
+    for cls in (False, True):
+        o, _ = oracle.forward(q, k, v, F, cls=cls)
+        np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
+    for x, y in zip(oracle.backward(q, k, v, do, F, cls=True), oracle.backward(q, k, v, do, F)):
+        np.testing.assert_allclose(x, y, atol=1e-12, rtol=0)
+
+
+def test_cls_special_rows():
+    # Offsets {4} at N = 5: rows 1..3 have no Fibonacci key, so under the
+    # class-token mask each sees key 0 only (O = V_0, LSE = its one score).
+    N, d = 5, 8
+    q, k, v = (_rand((1, 1, N, d), s) for s in (71, 72, 73))
+    o, lse = oracle.forward(q, k, v, [[4]], cls=True)
+    for j in (1, 2, 3):
+        assert np.array_equal(o[0, 0, j], v[0, 0, 0])
+        assert lse[0, 0, j] == pytest.approx(q[0, 0, j] @ k[0, 0, 0] / math.sqrt(d), abs=1e-14)
+    # row 4 sees key 0 once (4 is an offset), row 0 sees every key
+    s = q[0, 0, 0] @ k[0, 0].T / math.sqrt(d)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    np.testing.assert_allclose(o[0, 0, 0], p @ v[0, 0], atol=1e-14)
+    # one token: the class token attends itself
+    o, lse = oracle.forward(q[:, :, :1], k[:, :, :1], v[:, :, :1], [[]], cls=True)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+
+
+@pytest.mark.parametrize("N", [1, 2, 7, 60, 197])
+def test_cls_pair_count_closed_form(N):
+    # |Omega_cls| = |Omega| + 2 (N - 1 - |F n [1, N-1]|) + [0 not in F]
+    for F in ([], [0], [1, 2, 3, 5, 8], [0, 2, 4, 6, 10], [4, 7, 11, 18, 29]):
+        F = [f for f in F if f <= N - 1]
+        base = oracle.support_mask(N, F).sum()
+        pos = len([f for f in F if f >= 1])
+        want = base + 2 * (N - 1 - pos) + (0 not in F)
+        assert oracle.cls_support_mask(N, F).sum() == want

@@ -107,3 +107,33 @@ def test_window_overshoot_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "fib_offsets", overshoot)
     _expect_pin_failure(pins.test_offsets_brute_force_membership, 300, 20, "small")
+
+
+def test_cls_missing_column_is_caught(monkeypatch):
+    # class-token mask without its column: rows j >= 1 never gain key 0
+    monkeypatch.setattr(fo, "_cls_extra_rows", lambda n, offs: np.zeros(n, dtype=bool))
+    _expect_pin_failure(pins.test_cls_forward_matches_dense_brute_force, 13)
+
+
+def test_cls_key0_counted_twice_is_caught(monkeypatch):
+    # every row j >= 1 gains key 0, also when j is already an offset
+    monkeypatch.setattr(fo, "_cls_extra_rows", lambda n, offs: np.arange(n) >= 1)
+    _expect_pin_failure(pins.test_cls_forward_matches_dense_brute_force, 13)
+
+
+def test_cls_row0_counted_twice_is_caught(monkeypatch):
+    # the dense class-token row added on top of row 0's own Fibonacci keys in
+    # the backward (row 0's offset scores not masked out first)
+    src = fo.backward
+
+    def bad_backward(q, k, v, do, offs, cls=False):
+        dq, dk, dv = src(q, k, v, do, offs, cls=cls)
+        if cls:
+            row0 = np.zeros(np.shape(q))
+            row0[:, :, 0] = 1.0
+            g0 = src(q, k, v, np.asarray(do) * row0, offs, cls=False)
+            dq, dk, dv = dq + g0[0], dk + g0[1], dv + g0[2]
+        return dq, dk, dv
+
+    monkeypatch.setattr(oracle, "backward", bad_backward)
+    _expect_pin_failure(pins.test_cls_backward_matches_dense_brute_force, 13)

@@ -85,7 +85,18 @@ def measured_traffic(pass_name):
     return None
 
 
-def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0):
+def _cls_extra_pairs_per_slab(N, F):
+    """Pairs the class-token mask adds to each head's support: (0, k) and
+    (k, 0) for every k >= 1 that is not a distance, and (0, 0) when 0 is not
+    a distance."""
+    out = []
+    for fs in F:
+        pos = len([f for f in fs if f >= 1])
+        out.append(2 * (N - 1 - pos) + (0 if 0 in fs else 1))
+    return out
+
+
+def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0, cls=False):
     """The oracle (fp64 numpy), forward + backward over the whole batch,
     repeated until `budget_s` seconds of CPU time have passed."""
     import oracle  # test infrastructure; used only for this baseline leg
@@ -99,8 +110,8 @@ def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.forward(x["q"], x["k"], x["v"], F)
-        oracle.backward(x["q"], x["k"], x["v"], x["do"], F)
+        oracle.forward(x["q"], x["k"], x["v"], F, cls=cls)
+        oracle.backward(x["q"], x["k"], x["v"], x["do"], F, cls=cls)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 50:
@@ -127,6 +138,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--modified", action="store_true",
                     help="heads from README Algorithm 2's modified Wythoff pairs")
+    ap.add_argument("--cls", action="store_true",
+                    help="class-token mask (README Algorithm 2: row and column 0 dense)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 10 times "
                          "(scale reference for HBM byte counters), then exit")
@@ -158,11 +171,13 @@ def main():
     ptr, offs = fa.offsets(wl.N, a, b, w)
     F = [[int(f) for f in offs[ptr[h]:ptr[h + 1]]] for h in range(wl.H)]
     pairs_per_pass = int(wl.B * sum(_pairs_per_slab(wl.N, F)))
+    if args.cls:
+        pairs_per_pass += int(wl.B * sum(_cls_extra_pairs_per_slab(wl.N, F)))
     esize = 2 if wl.dtype == "bf16" else 4
     fwd_bytes, bwd_bytes = _bytes(wl, esize)
 
     inp = workloads.make_inputs(wl)
-    op = fa.Fibottention(wl.B, wl.H, wl.N, wl.d, wl.torch_dtype, a, b, w)
+    op = fa.Fibottention(wl.B, wl.H, wl.N, wl.d, wl.torch_dtype, a, b, w, cls=args.cls)
     R = max(2, args.sets)
     sets = []
     for _ in range(R):
@@ -172,11 +187,13 @@ def main():
         for n in ("dq", "dk", "dv"):
             s[n] = torch.empty(wl.B, wl.H, wl.N, wl.d, dtype=torch.float32, device=dev)
         s["ws"] = torch.empty(op.workspace_floats(), dtype=torch.float32, device=dev)
+        s["fws"] = torch.empty(max(op.fwd_workspace_floats(), 1), dtype=torch.float32,
+                               device=dev)
         sets.append(s)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def fwd(s):
-        op.forward(s["q"], s["k"], s["v"], s["o"], s["lse"], stream=stream)
+        op.forward(s["q"], s["k"], s["v"], s["o"], s["lse"], s["fws"], stream=stream)
 
     def bwd(s):
         op.backward(s["q"], s["k"], s["v"], s["lse"], s["do"], s["dq"], s["dk"], s["dv"],
@@ -240,6 +257,7 @@ def main():
             if args.workload == 2 else f"Fibottention attention, {wl.name}",
             "B": wl.B, "H": wl.H, "N": wl.N, "d_h": wl.d,
             "heads": "modified Wythoff pairs, rows 1..H" if args.modified else "Wythoff rows 1..H",
+            "mask": "class-token row and column dense" if args.cls else "Fibonacci support only",
             "pairs_per_pass": pairs_per_pass,
             "buffer_sets": R,
         },
@@ -248,17 +266,18 @@ def main():
         "wall_s_timed": wall,
         "kernels": kernels,
         "roofline": {
-            "kernel": f"{KERNELS[dom][0]} ({dom} pass)",
+            "kernel": f"all launches of the {dom} pass (class-token mask)" if args.cls
+            else f"{KERNELS[dom][0]} ({dom} pass)",
             "bound": "hbm",
             "achieved": ach,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(dom),
+            "traffic": None if args.cls else measured_traffic(dom),
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inp, F, pairs_per_pass)
+        line["cpu_baseline"] = cpu_baseline(wl, inp, F, pairs_per_pass, cls=args.cls)
     print(json.dumps(line), flush=True)
 
 

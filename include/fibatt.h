@@ -146,6 +146,37 @@ int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k,
                const void* v, const float* lse, const void* dout, float* dq,
                float* dk, float* dv, float* workspace, void* stream);
 
+/* Class-token variant (README Algorithm 2's mask over a class token and N
+ * patches: all ones, with the head's Fibonacci pattern among the patches).
+ * Token 0 is the class token: row 0 attends every key, every row attends
+ * key 0, and among tokens 1..N-1 the support is the head's as above (the
+ * distance between two patches is the same as between their positions).
+ * Pair (0, 0) is in the support.  Every row therefore has at least one key:
+ * LSE is finite everywhere.  Same layouts, ownership and error behaviour as
+ * fibatt_fwd / fibatt_bwd; the kernels are the general (not the bf16
+ * ViT-shape) ones plus dense row-0 and column-0 reductions over the slab,
+ * done in fixed order (bitwise reproducible).
+ *
+ * Workspace: fibatt_fwd_cls_workspace_floats(desc) fp32 elements (0 when N
+ * <= 1024, and then `workspace` may be NULL), fibatt_bwd_cls_workspace_floats
+ * (desc) for the backward (B*H*N, plus partial sums when N > 1024).  Both
+ * return -1 for an invalid descriptor.  Contents on entry are ignored. */
+int64_t fibatt_fwd_cls_workspace_floats(const fibatt_desc* desc);
+int64_t fibatt_bwd_cls_workspace_floats(const fibatt_desc* desc);
+
+/* Forward with the class-token mask.  Arguments as fibatt_fwd, plus the
+ * workspace described above. */
+int fibatt_fwd_cls(const fibatt_desc* desc, const void* q, const void* k,
+                   const void* v, void* o, float* lse, float* workspace,
+                   void* stream);
+
+/* Backward with the class-token mask: gradients of sum(O * dO) for
+ * fibatt_fwd_cls.  Arguments as fibatt_bwd (lse must come from
+ * fibatt_fwd_cls); workspace as described above. */
+int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k,
+                   const void* v, const float* lse, const void* dout, float* dq,
+                   float* dk, float* dv, float* workspace, void* stream);
+
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */
 const char* fibatt_last_error(void);

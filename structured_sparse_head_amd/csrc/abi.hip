@@ -216,6 +216,56 @@ int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k, const void
   return ok();
 }
 
+int64_t fibatt_fwd_cls_workspace_floats(const fibatt_desc* desc) {
+  fibatt::Problem p;
+  if (check_desc(desc, &p)) return -1;
+  ok();
+  return fibatt::fwd_cls_workspace_floats(p);
+}
+
+int64_t fibatt_bwd_cls_workspace_floats(const fibatt_desc* desc) {
+  fibatt::Problem p;
+  if (check_desc(desc, &p)) return -1;
+  ok();
+  return fibatt::bwd_cls_workspace_floats(p);
+}
+
+int fibatt_fwd_cls(const fibatt_desc* desc, const void* q, const void* k, const void* v, void* o,
+                   float* lse, float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
+    return rc;
+  if (fibatt::fwd_cls_workspace_floats(p) > 0 && (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const hipError_t e = fibatt::launch_fwd_cls(p, q, k, v, o, lse, workspace,
+                                              static_cast<hipStream_t>(stream), path_from_env());
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_fwd_cls launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k, const void* v,
+                   const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                   float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")) ||
+      (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const hipError_t e =
+      fibatt::launch_bwd_cls(p, q, k, v, lse, dout, dq, dk, dv, workspace,
+                             static_cast<hipStream_t>(stream), path_from_env());
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_bwd_cls launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fibatt_last_error(void) { return g_error.c_str(); }
 
 }  // extern "C"

@@ -85,6 +85,27 @@ __device__ __forceinline__ void store_f32_frag_diff(float* row, int part, const 
   }
 }
 
+// Query row j, one key kk: D_j += P dP, A += P dP K, Bv += P K.
+template <typename T, int D, int G, typename LoadK, typename LoadV>
+__device__ __forceinline__ void dq_key(int kk, float scale_log2, float lse2_j,
+                                       const uint32_t (&qf)[Geom<T, D, G>::kWPL],
+                                       const uint32_t (&dof)[Geom<T, D, G>::kWPL],
+                                       float (&acc_a)[Geom<T, D, G>::kDL],
+                                       float (&acc_b)[Geom<T, D, G>::kDL], float& d_j,
+                                       LoadK load_k, LoadV load_v) {
+  using Gm = Geom<T, D, G>;
+  using M = FragMath<T, Gm::kWPL>;
+  uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
+  load_k(kk, kf);
+  load_v(kk, vf);
+  const float s = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+  const float dp = group_sum<G>(M::dot(dof, vf));
+  const float p = fast_exp2(s - lse2_j);
+  const float pdp = p * dp;
+  d_j += pdp;
+  M::axpy2(acc_a, pdp, acc_b, p, kf);
+}
+
 // Query row j: accumulates A = sum P dP K and Bv = sum P K; returns D_j.
 template <typename T, int D, int G, typename LoadK, typename LoadV>
 __device__ __forceinline__ float dq_row(int j, int N, const int* deltas, int nd, float scale_log2,
@@ -93,23 +114,35 @@ __device__ __forceinline__ float dq_row(int j, int N, const int* deltas, int nd,
                                         float (&acc_a)[Geom<T, D, G>::kDL],
                                         float (&acc_b)[Geom<T, D, G>::kDL], LoadK load_k,
                                         LoadV load_v) {
-  using Gm = Geom<T, D, G>;
-  using M = FragMath<T, Gm::kWPL>;
   float d_j = 0.f;
   for (int i = 0; i < nd; ++i) {
     const int kk = j + deltas[i];
     if (kk < 0 || kk >= N) continue;
-    uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-    load_k(kk, kf);
-    load_v(kk, vf);
-    const float s = group_sum<G>(M::dot(qf, kf)) * scale_log2;
-    const float dp = group_sum<G>(M::dot(dof, vf));
-    const float p = fast_exp2(s - lse2_j);
-    const float pdp = p * dp;
-    d_j += pdp;
-    M::axpy2(acc_a, pdp, acc_b, p, kf);
+    dq_key<T, D, G>(kk, scale_log2, lse2_j, qf, dof, acc_a, acc_b, d_j, load_k, load_v);
   }
   return d_j;
+}
+
+// Key row kr, one query jj: dV += P dO_jj, dK += P (dP - D_jj) Q_jj.
+template <typename T, int D, int G, typename LoadQ, typename LoadDO, typename LoadRow>
+__device__ __forceinline__ void dkdv_query(int jj, float scale_log2,
+                                           const uint32_t (&kf)[Geom<T, D, G>::kWPL],
+                                           const uint32_t (&vf)[Geom<T, D, G>::kWPL],
+                                           float (&dk)[Geom<T, D, G>::kDL],
+                                           float (&dv)[Geom<T, D, G>::kDL], LoadQ load_q,
+                                           LoadDO load_do, LoadRow load_row) {
+  using Gm = Geom<T, D, G>;
+  using M = FragMath<T, Gm::kWPL>;
+  uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
+  load_q(jj, qf);
+  load_do(jj, dof);
+  float lse2_j, d_j;
+  load_row(jj, lse2_j, d_j);
+  const float s = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+  const float dp = group_sum<G>(M::dot(dof, vf));
+  const float p = fast_exp2(s - lse2_j);
+  M::axpy(dv, p, dof);
+  M::axpy(dk, p * (dp - d_j), qf);
 }
 
 // Key row kr: dK and dV over the queries kr + delta.
@@ -121,25 +154,18 @@ __device__ __forceinline__ void dkdv_row(int kr, int N, const int* deltas, int n
                                          float (&dk)[Geom<T, D, G>::kDL],
                                          float (&dv)[Geom<T, D, G>::kDL], LoadQ load_q,
                                          LoadDO load_do, LoadRow load_row) {
-  using Gm = Geom<T, D, G>;
-  using M = FragMath<T, Gm::kWPL>;
   for (int i = 0; i < nd; ++i) {
     const int jj = kr + deltas[i];
     if (jj < 0 || jj >= N) continue;
-    uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-    load_q(jj, qf);
-    load_do(jj, dof);
-    float lse2_j, d_j;
-    load_row(jj, lse2_j, d_j);
-    const float s = group_sum<G>(M::dot(qf, kf)) * scale_log2;
-    const float dp = group_sum<G>(M::dot(dof, vf));
-    const float p = fast_exp2(s - lse2_j);
-    M::axpy(dv, p, dof);
-    M::axpy(dk, p * (dp - d_j), qf);
+    dkdv_query<T, D, G>(jj, scale_log2, kf, vf, dk, dv, load_q, load_do, load_row);
   }
 }
 
-template <typename T, int D, int G, int NT, int MH>
+// CLS: class-token mask.  Row 0's dQ and D_0 come from the dense
+// class-token kernel (D_0 through the workspace), key 0's dK and dV from the
+// dense column kernel, which reads every D_j from the workspace; a row j >= 1
+// whose distance to token 0 is not a head distance also pairs with token 0.
+template <typename T, int D, int G, int NT, int MH, bool CLS>
 __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -166,21 +192,31 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
 
   // Query-centric pass: D_j and dQ_j.
   for (int j = tid / G; j < N; j += NT / G) {
+    const float lse2_j = a.lse[slab * N + j] * kLog2e;
+    if (CLS && j == 0) {
+      if (part == 0) {
+        s_d[0] = a.ws[slab * N];
+        s_lse2[0] = lse2_j;
+      }
+      continue;
+    }
     const size_t roff = base + static_cast<size_t>(j) * Gm::kRowBytes;
     uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
     frag_load_cached<T, D, G>(a.q + roff, part, qf);
     frag_load_cached<T, D, G>(a.dout + roff, part, dof);
-    const float lse2_j = a.lse[slab * N + j] * kLog2e;
     float acc_a[Gm::kDL], acc_b[Gm::kDL];
     zero_acc(acc_a);
     zero_acc(acc_b);
-    const float d_j = dq_row<T, D, G>(
-        j, N, s_deltas, nd, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b,
-        [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_a, r, part, f); },
-        [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_b, r, part, f); });
+    auto lk = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_a, r, part, f); };
+    auto lv = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_b, r, part, f); };
+    float d_j =
+        dq_row<T, D, G>(j, N, s_deltas, nd, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, lk, lv);
+    if (CLS && !has_delta(s_deltas, nd, j))
+      dq_key<T, D, G>(0, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, d_j, lk, lv);
     if (part == 0) {
       s_d[j] = d_j;
       s_lse2[j] = lse2_j;
+      if (CLS) a.ws[slab * N + j] = d_j;
     }
     store_f32_frag_diff<Gm::kDL>(a.dq + fbase + static_cast<size_t>(j) * D, part, acc_a, d_j,
                                  acc_b, a.scale);
@@ -192,6 +228,7 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   stage_rows_lds<T, D, NT, true>(lds_b, a.dout + base, N, tid);
   __syncthreads();
   for (int kr = tid / G; kr < N; kr += NT / G) {
+    if (CLS && kr == 0) continue;
     const size_t roff = base + static_cast<size_t>(kr) * Gm::kRowBytes;
     uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
     frag_load_cached<T, D, G>(a.k + roff, part, kf);
@@ -199,21 +236,22 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
     float dk[Gm::kDL], dv[Gm::kDL];
     zero_acc(dk);
     zero_acc(dv);
-    dkdv_row<T, D, G>(
-        kr, N, s_deltas, nd, a.scale_log2, kf, vf, dk, dv,
-        [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_a, r, part, f); },
-        [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_b, r, part, f); },
-        [&](int r, float& l2, float& dd) {
-          l2 = s_lse2[r];
-          dd = s_d[r];
-        });
+    auto lq = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_a, r, part, f); };
+    auto ldo = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_lds<T, D, G>(lds_b, r, part, f); };
+    auto lrow = [&](int r, float& l2, float& dd) {
+      l2 = s_lse2[r];
+      dd = s_d[r];
+    };
+    dkdv_row<T, D, G>(kr, N, s_deltas, nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
+    if (CLS && !has_delta(s_deltas, nd, kr))
+      dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
     store_f32_frag<Gm::kDL>(a.dk + fbase + static_cast<size_t>(kr) * D, part, dk, a.scale);
     store_f32_frag<Gm::kDL>(a.dv + fbase + static_cast<size_t>(kr) * D, part, dv, 1.0f);
   }
 }
 
 // Stream variant, query launch: dQ and D for a tile of query rows.
-template <typename T, int D, int G, int NT, int MH>
+template <typename T, int D, int G, int NT, int MH, bool CLS>
 __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
@@ -227,7 +265,7 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int j = tile * (NT / G) + tid / G;
-  if (j >= N) return;
+  if (j >= N || (CLS && j == 0)) return;
   const int part = tid % G;
   const size_t base = slab * N * Gm::kRowBytes;
   const char* ks = a.k + base;
@@ -239,20 +277,22 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   float acc_a[Gm::kDL], acc_b[Gm::kDL];
   zero_acc(acc_a);
   zero_acc(acc_b);
-  const float d_j = dq_row<T, D, G>(
-      j, N, s_deltas, s_nd, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b,
-      [&](int r, uint32_t(&f)[Gm::kWPL]) {
-        frag_load_cached<T, D, G>(ks + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-      },
-      [&](int r, uint32_t(&f)[Gm::kWPL]) {
-        frag_load_cached<T, D, G>(vs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-      });
+  auto lk = [&](int r, uint32_t(&f)[Gm::kWPL]) {
+    frag_load_cached<T, D, G>(ks + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
+  };
+  auto lv = [&](int r, uint32_t(&f)[Gm::kWPL]) {
+    frag_load_cached<T, D, G>(vs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
+  };
+  float d_j =
+      dq_row<T, D, G>(j, N, s_deltas, s_nd, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, lk, lv);
+  if (CLS && !has_delta(s_deltas, s_nd, j))
+    dq_key<T, D, G>(0, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, d_j, lk, lv);
   if (part == 0) a.ws[slab * N + j] = d_j;
   store_f32_frag_diff<Gm::kDL>(a.dq + (slab * N + j) * D, part, acc_a, d_j, acc_b, a.scale);
 }
 
 // Stream variant, key launch: dK and dV for a tile of key rows.
-template <typename T, int D, int G, int NT, int MH>
+template <typename T, int D, int G, int NT, int MH, bool CLS>
 __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
@@ -266,7 +306,7 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int kr = tile * (NT / G) + tid / G;
-  if (kr >= N) return;
+  if (kr >= N || (CLS && kr == 0)) return;
   const int part = tid % G;
   const size_t base = slab * N * Gm::kRowBytes;
   const size_t rbase = slab * N;
@@ -278,18 +318,19 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   float dk[Gm::kDL], dv[Gm::kDL];
   zero_acc(dk);
   zero_acc(dv);
-  dkdv_row<T, D, G>(
-      kr, N, s_deltas, s_nd, a.scale_log2, kf, vf, dk, dv,
-      [&](int r, uint32_t(&f)[Gm::kWPL]) {
-        frag_load_cached<T, D, G>(qs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-      },
-      [&](int r, uint32_t(&f)[Gm::kWPL]) {
-        frag_load_cached<T, D, G>(dos + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-      },
-      [&](int r, float& l2, float& dd) {
-        l2 = a.lse[rbase + r] * kLog2e;
-        dd = a.ws[rbase + r];
-      });
+  auto lq = [&](int r, uint32_t(&f)[Gm::kWPL]) {
+    frag_load_cached<T, D, G>(qs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
+  };
+  auto ldo = [&](int r, uint32_t(&f)[Gm::kWPL]) {
+    frag_load_cached<T, D, G>(dos + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
+  };
+  auto lrow = [&](int r, float& l2, float& dd) {
+    l2 = a.lse[rbase + r] * kLog2e;
+    dd = a.ws[rbase + r];
+  };
+  dkdv_row<T, D, G>(kr, N, s_deltas, s_nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
+  if (CLS && !has_delta(s_deltas, s_nd, kr))
+    dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
   store_f32_frag<Gm::kDL>(a.dk + (rbase + kr) * D, part, dk, a.scale);
   store_f32_frag<Gm::kDL>(a.dv + (rbase + kr) * D, part, dv, 1.0f);
 }
@@ -301,7 +342,7 @@ constexpr int bwd_group() {
   return (D * static_cast<int>(sizeof(T))) / 64;
 }
 
-template <typename T, int D, int MH>
+template <typename T, int D, int MH, bool CLS>
 hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const void* v,
                         const float* lse, const void* dout, float* dq, float* dk, float* dv,
                         float* ws, hipStream_t stream, Path path) {
@@ -328,7 +369,7 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes + 8 * static_cast<size_t>(p.N);
-    auto kern = bwd_slab_kernel<T, D, G, NT, MH>;
+    auto kern = bwd_slab_kernel<T, D, G, NT, MH, CLS>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         kSlabLdsBudget);
@@ -339,8 +380,8 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
     const int per = NT / G;
     a.tiles = (p.N + per - 1) / per;
     const unsigned blocks = static_cast<unsigned>(slabs * a.tiles);
-    hipLaunchKernelGGL((bwd_dq_stream_kernel<T, D, G, NT, MH>), dim3(blocks), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_stream_kernel<T, D, G, NT, MH>), dim3(blocks), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream,
                        a);
   }
   return hipGetLastError();
@@ -350,9 +391,17 @@ template <typename T, int D>
 hipError_t launch_bwd_d(const Problem& p, const void* q, const void* k, const void* v,
                         const float* lse, const void* dout, float* dq, float* dk, float* dv,
                         float* ws, hipStream_t stream, Path path) {
+  if (p.cls) {
+    if (p.H <= kSmallHeads)
+      return launch_bwd_t<T, D, kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream,
+                                                   path);
+    return launch_bwd_t<T, D, kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream,
+                                               path);
+  }
   if (p.H <= kSmallHeads)
-    return launch_bwd_t<T, D, kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
-  return launch_bwd_t<T, D, kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
+    return launch_bwd_t<T, D, kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream,
+                                                  path);
+  return launch_bwd_t<T, D, kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
 }
 
 }  // namespace
@@ -365,9 +414,9 @@ bool bwd_slab_fits(const Problem& p) {
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
                       float* ws, hipStream_t stream, Path path) {
-  if (path == Path::kAuto && bwd_slab_bf16_fits(p))
+  if (path == Path::kAuto && !p.cls && bwd_slab_bf16_fits(p))
     return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv, stream);
-  if (path == Path::kAuto && bwd_tile_bf16_fits(p))
+  if (path == Path::kAuto && !p.cls && bwd_tile_bf16_fits(p))
     return launch_bwd_tile_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
   if (p.dtype == DType::kBF16) {
     if (p.D == 64)

@@ -114,6 +114,28 @@ __device__ __forceinline__ void attend_row(const KV& kv, int j, int N, int part,
   }
 }
 
+// One more key kk for query row j (the class-token column): a single online
+// softmax step.
+template <typename T, int D, int G, typename KV>
+__device__ __forceinline__ void attend_key(const KV& kv, int kk, int part, float scale_log2,
+                                           const uint32_t (&qf)[Geom<T, D, G>::kWPL],
+                                           float (&acc)[Geom<T, D, G>::kDL], float& m, float& l) {
+  using Gm = Geom<T, D, G>;
+  using M = FragMath<T, Gm::kWPL>;
+  uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
+  kv.load_k(kk, part, kf);
+  kv.load_v(kk, part, vf);
+  const float s = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+  const float mn = fmaxf(m, s);
+  const float alpha = fast_exp2(m - mn);  // 0 when m = -inf
+  const float p = fast_exp2(s - mn);
+  l = __builtin_fmaf(l, alpha, p);
+#pragma unroll
+  for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
+  M::axpy(acc, p, vf);
+  m = mn;
+}
+
 // Normalise and write O (in T) and LSE (natural log) for row j.
 template <typename T, int D, int G, typename Args>
 __device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, int part,
@@ -143,7 +165,10 @@ __device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, in
   if (part == 0) a.lse[slab * a.N + j] = has ? (m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D, int G, int NT, int C, int MH>
+// CLS: class-token mask.  Row 0 is left to the dense class-token kernel;
+// a row j >= 1 whose distance j to token 0 is not a head distance also
+// attends key 0.
+template <typename T, int D, int G, int NT, int C, int MH, bool CLS>
 __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -165,6 +190,7 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   const int part = tid % G;
   const LdsKV<T, D, G> kv{lds_k, lds_v};
   for (int j = tid / G; j < N; j += NT / G) {
+    if (CLS && j == 0) continue;
     uint32_t qf[Gm::kWPL];
     frag_load_global<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
     float acc[Gm::kDL];
@@ -172,11 +198,13 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
     for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
     float m = -INFINITY, l = 0.f;
     attend_row<T, D, G, C>(kv, j, N, part, s_deltas, nd, a.scale_log2, qf, acc, m, l);
+    if (CLS && !has_delta(s_deltas, nd, j))
+      attend_key<T, D, G>(kv, 0, part, a.scale_log2, qf, acc, m, l);
     finish_row<T, D, G>(a, slab, j, part, acc, m, l);
   }
 }
 
-template <typename T, int D, int G, int NT, int C, int MH>
+template <typename T, int D, int G, int NT, int C, int MH, bool CLS>
 __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   using Gm = Geom<T, D, G>;
   __shared__ int s_deltas[kMaxSigned];
@@ -190,7 +218,7 @@ __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int j = tile * (NT / G) + tid / G;
-  if (j >= N) return;
+  if (j >= N || (CLS && j == 0)) return;
   const int part = tid % G;
   const size_t base = slab * N * Gm::kRowBytes;
   const GlobalKV<T, D, G> kv{a.k + base, a.v + base};
@@ -201,6 +229,8 @@ __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
   float m = -INFINITY, l = 0.f;
   attend_row<T, D, G, C>(kv, j, N, part, s_deltas, s_nd, a.scale_log2, qf, acc, m, l);
+  if (CLS && !has_delta(s_deltas, s_nd, j))
+    attend_key<T, D, G>(kv, 0, part, a.scale_log2, qf, acc, m, l);
   finish_row<T, D, G>(a, slab, j, part, acc, m, l);
 }
 
@@ -210,7 +240,7 @@ constexpr int fwd_group() {
   return (D * static_cast<int>(sizeof(T))) / 128;
 }
 
-template <typename T, int D, int MH>
+template <typename T, int D, int MH, bool CLS>
 hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                         float* lse, hipStream_t stream, Path path) {
   constexpr int G = fwd_group<T, D>();
@@ -232,7 +262,7 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes;
-    auto kern = fwd_slab_kernel<T, D, G, NT, C, MH>;
+    auto kern = fwd_slab_kernel<T, D, G, NT, C, MH, CLS>;
     // Opt the kernel into the full slab budget once per process.
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -243,7 +273,7 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   } else {
     const int rows = NT / G;
     a.tiles = (p.N + rows - 1) / rows;
-    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C, MH>),
+    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C, MH, CLS>),
                        dim3(static_cast<unsigned>(slabs * a.tiles)), dim3(NT), 0, stream, a);
   }
   return hipGetLastError();
@@ -252,9 +282,14 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
 template <typename T, int D>
 hipError_t launch_fwd_d(const Problem& p, const void* q, const void* k, const void* v, void* o,
                         float* lse, hipStream_t stream, Path path) {
+  if (p.cls) {
+    if (p.H <= kSmallHeads)
+      return launch_fwd_t<T, D, kSmallHeads, true>(p, q, k, v, o, lse, stream, path);
+    return launch_fwd_t<T, D, kMaxHeads, true>(p, q, k, v, o, lse, stream, path);
+  }
   if (p.H <= kSmallHeads)
-    return launch_fwd_t<T, D, kSmallHeads>(p, q, k, v, o, lse, stream, path);
-  return launch_fwd_t<T, D, kMaxHeads>(p, q, k, v, o, lse, stream, path);
+    return launch_fwd_t<T, D, kSmallHeads, false>(p, q, k, v, o, lse, stream, path);
+  return launch_fwd_t<T, D, kMaxHeads, false>(p, q, k, v, o, lse, stream, path);
 }
 
 }  // namespace
@@ -266,9 +301,9 @@ bool fwd_slab_fits(const Problem& p) {
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, hipStream_t stream, Path path) {
-  if (path == Path::kAuto && fwd_slab_bf16_fits(p))
+  if (path == Path::kAuto && !p.cls && fwd_slab_bf16_fits(p))
     return launch_fwd_slab_bf16(p, q, k, v, o, lse, stream);
-  if (path == Path::kAuto && fwd_tile_bf16_fits(p))
+  if (path == Path::kAuto && !p.cls && fwd_tile_bf16_fits(p))
     return launch_fwd_tile_bf16(p, q, k, v, o, lse, stream);
   if (p.dtype == DType::kBF16) {
     if (p.D == 64) return launch_fwd_d<bf16_t, 64>(p, q, k, v, o, lse, stream, path);

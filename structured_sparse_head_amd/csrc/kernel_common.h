@@ -272,4 +272,11 @@ __device__ __forceinline__ void build_deltas(int32_t a, int32_t b, int32_t lim, 
   *count = c;
 }
 
+// Whether `delta` is one of the head's `count` signed displacements.
+__device__ __forceinline__ bool has_delta(const int* deltas, int count, int delta) {
+  bool found = false;
+  for (int i = 0; i < count; ++i) found |= deltas[i] == delta;
+  return found;
+}
+
 }  // namespace fibatt

@@ -14,7 +14,8 @@ enum class DType : int { kF32 = 0, kBF16 = 1 };
 struct Problem {
   int B, H, N, D;
   DType dtype;
-  HeadTable heads;  // a, b, lim = min(w, N - 1) per head
+  HeadTable heads;   // a, b, lim = min(w, N - 1) per head
+  bool cls = false;  // class-token mask: row and column 0 dense
 };
 
 // LDS bytes a workgroup may use on the slab-resident paths (two workgroups
@@ -52,6 +53,19 @@ bool bwd_tile_bf16_fits(const Problem& p);
 hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
                                 float* dv, float* ws, hipStream_t stream);
+
+// Class-token mask (row and column 0 dense): the general kernels with the
+// token-0 pairs of rows and keys 1..N-1, plus the dense row/column kernels.
+// Dense rows are reduced in ranges of kSplitRows rows per workgroup.
+constexpr int kSplitRows = 1024;
+int cls_splits(const Problem& p);
+int64_t fwd_cls_workspace_floats(const Problem& p);
+int64_t bwd_cls_workspace_floats(const Problem& p);
+hipError_t launch_fwd_cls(const Problem& p, const void* q, const void* k, const void* v,
+                          void* o, float* lse, float* ws, hipStream_t stream, Path path);
+hipError_t launch_bwd_cls(const Problem& p, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                          float* ws, hipStream_t stream, Path path);
 
 // Persistent backward for bf16, d_h = 64, N <= 201 (the default when it fits).
 bool bwd_slab_bf16_fits(const Problem& p);

@@ -23,7 +23,9 @@ F32, BF16 = 0, 1
 MAX_HEADS = 128
 
 EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fibatt_offsets",
-            "fibatt_fwd", "fibatt_bwd", "fibatt_bwd_workspace_floats", "fibatt_last_error")
+            "fibatt_fwd", "fibatt_bwd", "fibatt_bwd_workspace_floats", "fibatt_fwd_cls",
+            "fibatt_bwd_cls", "fibatt_fwd_cls_workspace_floats",
+            "fibatt_bwd_cls_workspace_floats", "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -75,6 +77,13 @@ def lib() -> ctypes.CDLL:
     L.fibatt_bwd.restype = ctypes.c_int
     L.fibatt_bwd_workspace_floats.argtypes = [ctypes.POINTER(Desc)]
     L.fibatt_bwd_workspace_floats.restype = ctypes.c_int64
+    L.fibatt_fwd_cls.argtypes = [ctypes.POINTER(Desc)] + [vp] * 7
+    L.fibatt_fwd_cls.restype = ctypes.c_int
+    L.fibatt_bwd_cls.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10
+    L.fibatt_bwd_cls.restype = ctypes.c_int
+    for name in ("fibatt_fwd_cls_workspace_floats", "fibatt_bwd_cls_workspace_floats"):
+        getattr(L, name).argtypes = [ctypes.POINTER(Desc)]
+        getattr(L, name).restype = ctypes.c_int64
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -143,15 +152,18 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 class Fibottention:
     """A fixed problem shape (B, H, N, d_h, dtype) and per-head (a, b, w).
 
+    cls=True selects the class-token mask (fibatt_fwd_cls / fibatt_bwd_cls):
+    token 0 attends, and is attended by, every token.
     Keeps the marshalled descriptor so repeated calls cost one ctypes call.
     """
 
     def __init__(self, B: int, H: int, N: int, d_h: int, dtype: torch.dtype,
-                 a: Sequence[int], b: Sequence[int], w: Sequence[int]):
+                 a: Sequence[int], b: Sequence[int], w: Sequence[int], cls: bool = False):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
         self.shape = (B, H, N, d_h)
         self.dtype = dtype
+        self.cls = bool(cls)
         self._a, self._b, self._w = _i32(a), _i32(b), _i32(w)
         if not (len(self._a) == len(self._b) == len(self._w) == H):
             raise ValueError("a, b, w must have H entries")
@@ -167,13 +179,23 @@ class Fibottention:
                 raise ValueError("tensors must be contiguous device tensors")
         return [None if t is None else t.data_ptr() for t in tensors]
 
-    def workspace_floats(self) -> int:
-        n = self._lib.fibatt_bwd_workspace_floats(self._dp)
+    def _floats(self, fn) -> int:
+        n = fn(self._dp)
         if n < 0:
             _check(E_INVAL)
         return int(n)
 
-    def forward(self, q, k, v, o=None, lse=None, stream: Optional[int] = None):
+    def workspace_floats(self) -> int:
+        """fp32 elements of the backward's workspace."""
+        fn = self._lib.fibatt_bwd_cls_workspace_floats if self.cls else \
+            self._lib.fibatt_bwd_workspace_floats
+        return self._floats(fn)
+
+    def fwd_workspace_floats(self) -> int:
+        """fp32 elements of the forward's workspace (class-token mask only)."""
+        return self._floats(self._lib.fibatt_fwd_cls_workspace_floats) if self.cls else 0
+
+    def forward(self, q, k, v, o=None, lse=None, workspace=None, stream: Optional[int] = None):
         """(o, lse).  o in the input dtype, lse fp32 [B, H, N]."""
         for t in (q, k, v):
             if tuple(t.shape) != self.shape or t.dtype != self.dtype:
@@ -182,9 +204,17 @@ class Fibottention:
             o = torch.empty_like(q)
         if lse is None:
             lse = torch.empty(self.shape[:3], dtype=torch.float32, device=q.device)
-        ptrs = self._args(q, k, v, o, lse)
-        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-        _check(self._lib.fibatt_fwd(self._dp, *ptrs, s))
+        if self.cls:
+            n = self.fwd_workspace_floats()
+            if workspace is None and n > 0:
+                workspace = torch.empty(n, dtype=torch.float32, device=q.device)
+            ptrs = self._args(q, k, v, o, lse, workspace)
+            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            _check(self._lib.fibatt_fwd_cls(self._dp, *ptrs, s))
+        else:
+            ptrs = self._args(q, k, v, o, lse)
+            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            _check(self._lib.fibatt_fwd(self._dp, *ptrs, s))
         return o, lse
 
     def backward(self, q, k, v, lse, do, dq=None, dk=None, dv=None, workspace=None,
@@ -202,29 +232,31 @@ class Fibottention:
             workspace = torch.empty(self.workspace_floats(), dtype=torch.float32, device=dev)
         ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
         s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-        _check(self._lib.fibatt_bwd(self._dp, *ptrs, s))
+        fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
+        _check(fn(self._dp, *ptrs, s))
         return dq, dk, dv
 
 
-def forward(q, k, v, a, b, w):
+def forward(q, k, v, a, b, w, cls: bool = False):
     """One-shot forward for q, k, v of shape [B, H, N, d_h] on the GPU."""
     B, H, N, d = q.shape
-    return Fibottention(B, H, N, d, q.dtype, a, b, w).forward(q, k, v)
+    return Fibottention(B, H, N, d, q.dtype, a, b, w, cls=cls).forward(q, k, v)
 
 
-def backward(q, k, v, lse, do, a, b, w):
+def backward(q, k, v, lse, do, a, b, w, cls: bool = False):
     """One-shot backward; returns fp32 (dq, dk, dv)."""
     B, H, N, d = q.shape
-    return Fibottention(B, H, N, d, q.dtype, a, b, w).backward(q, k, v, lse, do)
+    return Fibottention(B, H, N, d, q.dtype, a, b, w, cls=cls).backward(q, k, v, lse, do)
 
 
 class FibottentionFunction(torch.autograd.Function):
-    """autograd wrapper: y = Fibottention(q, k, v); gradients from fibatt_bwd."""
+    """autograd wrapper: y = Fibottention(q, k, v); gradients from fibatt_bwd
+    (or fibatt_bwd_cls with cls=True)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, a, b, w):
+    def forward(ctx, q, k, v, a, b, w, cls=False):
         B, H, N, d = q.shape
-        op = Fibottention(B, H, N, d, q.dtype, a, b, w)
+        op = Fibottention(B, H, N, d, q.dtype, a, b, w, cls=cls)
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o, lse = op.forward(q, k, v)
         ctx.op = op
@@ -235,4 +267,4 @@ class FibottentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, lse = ctx.saved_tensors
         dq, dk, dv = ctx.op.backward(q, k, v, lse, do.to(q.dtype).contiguous())
-        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None

@@ -217,3 +217,51 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(2, 3, 65, 64)
     with pytest.raises(ValueError):
         op.forward(q, q, q, o=q, lse=torch.zeros(2, 3, 65))
+
+
+# --------------------------------------------------------------------------
+# Class-token entry points: validation and workspace sizes (no launch)
+# --------------------------------------------------------------------------
+
+def _fwd_cls(desc, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD, ws=GOOD):
+    return fa.lib().fibatt_fwd_cls(ctypes.byref(desc) if desc is not None else None, q, k, v, o,
+                                   lse, ws, None)
+
+
+def _bwd_cls(desc, ptrs=None):
+    p = [GOOD] * 9 if ptrs is None else ptrs
+    return fa.lib().fibatt_bwd_cls(ctypes.byref(desc) if desc is not None else None, *p, None)
+
+
+def test_cls_entry_points_reject_bad_arguments():
+    bad = _Case(w=[65, 66, 65])
+    assert _fwd_cls(bad.desc) == fa.E_INVAL
+    assert _bwd_cls(bad.desc) == fa.E_INVAL
+    assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(bad.desc)) == -1
+    assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(bad.desc)) == -1
+    c = _Case()
+    assert _fwd_cls(None) == fa.E_INVAL
+    for i in range(5):
+        args = [GOOD] * 6
+        args[i] = None
+        assert _fwd_cls(c.desc, *args) == fa.E_INVAL
+        args[i] = GOOD + 4
+        assert _fwd_cls(c.desc, *args) == fa.E_INVAL
+    for i in range(9):
+        ptrs = [GOOD] * 9
+        ptrs[i] = None
+        assert _bwd_cls(c.desc, ptrs) == fa.E_INVAL
+    # N > 1024 needs a forward workspace; a NULL one is rejected
+    big = _Case(N=2049, w=[2049] * 3)
+    assert _fwd_cls(big.desc, ws=None) == fa.E_INVAL
+    assert b"workspace" in fa.lib().fibatt_last_error()
+
+
+def test_cls_workspace_sizes():
+    c = _Case()   # B=2, H=3, N=65, d_h=64: one range per slab
+    assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(c.desc)) == 0
+    assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(c.desc)) == 2 * 3 * 65
+    big = _Case(N=2049, w=[2049] * 3, d_h=128)   # three ranges of 1024 rows
+    assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(big.desc)) == 6 * 3 * 130
+    assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(big.desc)) == \
+        6 * 2049 + 6 * 3 * 257

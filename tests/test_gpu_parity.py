@@ -49,11 +49,11 @@ def _heads(H, N, w=None, ab=None):
     return a, b, w, F
 
 
-def _gpu_run(inp, a, b, w, with_bwd=True):
+def _gpu_run(inp, a, b, w, with_bwd=True, cls=False):
     dev = torch.device("cuda:0")
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     B, H, N, d = q.shape
-    op = fa.Fibottention(B, H, N, d, q.dtype, a, b, w)
+    op = fa.Fibottention(B, H, N, d, q.dtype, a, b, w, cls=cls)
     o, lse = op.forward(q, k, v)
     out = {"o": o, "lse": lse}
     if with_bwd:
@@ -68,7 +68,7 @@ def _f64(t):
     return t.to(torch.float64).numpy()
 
 
-def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True):
+def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True, cls=False):
     """Element-by-element comparison on the selected (batch, head) slabs."""
     sel_b = slice(None) if batches is None else list(batches)
     x = {n: _f64(inp[n])[sel_b] for n in inp}
@@ -78,14 +78,14 @@ def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True):
     g = {n: _f64(t)[sel_b] for n, t in gpu.items()}
     if heads is not None:
         g = {n: t[:, heads] for n, t in g.items()}
-    o, lse = oracle.forward(x["q"], x["k"], x["v"], F)
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], F, cls=cls)
     err = {"o": float(np.abs(g["o"] - o).max()) if o.size else 0.0}
     fin = np.isfinite(lse)
     assert np.array_equal(np.isfinite(g["lse"]), fin), "empty-row pattern of LSE differs"
     assert (g["lse"][~fin] == -np.inf).all()
     err["lse"] = float(np.abs(g["lse"][fin] - lse[fin]).max()) if fin.any() else 0.0
     if with_bwd:
-        dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], F)
+        dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], F, cls=cls)
         for n, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
             err[n] = float(np.abs(g[n] - ref).max()) if ref.size else 0.0
     _say(f"    max-abs errors: {err}")
@@ -254,3 +254,45 @@ def test_autograd_function_matches_oracle():
     assert np.abs(_f64(y.detach().cpu()) - o).max() <= 1e-4
     for t, ref in ((q, dq), (k, dk), (v, dv)):
         assert np.abs(_f64(t.grad.cpu()) - ref).max() <= 1e-4
+
+
+CLS = [
+    # (name, B, H, N, d, dtype, ab, w): class-token mask (row and column 0 dense)
+    ("fp32 N65", 2, 3, 65, 64, torch.float32, None, None),
+    ("bf16 vit N197 H12", 2, 12, 197, 64, torch.bfloat16, None, None),
+    ("bf16 d128 N300 diag windows", 1, 3, 300, 128, torch.bfloat16, ([0, 3, 5], [1, 3, 1]),
+     [300, 50, 3]),
+    ("fp32 N5 empty supports", 2, 3, 5, 64, torch.float32, None, None),
+    ("bf16 N1", 2, 3, 1, 64, torch.bfloat16, None, None),
+    ("fp32 d128 N2", 1, 3, 2, 128, torch.float32, None, None),
+    ("bf16 N2500 three ranges", 1, 3, 2500, 64, torch.bfloat16, None, None),
+    ("fp32 d128 N1100 two ranges", 1, 2, 1100, 128, torch.float32, None, None),
+]
+
+
+@pytest.mark.parametrize("case", CLS, ids=[c[0] for c in CLS])
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
+def test_cls_mask(case, path):
+    name, B, H, N, d, dtype, ab, w = case
+    if path == "slab" and 2 * N * d * (2 if dtype == torch.bfloat16 else 4) + 8 * N > 80 * 1024:
+        pytest.skip("shape exceeds the LDS slab budget; the slab variant rejects it")
+    _say(f"case: class-token mask {name} B={B} H={H} N={N} d={d} {dtype} path={path}")
+    _set_path(path)
+    try:
+        inp = workloads.random_case(4321 + N, B, H, N, d, dtype)
+        a, b, w, F = _heads(H, N, w=w, ab=ab)
+        gpu = _gpu_run(inp, a, b, w, cls=True)
+        assert torch.isfinite(gpu["lse"]).all()
+        _compare(gpu, inp, F, TOL[dtype], cls=True)
+    finally:
+        _set_path(None)
+
+
+def test_cls_backward_bitwise_deterministic():
+    _say("case: class-token mask determinism, bf16 N=2500 (three ranges), two runs")
+    inp = workloads.random_case(99, 1, 4, 2500, 64, torch.bfloat16)
+    a, b, w, F = _heads(4, 2500)
+    r1 = _gpu_run(inp, a, b, w, cls=True)
+    r2 = _gpu_run(inp, a, b, w, cls=True)
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n

@@ -7,6 +7,8 @@ neither imports nor links anything from ``structured_sparse_head_amd``.
 
 from .fibottention import (  # noqa: F401
     backward,
+    block_backward,
+    block_forward,
     cls_support_mask,
     dense_backward,
     dense_forward,

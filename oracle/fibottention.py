@@ -398,6 +398,53 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# One attention layer (README Algorithm 3): projections around the core
+# ---------------------------------------------------------------------------
+
+
+def _split_heads(t, h):
+    """[B, N, h*d] -> [B, h, N, d] (head i owns columns i*d .. (i+1)*d)."""
+    B, N, c = t.shape
+    return t.reshape(B, N, h, c // h).transpose(0, 2, 1, 3)
+
+
+def _merge_heads(t):
+    """[B, h, N, d] -> [B, N, h*d]: README Algorithm 3's concatenation Z."""
+    B, h, N, d = t.shape
+    return t.transpose(0, 2, 1, 3).reshape(B, N, h * d)
+
+
+def block_forward(x, wq, wk, wv, wz, offsets_per_head, cls=False):
+    """README Algorithm 3 over a batch.  x: [B, N, c]; wq, wk, wv: [c, h*d]
+    (head i's W_i^Q, W_i^K, W_i^V are columns i*d .. (i+1)*d); wz: [h*d, c].
+    Q_i = X W_i^Q, K_i = X W_i^K, V_i = X W_i^V; Z_i = the head's sparse
+    attention (``forward``, with its 1/sqrt(d) scale); O = concat(Z_i) W^Z."""
+    x, wq, wk, wv, wz = (np.asarray(t, dtype=np.float64) for t in (x, wq, wk, wv, wz))
+    h = len(offsets_per_head)
+    q, k, v = (_split_heads(x @ w, h) for w in (wq, wk, wv))
+    z, _ = forward(q, k, v, offsets_per_head, cls=cls)
+    return _merge_heads(z) @ wz
+
+
+def block_backward(x, wq, wk, wv, wz, dout, offsets_per_head, cls=False):
+    """Gradients of sum(O * dout) for ``block_forward`` with respect to x,
+    wq, wk, wv and wz (chain rule through the four projections)."""
+    x, wq, wk, wv, wz, dout = (np.asarray(t, dtype=np.float64)
+                               for t in (x, wq, wk, wv, wz, dout))
+    h = len(offsets_per_head)
+    q, k, v = (_split_heads(x @ w, h) for w in (wq, wk, wv))
+    z, _ = forward(q, k, v, offsets_per_head, cls=cls)
+    zc = _merge_heads(z)
+    dwz = np.einsum("bni,bnj->ij", zc, dout)
+    dz = _split_heads(dout @ wz.T, h)
+    dq, dk, dv = backward(q, k, v, dz, offsets_per_head, cls=cls)
+    dQ, dK, dV = (_merge_heads(t) for t in (dq, dk, dv))
+    dx = dQ @ wq.T + dK @ wk.T + dV @ wv.T
+    dwq, dwk, dwv = (np.einsum("bni,bnj->ij", x, t) for t in (dQ, dK, dV))
+    return dx, dwq, dwk, dwv, dwz
+
+
+# ---------------------------------------------------------------------------
 # Dense brute force (tiny N only): the definition with an explicit N x N mask
 # ---------------------------------------------------------------------------
 

@@ -463,3 +463,65 @@ def test_cls_pair_count_closed_form(N):
         pos = len([f for f in F if f >= 1])
         want = base + 2 * (N - 1 - pos) + (0 not in F)
         assert oracle.cls_support_mask(N, F).sum() == want
+
+
+# --------------------------------------------------------------------------
+# One attention layer (README Algorithm 3)
+# --------------------------------------------------------------------------
+
+def _block_case(B, N, H, dh, seed, F=None):
+    c = H * dh
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, N, c))
+    wq, wk, wv, wz = (rng.standard_normal((c, c)) / math.sqrt(c) for _ in range(4))
+    dout = rng.standard_normal((B, N, c))
+    if F is None:
+        a, b = oracle.wythoff_rows(H)
+        F = [oracle.fib_offsets(int(a[h]), int(b[h]), N, N) for h in range(H)]
+    return x, wq, wk, wv, wz, dout, F
+
+
+@pytest.mark.parametrize("cls", [False, True])
+def test_block_matches_torch_autograd_fp64(cls):
+    B, N, H, dh = 2, 23, 3, 8
+    x, wq, wk, wv, wz, dout, F = _block_case(B, N, H, dh, seed=7)
+    mk = oracle.cls_support_mask if cls else oracle.support_mask
+    masks = torch.from_numpy(np.stack([mk(N, f) for f in F]))[None]
+    t = {n: torch.from_numpy(a).requires_grad_() for n, a in
+         (("x", x), ("wq", wq), ("wk", wk), ("wv", wv), ("wz", wz))}
+
+    def heads(y):
+        return y.reshape(B, N, H, dh).permute(0, 2, 1, 3)
+
+    q, k, v = (heads(t["x"] @ t[w]) for w in ("wq", "wk", "wv"))
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous()) / math.sqrt(dh)
+    p = torch.softmax(s.masked_fill(~masks, float("-inf")), -1)
+    p = torch.where(masks.any(-1, keepdim=True), p, torch.zeros_like(p))
+    z = torch.matmul(p, v).permute(0, 2, 1, 3).reshape(B, N, H * dh)
+    out = z @ t["wz"]
+    out.backward(torch.from_numpy(dout))
+    ref = oracle.block_forward(x, wq, wk, wv, wz, F, cls=cls)
+    np.testing.assert_allclose(ref, out.detach().numpy(), atol=1e-12, rtol=0)
+    grads = oracle.block_backward(x, wq, wk, wv, wz, dout, F, cls=cls)
+    for g, n in zip(grads, ("x", "wq", "wk", "wv", "wz")):
+        np.testing.assert_allclose(g, t[n].grad.numpy(), atol=1e-11, rtol=0, err_msg=n)
+
+
+def test_block_with_every_distance_is_torch_multihead_attention():
+    # Fib(0, 1) covers every distance 0..3 at N = 4: the layer is plain
+    # multi-head attention, here torch.nn.MultiheadAttention without biases.
+    B, N, H, dh = 3, 4, 2, 8
+    c = H * dh
+    F = [oracle.fib_offsets(0, 1, N, N)] * H
+    x, wq, wk, wv, wz, dout, _ = _block_case(B, N, H, dh, seed=8, F=F)
+    mha = torch.nn.MultiheadAttention(c, H, bias=False, batch_first=True, dtype=torch.float64)
+    with torch.no_grad():
+        mha.in_proj_weight.copy_(torch.from_numpy(np.concatenate([wq.T, wk.T, wv.T])))
+        mha.out_proj.weight.copy_(torch.from_numpy(wz.T))
+    tx = torch.from_numpy(x).requires_grad_()
+    out, _ = mha(tx, tx, tx, need_weights=False)
+    out.backward(torch.from_numpy(dout))
+    np.testing.assert_allclose(oracle.block_forward(x, wq, wk, wv, wz, F),
+                               out.detach().numpy(), atol=1e-12, rtol=0)
+    dx = oracle.block_backward(x, wq, wk, wv, wz, dout, F)[0]
+    np.testing.assert_allclose(dx, tx.grad.numpy(), atol=1e-12, rtol=0)

@@ -137,3 +137,30 @@ def test_cls_row0_counted_twice_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "backward", bad_backward)
     _expect_pin_failure(pins.test_cls_backward_matches_dense_brute_force, 13)
+
+
+def test_block_head_split_interleaved_is_caught(monkeypatch):
+    # heads taken as interleaved columns (column c -> head c mod h) instead of
+    # contiguous blocks of d columns
+    def interleaved(t, h):
+        B, N, c = t.shape
+        return t.reshape(B, N, c // h, h).transpose(0, 3, 1, 2)
+
+    def merge(t):
+        B, h, N, d = t.shape
+        return t.transpose(0, 2, 3, 1).reshape(B, N, h * d)
+
+    monkeypatch.setattr(fo, "_split_heads", interleaved)
+    monkeypatch.setattr(fo, "_merge_heads", merge)
+    _expect_pin_failure(pins.test_block_matches_torch_autograd_fp64, False)
+
+
+def test_block_missing_value_projection_gradient_is_caught(monkeypatch):
+    src = fo.block_backward
+
+    def bad(*args, **kw):
+        dx, dwq, dwk, dwv, dwz = src(*args, **kw)
+        return dx, dwq, dwk, np.zeros_like(dwv), dwz
+
+    monkeypatch.setattr(oracle, "block_backward", bad)
+    _expect_pin_failure(pins.test_block_matches_torch_autograd_fp64, False)

@@ -128,6 +128,91 @@ def cpu_baseline(wl, inp, F, pairs_per_pass, budget_s=10.0, cls=False):
     }
 
 
+def bench_block(args):
+    """One ViT-B/16 attention layer with Fibottention heads (README Algorithm 3):
+    QKV projection, sparse core, output projection, forward + backward through
+    autograd, B=64, N=197, c=768, h=12, bf16."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_head_amd as fa
+
+    B, N, C, H = 64, 197, 768, 12
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16
+    layer = fa.FibottentionAttention(C, H, N, modified=args.modified, cls=args.cls, device=dev,
+                                     dtype=dt)
+    layer.reset_parameters(torch.Generator().manual_seed(0))
+    rng = np.random.default_rng(2)
+    R = max(2, args.sets)
+    xs = [torch.from_numpy(rng.standard_normal((B, N, C), dtype=np.float32)).to(dev, dt)
+          .requires_grad_() for _ in range(R)]
+    gs = [torch.from_numpy(rng.standard_normal((B, N, C), dtype=np.float32)).to(dev, dt)
+          for _ in range(R)]
+
+    def step(i):
+        layer(xs[i % R]).backward(gs[i % R])
+
+    def timed(body, n):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            body(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    ms_step = timed(step, K)
+    with torch.no_grad():
+        ms_fwd = timed(lambda i: layer(xs[i % R]), K)
+        x2 = [x.detach().reshape(B * N, C) for x in xs]
+        ms_qkv = timed(lambda i: torch.mm(x2[i % R], layer.w_qkv), K)
+        ms_out = timed(lambda i: torch.mm(x2[i % R], layer.w_z), K)
+        qkv = [layer.project_qkv(x.detach()) for x in xs[:2]]
+        op = fa.Fibottention(B, H, N, C // H, dt, layer.a, layer.b, layer.w, cls=args.cls)
+        ms_core = timed(lambda i: op.forward(*qkv[i % 2]), K)
+    gemm_fwd_flops = 2 * B * N * C * 3 * C + 2 * B * N * C * C
+    gemm_tflops = gemm_fwd_flops / ((ms_qkv + ms_out) * 1e-3) / 1e12
+    line = {
+        "metric": "tokens/s through one ViT-B/16 Fibottention attention layer (fwd+bwd), 1 GPU",
+        "value": B * N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Fibottention ViT-B/16 attention layer (QKV and output projections, "
+                        "sparse core), B=64 N=197 c=768 h=12",
+            "heads": "modified Wythoff pairs, rows 1..H" if args.modified else "Wythoff rows 1..H",
+            "mask": "class-token row and column dense" if args.cls else "Fibonacci support only",
+            "buffer_sets": R,
+        },
+        "forward_us": {"layer": ms_fwd * 1e3, "qkv_projection": ms_qkv * 1e3,
+                       "sparse_core": ms_core * 1e3, "output_projection": ms_out * 1e3},
+        "roofline": {
+            "kernel": "forward projection GEMMs (torch.mm, bf16)",
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": 2500.0,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / 2500.0,
+            "traffic": None,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +225,8 @@ def main():
                     help="heads from README Algorithm 2's modified Wythoff pairs")
     ap.add_argument("--cls", action="store_true",
                     help="class-token mask (README Algorithm 2: row and column 0 dense)")
+    ap.add_argument("--block", action="store_true",
+                    help="time one ViT-B/16 attention layer (projections + sparse core) instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 10 times "
                          "(scale reference for HBM byte counters), then exit")
@@ -159,6 +246,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 10}), flush=True)
+        return
+
+    if args.block:
+        bench_block(args)
         return
 
     import workloads

@@ -27,3 +27,4 @@ from .fibatt import (  # noqa: F401
     wythoff_modified,
     wythoff_rows,
 )
+from .block import FibottentionAttention  # noqa: F401,E402

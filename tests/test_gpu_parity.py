@@ -296,3 +296,54 @@ def test_cls_backward_bitwise_deterministic():
     r2 = _gpu_run(inp, a, b, w, cls=True)
     for n in r1:
         assert torch.equal(r1[n], r2[n]), n
+
+
+BLOCK = [
+    # (name, B, N, dim, heads, dtype, cls, modified)
+    ("fp32 ViT-B dims N197", 2, 197, 768, 12, torch.float32, False, False),
+    ("bf16 ViT-B dims N197", 2, 197, 768, 12, torch.bfloat16, False, False),
+    ("bf16 class token modified", 2, 197, 768, 12, torch.bfloat16, True, True),
+    ("fp32 d128 N300", 1, 300, 512, 4, torch.float32, False, False),
+]
+# Tolerance of a whole layer, relative to the largest reference magnitude of
+# each tensor: fp32 1e-4; bf16 2e-2 (Q, K, V, Z and O are each rounded to
+# bf16, 2^-9 relative, and the score and weight-gradient sums amplify that by
+# a few units at most).
+BLOCK_TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.mark.parametrize("case", BLOCK, ids=[c[0] for c in BLOCK])
+def test_attention_layer(case):
+    name, B, N, dim, H, dtype, cls, modified = case
+    _say(f"case: attention layer {name} B={B} N={N} dim={dim} H={H} {dtype} cls={cls}")
+    dev = torch.device("cuda:0")
+    layer = fa.FibottentionAttention(dim, H, N, modified=modified, cls=cls, device=dev,
+                                     dtype=dtype)
+    rng = np.random.default_rng(500 + N)
+    wq, wk, wv, wz = (rng.standard_normal((dim, dim), dtype=np.float32) / np.sqrt(dim)
+                      for _ in range(4))
+    x = rng.standard_normal((B, N, dim), dtype=np.float32)
+    dout = rng.standard_normal((B, N, dim), dtype=np.float32)
+    with torch.no_grad():
+        layer.w_qkv.copy_(torch.from_numpy(np.concatenate([wq, wk, wv], axis=1)))
+        layer.w_z.copy_(torch.from_numpy(wz))
+    tx = torch.from_numpy(x).to(dev, dtype).requires_grad_()
+    out = layer(tx)
+    out.backward(torch.from_numpy(dout).to(dev, dtype))
+    torch.cuda.synchronize()
+    # the oracle sees exactly the rounded values the GPU saw
+    r = lambda t: t.detach().to(torch.float64).cpu().numpy()  # noqa: E731
+    wqkv = r(layer.w_qkv)
+    args = (r(tx), wqkv[:, :dim], wqkv[:, dim:2 * dim], wqkv[:, 2 * dim:], r(layer.w_z))
+    F = [oracle.fib_offsets(int(layer.a[h]), int(layer.b[h]), int(layer.w[h]), N)
+         for h in range(H)]
+    ref_out = oracle.block_forward(*args, F, cls=cls)
+    ref_g = oracle.block_backward(*args, r(torch.from_numpy(dout).to(dtype)), F, cls=cls)
+    g_qkv = r(layer.w_qkv.grad)
+    got = {"out": r(out), "dx": r(tx.grad), "dwq": g_qkv[:, :dim], "dwk": g_qkv[:, dim:2 * dim],
+           "dwv": g_qkv[:, 2 * dim:], "dwz": r(layer.w_z.grad)}
+    ref = dict(zip(("dx", "dwq", "dwk", "dwv", "dwz"), ref_g), out=ref_out)
+    rel = {n: float(np.abs(got[n] - ref[n]).max() / max(1.0, np.abs(ref[n]).max())) for n in ref}
+    _say(f"    max-abs error / max(1, max |ref|): {rel}")
+    for n, e in rel.items():
+        assert e <= BLOCK_TOL[dtype], (n, e)

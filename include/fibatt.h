@@ -177,6 +177,48 @@ int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k,
                    const void* v, const float* lse, const void* dout, float* dq,
                    float* dk, float* dv, float* workspace, void* stream);
 
+/* Heads given by an explicit distance table instead of (a, b, w): any
+ * symmetric dilation set, e.g. the constant-factor (c n) and exponential
+ * dilation sequences that the Fibottention paper's method section sets its
+ * Fibonacci sequences against (support set of a general sequence (f_n) and
+ * window w), or a table from fibatt_offsets edited by hand.  Query
+ * j attends key k iff |j - k| is one of its head's distances (0 is the
+ * diagonal); everything else is as for fibatt_fwd / fibatt_bwd (or, with
+ * cls = 1, as for fibatt_fwd_cls / fibatt_bwd_cls).
+ *  head_ptr    : HOST, H + 1 int32, head_ptr[0] = 0, non-decreasing; head h
+ *                owns entries head_ptr[h] .. head_ptr[h + 1] - 1, at most 64.
+ *  offs        : HOST, head_ptr[H] int32 distances, strictly ascending within
+ *                a head, each in [0, N - 1] (checked on the host).
+ *  offs_device : DEVICE copy of offs (same values, 4-byte aligned), read by
+ *                the kernels; it must stay valid until the enqueued work has
+ *                run.  The library cannot check that it equals offs.
+ * Errors: as fibatt_fwd, plus E_INVAL for a malformed table and
+ * E_UNSUPPORTED for a head with more than 64 distances. */
+typedef struct {
+  int32_t B, H, N, d_h;
+  int32_t dtype;
+  int32_t cls; /* 0: mask from the table only; 1: plus the class-token row and column */
+  const int32_t* head_ptr;
+  const int32_t* offs;
+  const int32_t* offs_device;
+} fibatt_table_desc;
+
+/* Workspace sizes (fp32 elements) for the two calls below, or -1 for an
+ * invalid descriptor: forward 0 (cls = 0) or as fibatt_fwd_cls_workspace_floats;
+ * backward B*H*N (cls = 0) or as fibatt_bwd_cls_workspace_floats. */
+int64_t fibatt_fwd_table_workspace_floats(const fibatt_table_desc* desc);
+int64_t fibatt_bwd_table_workspace_floats(const fibatt_table_desc* desc);
+
+/* Forward and backward with table heads; arguments as fibatt_fwd_cls /
+ * fibatt_bwd_cls (the forward workspace may be NULL when its size is 0). */
+int fibatt_fwd_table(const fibatt_table_desc* desc, const void* q,
+                     const void* k, const void* v, void* o, float* lse,
+                     float* workspace, void* stream);
+int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q,
+                     const void* k, const void* v, const float* lse,
+                     const void* dout, float* dq, float* dk, float* dv,
+                     float* workspace, void* stream);
+
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */
 const char* fibatt_last_error(void);

@@ -18,6 +18,7 @@ from .fibatt import (  # noqa: F401
     FibattError,
     Fibottention,
     FibottentionFunction,
+    FibottentionTable,
     backward,
     forward,
     lib,

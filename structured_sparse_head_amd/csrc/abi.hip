@@ -58,36 +58,84 @@ int check_heads(int32_t H, int32_t N, const int32_t* a, const int32_t* b, const 
   return FIBATT_OK;
 }
 
-int check_desc(const fibatt_desc* d, fibatt::Problem* p) {
-  if (!d) return fail(FIBATT_E_INVAL, "desc is NULL");
-  if (d->B < 1 || d->H < 1 || d->N < 1)
-    return fail(FIBATT_E_INVAL, "B, H, N must be >= 1 (got %d, %d, %d)", d->B, d->H, d->N);
-  if (d->d_h != 64 && d->d_h != 128)
-    return fail(FIBATT_E_UNSUPPORTED, "d_h = %d: supported head widths are 64 and 128", d->d_h);
-  if (d->dtype != FIBATT_F32 && d->dtype != FIBATT_BF16)
+// Shape and type checks shared by both descriptor kinds; fills p's sizes.
+int check_shape(int32_t B, int32_t H, int32_t N, int32_t d_h, int32_t dtype, fibatt::Problem* p) {
+  if (B < 1 || H < 1 || N < 1)
+    return fail(FIBATT_E_INVAL, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (d_h != 64 && d_h != 128)
+    return fail(FIBATT_E_UNSUPPORTED, "d_h = %d: supported head widths are 64 and 128", d_h);
+  if (dtype != FIBATT_F32 && dtype != FIBATT_BF16)
     return fail(FIBATT_E_UNSUPPORTED, "dtype %d: supported are FIBATT_F32 and FIBATT_BF16",
-                d->dtype);
-  if (d->H > FIBATT_MAX_HEADS)
-    return fail(FIBATT_E_UNSUPPORTED, "H = %d exceeds FIBATT_MAX_HEADS = %d", d->H,
+                dtype);
+  if (H > FIBATT_MAX_HEADS)
+    return fail(FIBATT_E_UNSUPPORTED, "H = %d exceeds FIBATT_MAX_HEADS = %d", H,
                 FIBATT_MAX_HEADS);
-  const int64_t slabs = static_cast<int64_t>(d->B) * d->H;
+  const int64_t slabs = static_cast<int64_t>(B) * H;
   // Kernel grids are 1-D with at most 2^31 - 1 workgroups (the smallest row
   // tile is 32 rows, and the streaming backward launches two tiles per
   // tile); element offsets are computed in 64-bit.
-  if (slabs * ((d->N + 31) / 32) * 2 > 0x7fffffffll)
+  if (slabs * ((N + 31) / 32) * 2 > 0x7fffffffll)
     return fail(FIBATT_E_UNSUPPORTED, "B*H*N too large for one launch");
-  int rc = check_heads(d->H, d->N, d->a, d->b, d->w);
+  p->B = B;
+  p->H = H;
+  p->N = N;
+  p->D = d_h;
+  p->dtype = dtype == FIBATT_BF16 ? fibatt::DType::kBF16 : fibatt::DType::kF32;
+  return FIBATT_OK;
+}
+
+int check_desc(const fibatt_desc* d, fibatt::Problem* p) {
+  if (!d) return fail(FIBATT_E_INVAL, "desc is NULL");
+  int rc = check_shape(d->B, d->H, d->N, d->d_h, d->dtype, p);
   if (rc) return rc;
-  p->B = d->B;
-  p->H = d->H;
-  p->N = d->N;
-  p->D = d->d_h;
-  p->dtype = d->dtype == FIBATT_BF16 ? fibatt::DType::kBF16 : fibatt::DType::kF32;
+  rc = check_heads(d->H, d->N, d->a, d->b, d->w);
+  if (rc) return rc;
+  p->heads.table = nullptr;
+  p->host_table = nullptr;
   for (int h = 0; h < d->H; ++h) {
     p->heads.a[h] = d->a[h];
     p->heads.b[h] = d->b[h];
     p->heads.lim[h] = (d->w[h] < d->N - 1) ? d->w[h] : d->N - 1;
   }
+  return FIBATT_OK;
+}
+
+int check_table_desc(const fibatt_table_desc* d, fibatt::Problem* p) {
+  if (!d) return fail(FIBATT_E_INVAL, "desc is NULL");
+  int rc = check_shape(d->B, d->H, d->N, d->d_h, d->dtype, p);
+  if (rc) return rc;
+  if (d->cls != 0 && d->cls != 1) return fail(FIBATT_E_INVAL, "cls must be 0 or 1");
+  if (!d->head_ptr) return fail(FIBATT_E_INVAL, "head_ptr is NULL");
+  if (d->head_ptr[0] != 0) return fail(FIBATT_E_INVAL, "head_ptr[0] must be 0");
+  for (int h = 0; h < d->H; ++h) {
+    const int32_t n = d->head_ptr[h + 1] - d->head_ptr[h];
+    if (d->head_ptr[h + 1] < d->head_ptr[h])
+      return fail(FIBATT_E_INVAL, "head_ptr must be non-decreasing (head %d)", h);
+    if (n > fibatt::kMaxOffsets)
+      return fail(FIBATT_E_UNSUPPORTED, "head %d has %d distances; at most %d are supported", h,
+                  n, fibatt::kMaxOffsets);
+  }
+  const int32_t total = d->head_ptr[d->H];
+  if (total > 0 && (!d->offs || !d->offs_device))
+    return fail(FIBATT_E_INVAL, "offs and offs_device must be non-NULL");
+  if (total > 0 && (reinterpret_cast<uintptr_t>(d->offs_device) & 3u))
+    return fail(FIBATT_E_INVAL, "offs_device is not 4-byte aligned");
+  for (int h = 0; h < d->H; ++h) {
+    for (int32_t i = d->head_ptr[h]; i < d->head_ptr[h + 1]; ++i) {
+      const int32_t f = d->offs[i];
+      if (f < 0 || f >= d->N)
+        return fail(FIBATT_E_INVAL, "head %d: distance %d outside [0, N - 1 = %d]", h, f,
+                    d->N - 1);
+      if (i > d->head_ptr[h] && f <= d->offs[i - 1])
+        return fail(FIBATT_E_INVAL, "head %d: distances must be strictly ascending", h);
+    }
+    p->heads.a[h] = d->head_ptr[h];
+    p->heads.b[h] = d->head_ptr[h + 1] - d->head_ptr[h];
+    p->heads.lim[h] = d->N - 1;
+  }
+  p->heads.table = d->offs_device;
+  p->host_table = d->offs;
+  p->cls = d->cls != 0;
   return FIBATT_OK;
 }
 
@@ -263,6 +311,60 @@ int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k, const 
                              static_cast<hipStream_t>(stream), path_from_env());
   if (e != hipSuccess)
     return fail(FIBATT_E_HIP, "fibatt_bwd_cls launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t fibatt_fwd_table_workspace_floats(const fibatt_table_desc* desc) {
+  fibatt::Problem p;
+  if (check_table_desc(desc, &p)) return -1;
+  ok();
+  return p.cls ? fibatt::fwd_cls_workspace_floats(p) : 0;
+}
+
+int64_t fibatt_bwd_table_workspace_floats(const fibatt_table_desc* desc) {
+  fibatt::Problem p;
+  if (check_table_desc(desc, &p)) return -1;
+  ok();
+  return p.cls ? fibatt::bwd_cls_workspace_floats(p) : static_cast<int64_t>(p.B) * p.H * p.N;
+}
+
+int fibatt_fwd_table(const fibatt_table_desc* desc, const void* q, const void* k, const void* v,
+                     void* o, float* lse, float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_table_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
+    return rc;
+  if (p.cls && fibatt::fwd_cls_workspace_floats(p) > 0 && (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = p.cls ? fibatt::launch_fwd_cls(p, q, k, v, o, lse, workspace, s,
+                                                      path_from_env())
+                             : fibatt::launch_fwd(p, q, k, v, o, lse, s, path_from_env());
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_fwd_table launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q, const void* k, const void* v,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_table_desc(desc, &p);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")) ||
+      (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      p.cls ? fibatt::launch_bwd_cls(p, q, k, v, lse, dout, dq, dk, dv, workspace, s,
+                                     path_from_env())
+            : fibatt::launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, workspace, s, path_from_env());
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_bwd_table launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   float* s_lse2 = reinterpret_cast<float*>(smem + 2 * N * Gm::kRowBytes);
   float* s_d = s_lse2 + N;
 
-  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   stage_rows_lds<T, D, NT, false>(lds_a, a.k + base, N, tid);
   stage_rows_lds<T, D, NT, false>(lds_b, a.v + base, N, tid);
   __syncthreads();
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   const int tile = blockIdx.x % a.tiles;
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
-  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int j = tile * (NT / G) + tid / G;
   if (j >= N || (CLS && j == 0)) return;
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   const int tile = blockIdx.x % a.tiles;
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
-  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int kr = tile * (NT / G) + tid / G;
   if (kr >= N || (CLS && kr == 0)) return;

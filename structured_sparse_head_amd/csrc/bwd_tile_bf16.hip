@@ -53,10 +53,11 @@ struct BwdTileArgs {
 
 // The head's signed displacements in LDS (thread 0 builds them), padded with
 // zeros to a whole last group; returns their count after a barrier.
-__device__ __forceinline__ int stage_deltas(int32_t a, int32_t b, int32_t lim, int* dist,
+template <int MH>
+__device__ __forceinline__ int stage_deltas(const HeadTableT<MH>& ht, int h, int* dist,
                                             int* deltas, int* nd) {
   if (threadIdx.x == 0) {
-    build_deltas(a, b, lim, dist, deltas, nd);
+    build_deltas(ht, h, dist, deltas, nd);
     for (int i = 0; i < 4; ++i) deltas[*nd + i] = 0;
   }
   __syncthreads();
@@ -100,7 +101,7 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
-  const int nd = stage_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   const int N = a.N;
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
-  const int nd = stage_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   const int N = a.N;
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;

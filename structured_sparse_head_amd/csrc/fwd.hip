@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   const size_t slab = blockIdx.x;
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
-  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   const size_t base = slab * N * Gm::kRowBytes;
   char* lds_k = smem;
   char* lds_v = smem + N * Gm::kRowBytes;
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   const int tile = blockIdx.x % a.tiles;
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
-  if (tid == 0) build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+  if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   __syncthreads();
   const int j = tile * (NT / G) + tid / G;
   if (j >= N || (CLS && j == 0)) return;

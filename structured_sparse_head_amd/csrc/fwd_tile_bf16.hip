@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   const int h = slab % a.H;
   const int tid = threadIdx.x;
   if (tid == 0) {
-    build_deltas(a.ht.a[h], a.ht.b[h], a.ht.lim[h], s_dist, s_deltas, &s_nd);
+    build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
     for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;  // a whole last group
   }
   __syncthreads();

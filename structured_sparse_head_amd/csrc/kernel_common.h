@@ -21,11 +21,16 @@ constexpr int kMaxSigned = 2 * kMaxOffsets;
 // Per-head sequence parameters handed to every kernel by value.  Kernel
 // arguments are copied at every launch, so kernels are instantiated for a
 // small table (up to 16 heads, ~200 bytes) and for the full one.
+// Two modes: with `table` null, head h's distances are the terms of
+// Fib(a[h], b[h]) up to lim[h]; with `table` set (a caller-supplied device
+// array of distances), head h's distances are table[a[h] .. a[h] + b[h]),
+// ascending, each below N.
 template <int MH>
 struct HeadTableT {
   int32_t a[MH];
   int32_t b[MH];
   int32_t lim[MH];  // min(w, N - 1)
+  const int32_t* table;
 };
 using HeadTable = HeadTableT<kMaxHeads>;
 constexpr int kSmallHeads = 16;
@@ -38,6 +43,7 @@ HeadTableT<MH> shrink_heads(const HeadTable& t, int H) {
     r.b[h] = t.b[h];
     r.lim[h] = t.lim[h];
   }
+  r.table = t.table;
   return r;
 }
 
@@ -251,13 +257,20 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Signed key displacements of one head, built in LDS by thread 0 from the
-// head's (a, b, lim): -f and +f for every distance f > 0, and 0 once when it
-// is a distance.  `dist` is LDS scratch of kMaxOffsets ints.  Callers
-// synchronise before reading `deltas` / `count`.
-__device__ __forceinline__ void build_deltas(int32_t a, int32_t b, int32_t lim, int* dist,
+// Signed key displacements of head h, built in LDS by thread 0 from the
+// head's (a, b, lim) or its slice of the distance table: -f and +f for every
+// distance f > 0, and 0 once when it is a distance.  `dist` is LDS scratch of
+// kMaxOffsets ints.  Callers synchronise before reading `deltas` / `count`.
+template <int MH>
+__device__ __forceinline__ void build_deltas(const HeadTableT<MH>& ht, int h, int* dist,
                                              int* deltas, int* count) {
-  const int n = fib_offsets_gen(a, b, lim, dist, kMaxOffsets);
+  int n;
+  if (ht.table) {
+    n = ht.b[h];
+    for (int i = 0; i < n; ++i) dist[i] = ht.table[ht.a[h] + i];
+  } else {
+    n = fib_offsets_gen(ht.a[h], ht.b[h], ht.lim[h], dist, kMaxOffsets);
+  }
   const int m = n < kMaxOffsets ? n : kMaxOffsets;
   int c = 0;
   for (int i = 0; i < m; ++i) {

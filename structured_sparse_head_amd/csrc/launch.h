@@ -14,9 +14,22 @@ enum class DType : int { kF32 = 0, kBF16 = 1 };
 struct Problem {
   int B, H, N, D;
   DType dtype;
-  HeadTable heads;   // a, b, lim = min(w, N - 1) per head
+  // Fibonacci heads: a, b, lim = min(w, N - 1).  Distance-table heads:
+  // a = first index, b = count, heads.table = the device copy of the table.
+  HeadTable heads;
+  const int32_t* host_table = nullptr;  // host copy of the table, or null
   bool cls = false;  // class-token mask: row and column 0 dense
 };
+
+// Ascending distances of head h (at most kMaxOffsets are written).
+inline int head_distances(const Problem& p, int h, int32_t* out) {
+  if (p.host_table) {
+    const int n = p.heads.b[h];
+    for (int i = 0; i < n && i < kMaxOffsets; ++i) out[i] = p.host_table[p.heads.a[h] + i];
+    return n;
+  }
+  return fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], out, kMaxOffsets);
+}
 
 // LDS bytes a workgroup may use on the slab-resident paths (two workgroups
 // per CU fit in gfx950's 160 KiB).

@@ -187,7 +187,7 @@ inline bool pack_records(const Problem& p, u32x4* rec, int MH) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (h < p.H) {
       int32_t dist[kMaxOffsets];
-      const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], dist, kMaxOffsets);
+      const int n = head_distances(p, h, dist);
       if (n > kMaxOffsets) return false;
       int c = 0;
       bool has0 = false;

@@ -140,7 +140,7 @@ inline int max_signed(const Problem& p) {
   int best = 0;
   for (int h = 0; h < p.H; ++h) {
     int32_t dist[kMaxOffsets];
-    const int n = fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], dist, kMaxOffsets);
+    const int n = head_distances(p, h, dist);
     int c = 0;
     for (int i = 0; i < (n < kMaxOffsets ? n : kMaxOffsets); ++i) c += dist[i] == 0 ? 1 : 2;
     best = c > best ? c : best;

@@ -25,7 +25,9 @@ MAX_HEADS = 128
 EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fibatt_offsets",
             "fibatt_fwd", "fibatt_bwd", "fibatt_bwd_workspace_floats", "fibatt_fwd_cls",
             "fibatt_bwd_cls", "fibatt_fwd_cls_workspace_floats",
-            "fibatt_bwd_cls_workspace_floats", "fibatt_last_error")
+            "fibatt_bwd_cls_workspace_floats", "fibatt_fwd_table", "fibatt_bwd_table",
+            "fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats",
+            "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -45,6 +47,20 @@ class Desc(ctypes.Structure):
         ("a", ctypes.POINTER(ctypes.c_int32)),
         ("b", ctypes.POINTER(ctypes.c_int32)),
         ("w", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class TableDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("d_h", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("cls", ctypes.c_int32),
+        ("head_ptr", ctypes.POINTER(ctypes.c_int32)),
+        ("offs", ctypes.POINTER(ctypes.c_int32)),
+        ("offs_device", ctypes.c_void_p),
     ]
 
 
@@ -83,6 +99,13 @@ def lib() -> ctypes.CDLL:
     L.fibatt_bwd_cls.restype = ctypes.c_int
     for name in ("fibatt_fwd_cls_workspace_floats", "fibatt_bwd_cls_workspace_floats"):
         getattr(L, name).argtypes = [ctypes.POINTER(Desc)]
+        getattr(L, name).restype = ctypes.c_int64
+    L.fibatt_fwd_table.argtypes = [ctypes.POINTER(TableDesc)] + [vp] * 7
+    L.fibatt_fwd_table.restype = ctypes.c_int
+    L.fibatt_bwd_table.argtypes = [ctypes.POINTER(TableDesc)] + [vp] * 10
+    L.fibatt_bwd_table.restype = ctypes.c_int
+    for name in ("fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats"):
+        getattr(L, name).argtypes = [ctypes.POINTER(TableDesc)]
         getattr(L, name).restype = ctypes.c_int64
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
@@ -234,6 +257,63 @@ class Fibottention:
         s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
         fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
         _check(fn(self._dp, *ptrs, s))
+        return dq, dk, dv
+
+
+class FibottentionTable:
+    """Heads given by an explicit distance table (fibatt_fwd_table /
+    fibatt_bwd_table): head h attends the distances offs[head_ptr[h] ..
+    head_ptr[h+1]).  The table is copied to the device once, here."""
+
+    def __init__(self, B: int, H: int, N: int, d_h: int, dtype: torch.dtype, head_ptr, offs,
+                 cls: bool = False, device=None):
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.shape = (B, H, N, d_h)
+        self.dtype = dtype
+        self._ptr, self._offs = _i32(head_ptr), _i32(offs)
+        if len(self._ptr) != H + 1:
+            raise ValueError("head_ptr must have H + 1 entries")
+        dev = torch.device("cuda:0") if device is None else torch.device(device)
+        # one padding entry keeps the device copy non-empty
+        self._offs_dev = torch.from_numpy(
+            np.concatenate([self._offs, np.zeros(1, dtype=np.int32)])).to(dev)
+        assert self._offs_dev.dtype == torch.int32
+        self.desc = TableDesc(B, H, N, d_h, _DTYPES[dtype], int(bool(cls)), _ptr(self._ptr),
+                              _ptr(self._offs), self._offs_dev.data_ptr())
+        self._dp = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    _args = Fibottention._args
+
+    def _floats(self, fn) -> int:
+        n = fn(self._dp)
+        if n < 0:
+            _check(E_INVAL)
+        return int(n)
+
+    def forward(self, q, k, v, o=None, lse=None, workspace=None, stream: Optional[int] = None):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(self.shape[:3], dtype=torch.float32, device=q.device)
+        n = self._floats(self._lib.fibatt_fwd_table_workspace_floats)
+        if workspace is None and n > 0:
+            workspace = torch.empty(n, dtype=torch.float32, device=q.device)
+        ptrs = self._args(q, k, v, o, lse, workspace)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        _check(self._lib.fibatt_fwd_table(self._dp, *ptrs, s))
+        return o, lse
+
+    def backward(self, q, k, v, lse, do, workspace=None, stream: Optional[int] = None):
+        dev = q.device
+        dq, dk, dv = (torch.empty(self.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        if workspace is None:
+            n = self._floats(self._lib.fibatt_bwd_table_workspace_floats)
+            workspace = torch.empty(n, dtype=torch.float32, device=dev)
+        ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
+        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        _check(self._lib.fibatt_bwd_table(self._dp, *ptrs, s))
         return dq, dk, dv
 
 

@@ -265,3 +265,50 @@ def test_cls_workspace_sizes():
     assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(big.desc)) == 6 * 3 * 130
     assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(big.desc)) == \
         6 * 2049 + 6 * 3 * 257
+
+
+# --------------------------------------------------------------------------
+# Distance-table heads: validation and workspace sizes (no launch)
+# --------------------------------------------------------------------------
+
+def _tdesc(ptr, offs, B=2, H=None, N=65, d_h=64, dtype=fa.BF16, cls=0, dev=GOOD):
+    ptr, offs = fb._i32(ptr), fb._i32(offs)
+    H = len(ptr) - 1 if H is None else H
+    d = fb.TableDesc(B, H, N, d_h, dtype, cls, fb._ptr(ptr), fb._ptr(offs), dev)
+    d._keep = (ptr, offs)
+    return d
+
+
+def _fwd_t(d, ws=GOOD):
+    return fa.lib().fibatt_fwd_table(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, ws, None)
+
+
+def test_table_validation():
+    L = fa.lib()
+    good = _tdesc([0, 3, 3, 5], [1, 2, 4, 0, 7])
+    assert L.fibatt_bwd_table_workspace_floats(ctypes.byref(good)) == 2 * 3 * 65
+    assert L.fibatt_fwd_table_workspace_floats(ctypes.byref(good)) == 0
+    cases = [
+        (_tdesc([1, 3], [1, 2, 3]), fa.E_INVAL, b"head_ptr[0]"),
+        (_tdesc([0, 3, 2], [1, 2, 3]), fa.E_INVAL, b"non-decreasing"),
+        (_tdesc([0, 3], [1, 3, 2]), fa.E_INVAL, b"ascending"),
+        (_tdesc([0, 2], [1, 1]), fa.E_INVAL, b"ascending"),
+        (_tdesc([0, 2], [-1, 3]), fa.E_INVAL, b"outside"),
+        (_tdesc([0, 2], [1, 65]), fa.E_INVAL, b"outside"),
+        (_tdesc([0, 65], list(range(65)), N=100), fa.E_UNSUPPORTED, b"at most 64"),
+        (_tdesc([0, 2], [1, 2], cls=2), fa.E_INVAL, b"cls"),
+        (_tdesc([0, 2], [1, 2], dev=None), fa.E_INVAL, b"offs_device"),
+        (_tdesc([0, 2], [1, 2], dev=GOOD + 2), fa.E_INVAL, b"aligned"),
+        (_tdesc([0, 2], [1, 2], d_h=96), fa.E_UNSUPPORTED, b"d_h"),
+    ]
+    for d, code, msg in cases:
+        assert _fwd_t(d) == code, msg
+        assert msg in L.fibatt_last_error(), (msg, L.fibatt_last_error())
+        assert L.fibatt_bwd_table_workspace_floats(ctypes.byref(d)) == -1
+    # an empty table is valid (every row empty) and needs no device copy
+    assert L.fibatt_bwd_table_workspace_floats(ctypes.byref(_tdesc([0, 0], [], dev=None))) \
+        == 2 * 65
+    # class-token mask: workspace as for fibatt_*_cls
+    big = _tdesc([0, 2], [1, 2], N=2049, d_h=128, cls=1)
+    assert L.fibatt_fwd_table_workspace_floats(ctypes.byref(big)) == 2 * 3 * 130
+    assert _fwd_t(big, ws=None) == fa.E_INVAL

@@ -347,3 +347,75 @@ def test_attention_layer(case):
     _say(f"    max-abs error / max(1, max |ref|): {rel}")
     for n, e in rel.items():
         assert e <= BLOCK_TOL[dtype], (n, e)
+
+
+def _table(lists):
+    ptr = np.zeros(len(lists) + 1, dtype=np.int32)
+    for h, fs in enumerate(lists):
+        ptr[h + 1] = ptr[h] + len(fs)
+    offs = np.array([f for fs in lists for f in fs], dtype=np.int32)
+    return ptr, offs
+
+
+_rng_sets = np.random.default_rng(77)
+TABLES = [
+    # (name, B, N, d, dtype, per-head distances, cls)
+    ("bf16 N197 constant dilation", 2, 197, 64, torch.bfloat16,
+     [list(range(3, 37, 3)), list(range(5, 61, 5)), [0] + list(range(7, 78, 7))], False),
+    ("bf16 N197 exponential", 2, 197, 64, torch.bfloat16,
+     [[1, 2, 4, 8, 16, 32, 64, 128], [0, 1, 2, 4, 8, 16, 32, 64, 128], [3, 9, 27, 81]], False),
+    ("bf16 N197 sliding windows 40 and 64", 1, 197, 64, torch.bfloat16,
+     [list(range(1, 41)), list(range(0, 64))], False),
+    ("bf16 d128 N700 exponential", 1, 700, 128, torch.bfloat16,
+     [[2 ** i for i in range(10)], [3, 9, 27, 81, 243], []], False),
+    ("bf16 N1569 exponential", 1, 1569, 64, torch.bfloat16,
+     [[2 ** i for i in range(11)], [0] + [5 * 2 ** i for i in range(9)]], False),
+    ("fp32 N90 random sets", 2, 90, 64, torch.float32,
+     [sorted(_rng_sets.choice(90, size=s, replace=False).tolist()) for s in (1, 7, 20, 64)],
+     False),
+    ("bf16 N197 exponential class token", 2, 197, 64, torch.bfloat16,
+     [[1, 2, 4, 8, 16, 32, 64, 128], [6, 12, 24, 48, 96]], True),
+]
+
+
+@pytest.mark.parametrize("case", TABLES, ids=[c[0] for c in TABLES])
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
+def test_distance_table_heads(case, path):
+    name, B, N, d, dtype, lists, cls = case
+    if path == "slab" and 2 * N * d * (2 if dtype == torch.bfloat16 else 4) + 8 * N > 80 * 1024:
+        pytest.skip("shape exceeds the LDS slab budget; the slab variant rejects it")
+    H = len(lists)
+    _say(f"case: distance table {name} B={B} H={H} N={N} d={d} {dtype} cls={cls} path={path}")
+    _set_path(path)
+    try:
+        inp = workloads.random_case(900 + N + H, B, H, N, d, dtype)
+        ptr, offs = _table(lists)
+        op = fa.FibottentionTable(B, H, N, d, dtype, ptr, offs, cls=cls)
+        dev = torch.device("cuda:0")
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = op.forward(q, k, v)
+        dq, dk, dv = op.backward(q, k, v, lse, do)
+        torch.cuda.synchronize()
+        gpu = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+        _compare(gpu, inp, [list(l) for l in lists], TOL[dtype], cls=cls)
+    finally:
+        _set_path(None)
+
+
+@pytest.mark.parametrize("shape", [(2, 12, 197, 64, torch.bfloat16), (1, 4, 700, 128, torch.bfloat16),
+                                   (2, 3, 65, 64, torch.float32)])
+def test_fibonacci_table_matches_wythoff_heads_bitwise(shape):
+    B, H, N, d, dtype = shape
+    _say(f"case: Fibonacci table vs (a, b, w) heads B={B} H={H} N={N} d={d} {dtype}")
+    inp = workloads.random_case(55 + N, B, H, N, d, dtype)
+    a, b, w, F = _heads(H, N)
+    ptr, offs = fa.offsets(N, a, b, w)
+    ref = _gpu_run(inp, a, b, w)
+    op = fa.FibottentionTable(B, H, N, d, dtype, ptr, offs)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = op.forward(q, k, v)
+    dq, dk, dv = op.backward(q, k, v, lse, do)
+    torch.cuda.synchronize()
+    for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(t.cpu(), ref[n]), n

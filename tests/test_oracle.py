@@ -525,3 +525,19 @@ def test_block_with_every_distance_is_torch_multihead_attention():
                                out.detach().numpy(), atol=1e-12, rtol=0)
     dx = oracle.block_backward(x, wq, wk, wv, wz, dout, F)[0]
     np.testing.assert_allclose(dx, tx.grad.numpy(), atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("F", [
+    [[3, 6, 9, 12], [0, 5, 10, 15, 20]],                 # constant dilation c n
+    [[1, 2, 4, 8, 16, 32], [0, 1, 2, 4, 8, 16, 32]],     # exponential 2^n
+    [list(range(1, 12)), []],                           # sliding window, empty head
+])
+def test_dilation_tables_match_dense_brute_force(F):
+    N = 37
+    q, k, v, do = (_rand((2, len(F), N, 8), 200 + t) for t in range(4))
+    masks = np.stack([oracle.support_mask(N, f) for f in F])
+    o, lse = oracle.forward(q, k, v, F)
+    o2, lse2, _ = oracle.dense_forward(q, k, v, masks)
+    np.testing.assert_allclose(o, o2, atol=1e-12, rtol=0)
+    for x, y in zip(oracle.backward(q, k, v, do, F), oracle.dense_backward(q, k, v, do, masks)):
+        np.testing.assert_allclose(x, y, atol=1e-12, rtol=0)

@@ -414,8 +414,8 @@ bool bwd_slab_fits(const Problem& p) {
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
                       float* ws, hipStream_t stream, Path path) {
-  if (path == Path::kAuto && !p.cls && bwd_slab_bf16_fits(p))
-    return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv, stream);
+  if (path == Path::kAuto && bwd_slab_bf16_fits(p))
+    return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
   if (path == Path::kAuto && !p.cls && bwd_tile_bf16_fits(p))
     return launch_bwd_tile_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
   if (p.dtype == DType::kBF16) {

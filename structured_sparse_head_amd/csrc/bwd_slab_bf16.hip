@@ -35,6 +35,16 @@
 //     output row has one writer: no atomics, bitwise reproducible.
 // Q, K, V, dO and LSE are each read from HBM once; dQ, dK, dV written once,
 // dQ and dV a chunk per step of the following pass rather than in bursts.
+//
+// Class-token mask (CLS): a row j >= 1 whose distance j to token 0 is not a
+// head distance pairs with token 0 in both roles.  As query j it meets key 0
+// (one more term of D_j and dQ_j, with K_0 and V_0 from LDS); as key j it is
+// met by query 0 (one more term of dK_j and dV_j).  The latter needs Q_0,
+// dO_0, LSE_0 and the dense D_0, which the class-token row kernel has left in
+// the workspace before this kernel runs; Q_0 and dO_0 are staged in LDS by
+// the lanes of row 0.  Row 0's own D is that dense D_0; its dQ and key 0's
+// dK and dV are replaced by the dense class-token kernels afterwards.  Every
+// D_j goes to the workspace for the column kernel.
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -54,8 +64,12 @@ constexpr int kGroups = (kMaxPos + 3) / 4;   // distance groups of four in the q
 // the last sequence row own private rows.
 constexpr int kLdsPerRow = 2 * kBf16Stride + kF32Stride;  // >= 2 * kF32Stride
 constexpr int kTableBytes = kRowsB * kTableCols * 8;
+// Class-token mask: bf16 Q_0 and dO_0, then (P, dS / sqrt(d)) of every lane
+// group's row paired with query 0.
+constexpr int kStageBytes = 256 + kRowsB * 8;
 constexpr int kLdsMax = 160 * 1024;
-constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 201
+constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;                   // 201
+constexpr int kMaxRowsBwdCls = (kLdsMax - kTableBytes - kStageBytes) / kLdsPerRow;  // 197
 
 template <int MH>
 struct Args {
@@ -67,6 +81,7 @@ struct Args {
   float* dq;
   float* dk;
   float* dv;
+  float* ws;    // class-token mask: D per row (D_0 read, every D_j written)
   int H;
   int N;
   int slabs;
@@ -284,7 +299,7 @@ __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, D
   for (; i < n; ++i) step(i);
 }
 
-template <int MH>
+template <int MH, bool CLS>
 __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -334,6 +349,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     char* lds_q = smem;
     char* lds_do = smem + N * kF32Stride;
     float2* tbl = reinterpret_cast<float2*>(smem + N * kLdsPerRow);
+    char* lds_r0 = smem + N * kLdsPerRow + kTableBytes;  // CLS: Q_0 then dO_0, bf16
+    float2* side = reinterpret_cast<float2*>(lds_r0 + 256);  // CLS: row's pair with query 0
     // Lanes past the last row repeat row N - 1 exactly (their extra terms
     // are exact zeros; their table rows are private), so every lane and wave
     // runs the same code and stores without branches: the memory wait
@@ -352,6 +369,12 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       dw[2 * m + 1] = pf.dout[m].y;
     }
     const float lse2 = pf.lse * kLog2e;
+    if (CLS && row == 0) {
+      *reinterpret_cast<u32x4*>(lds_r0 + part * 32) = u32x4{qw[0], qw[1], qw[2], qw[3]};
+      *reinterpret_cast<u32x4*>(lds_r0 + part * 32 + 16) = u32x4{qw[4], qw[5], qw[6], qw[7]};
+      *reinterpret_cast<u32x4*>(lds_r0 + 128 + part * 32) = u32x4{dw[0], dw[1], dw[2], dw[3]};
+      *reinterpret_cast<u32x4*>(lds_r0 + 144 + part * 32) = u32x4{dw[4], dw[5], dw[6], dw[7]};
+    }
     __syncthreads();
     // Start the next slab's loads; they land while this slab is computed.
     const int next = slab + gridDim.x;
@@ -372,7 +395,31 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     }
     constexpr int z = 2 * kMaxPos;  // table column of distance 0
     const bool wr = part == 0;      // table rows: row (private per lane group)
+    // Class-token mask: this row's pair with token 0 (query role: P and dP
+    // against key 0; key role: P and dS / sqrt(d) from query 0).
+    const bool need0 = CLS && rr >= 1 && !dist.has(rr, npos);
+    const size_t r0g = static_cast<size_t>(slab) * N;  // row 0 of the slab
+    if constexpr (CLS) {
+      // Key role: query 0 against this row's key, from the staged Q_0, dO_0.
+      u32x4 kb[2], vb[2], qz[2], dz[2];
+      qz[0] = *reinterpret_cast<const u32x4*>(lds_r0 + part * 32);
+      qz[1] = *reinterpret_cast<const u32x4*>(lds_r0 + part * 32 + 16);
+      dz[0] = *reinterpret_cast<const u32x4*>(lds_r0 + 128 + part * 32);
+      dz[1] = *reinterpret_cast<const u32x4*>(lds_r0 + 144 + part * 32);
+      const uint32_t q0w[8] = {qz[0].x, qz[0].y, qz[0].z, qz[0].w,
+                               qz[1].x, qz[1].y, qz[1].z, qz[1].w};
+      const uint32_t d0w[8] = {dz[0].x, dz[0].y, dz[0].z, dz[0].w,
+                               dz[1].x, dz[1].y, dz[1].z, dz[1].w};
+      load_bf16_q(lds_k + part * 32, rr, kb);
+      load_bf16_q(lds_v + part * 32, rr, vb);
+      const float s0k = dot_q(q0w, kb);
+      const float dp0k = dot_q(d0w, vb);
+      const float lse2_0 = a.lse[r0g] * kLog2e;
+      const float pk = need0 ? fast_exp2(__builtin_fmaf(s0k, a.c, -lse2_0)) : 0.f;
+      if (wr) side[row] = make_float2(pk, pk * (dp0k - a.ws[r0g]) * a.scale);
+    }
     float dqa[16];
+    float drow = 0.f;  // D of this row (class-token mask: to the workspace)
     {
       float d = 0.f;
       query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, row, N, part, slot, qw, dw, a.c, lse2, 0,
@@ -390,6 +437,16 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         if (wr) tbl[row * kTableCols + z] = make_float2(p, dp);
         d = __builtin_fmaf(p, dp, d);
       }
+      float pq = 0.f, dpq = 0.f;
+      if constexpr (CLS) {
+        u32x4 kb[2], vb[2];
+        load_bf16_q(lds_k + part * 32, 0, kb);
+        load_bf16_q(lds_v + part * 32, 0, vb);
+        const float s = dot_q(qw, kb);
+        dpq = dot_q(dw, vb);
+        pq = need0 ? fast_exp2(__builtin_fmaf(s, a.c, -lse2)) : 0.f;
+        d = rr == 0 ? a.ws[r0g] : __builtin_fmaf(pq, dpq, d);  // row 0: the dense D_0
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqa[e] = 0.f;
       dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, dqa);
@@ -402,11 +459,18 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         axpy_q(dqa, ds, kf);
         if (wr) tbl[row * kTableCols + z] = make_float2(e.x, ds * a.scale);
       }
+      if constexpr (CLS) {
+        u32x4 kf[4];
+        load_f32_q(lds_kf + part * 64, 0, kf);
+        axpy_q(dqa, pq * (dpq - d), kf);
+      }
+      drow = d;
     }
     // The next slab's loads (issued a whole pass ago) complete here, before
     // any store of this slab: the wait counter retires memory operations in
     // issue order, so no later wait has to drain this slab's stores.
     settle(pf);
+    if constexpr (CLS) a.ws[grow] = drow;  // the row's four lanes write the same value
     __syncthreads();  // K and V are no longer read; the table is complete
     if (mine) {
       store_f32_q_lds(lds_q, row, part, qw);
@@ -428,6 +492,11 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         load_f32_q(lds_do + part * 64, rr, xb);
         axpy_q(acc, tbl[rr * kTableCols + z].x, xb);
       }
+      if constexpr (CLS) {
+        u32x4 xb[4];
+        load_f32_q(lds_do + part * 64, 0, xb);
+        axpy_q(acc, side[rr].x, xb);
+      }
       const Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part, acc, 1.0f};
       float acc2[16];
 #pragma unroll
@@ -439,6 +508,11 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         load_f32_q(lds_q + part * 64, rr, xb);
         axpy_q(acc2, tbl[rr * kTableCols + z].y, xb);
       }
+      if constexpr (CLS) {
+        u32x4 xb[4];
+        load_f32_q(lds_q + part * 64, 0, xb);
+        axpy_q(acc2, side[rr].y, xb);
+      }
       float4* dk = reinterpret_cast<float4*>(a.dk + grow * 64) + part;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -447,10 +521,10 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   }
 }
 
-template <int MH>
+template <int MH, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                    hipStream_t stream) {
+                    float* ws, hipStream_t stream) {
   Args<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
@@ -460,6 +534,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.ws = ws;
   a.H = p.H;
   a.N = p.N;
   a.slabs = p.B * p.H;
@@ -467,11 +542,12 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.c = kLog2e * 0.125f;
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
   a.blocks = plan_blocks(p.N, p.H, a.rec);
-  const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes;
-  auto kern = bwd_slab_bf16_kernel<MH>;
+  constexpr int kStage = CLS ? kStageBytes : 0;
+  const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes + kStage;
+  auto kern = bwd_slab_bf16_kernel<MH, CLS>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kMaxRowsBwd * kLdsPerRow + kTableBytes);
+      (CLS ? kMaxRowsBwdCls : kMaxRowsBwd) * kLdsPerRow + kTableBytes + kStage);
   if (attr != hipSuccess) return attr;
   const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
@@ -482,14 +558,21 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
 }  // namespace
 
 bool bwd_slab_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kMaxRowsBwd && records_fit(p);
+  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= (p.cls ? kMaxRowsBwdCls : kMaxRowsBwd) &&
+         records_fit(p);
 }
 
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
-                                float* dv, hipStream_t stream) {
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, stream);
-  return launch_t<kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, stream);
+                                float* dv, float* ws, hipStream_t stream) {
+  if (p.cls) {
+    if (p.H <= kSmallHeads)
+      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  }
+  if (p.H <= kSmallHeads)
+    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
 }
 
 }  // namespace fibatt

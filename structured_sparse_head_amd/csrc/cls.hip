@@ -9,9 +9,14 @@
 // The general kernels handle rows and keys 1..N-1 (each of them pairs with
 // token 0 once more when its distance to token 0 is not a head distance).
 // This file holds the dense parts, which involve every token of a slab:
-//  * forward row 0: softmax of Q_0 . K_k over all k, O_0 = sum_k P_0k V_k;
-//  * backward row 0: D_0 = sum_k P_0k dP_0k and dQ_0 = sum_k dS_0k K_k;
-//  * backward column 0: dV_0 = sum_j P_j0 dO_j, dK_0 = sum_j dS_j0 Q_j.
+//  * forward row 0: softmax of Q_0 . K_k over all k, O_0 = sum_k P_0k V_k
+//    (launched after the main forward, whose row 0 it replaces);
+//  * backward row 0: D_0 = sum_k P_0k dP_0k and dQ_0 = sum_k dS_0k K_k
+//    (launched first: the main backward reads D_0; dQ_0 waits in the
+//    workspace, because the main kernels may write row 0 of dQ);
+//  * backward column 0: dV_0 = sum_j P_j0 dO_j, dK_0 = sum_j dS_j0 Q_j
+//    (launched last, with every D_j in the workspace; it also copies dQ_0
+//    into place).
 // A slab's N rows are split into ranges of kSplitRows; one workgroup reduces
 // one range (each lane group walks every NG-th row of it and the groups are
 // combined in LDS in a fixed order), and with more than one range a second
@@ -36,6 +41,7 @@ struct ClsArgs {
   float* dk;
   float* dv;
   float* ws_d;   // D per row, [slabs, N]
+  float* dq0;    // dQ of row 0 per slab, [slabs, D], copied into dq last
   float* part;   // per-range partials
   int N;
   int splits;    // ranges per slab
@@ -43,7 +49,7 @@ struct ClsArgs {
   float scale;
 };
 
-// Lane-group width: 64 bytes of a row per lane.
+// Lane-group width for the per-row dot products: 64 bytes of a row per lane.
 template <typename T, int D>
 constexpr int cls_group() {
   return (D * static_cast<int>(sizeof(T))) / 64;
@@ -58,108 +64,143 @@ __device__ __forceinline__ void store_elem(char* row, int e, float x) {
   }
 }
 
-// Sums x (each group's kDL elements of a D-vector) over the workgroup's
-// groups in group order; thread t < D receives element t.  `buf` holds
-// NG * D floats.
-template <int D, int G, int NT>
-__device__ __forceinline__ float groups_sum(float* buf, int tid, const float* x) {
-  constexpr int kDL = D / G;
-  const int g = tid / G, part = tid % G;
+// Block-wide max and sum of one value per thread: a butterfly inside each
+// wave, then the waves in order.  Every thread gets wave 0's lane 0 order.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < NT / 64; ++i) r += red[i];
+  __syncthreads();
+  return r;
+}
+
+// Weighted sums of n rows of x (row-major [rows, D] in T, rows r0 ..):
+// out_c[e] = sum_i coef_c[i] x_{r0 + i}[e] for NC coefficient arrays (LDS).
+// Each thread takes one 16-byte chunk of a row and every KG-th row; the KG
+// partial sums of an element are added in order.  Thread e < D gets element
+// e; `red` holds KG * D floats.
+template <typename T, int D, int NT, int NC>
+__device__ __forceinline__ void rows_wsum(const char* x, int r0, int n, const float* const* coef,
+                                          float* red, float (&out)[NC]) {
+  constexpr int CH = 16 / static_cast<int>(sizeof(T));  // elements per chunk
+  constexpr int CPR = D / CH;                           // chunks per row
+  constexpr int KG = NT / CPR;                          // row groups
+  const int tid = threadIdx.x;
+  const int c = tid % CPR, kg = tid / CPR;
+  float acc[NC][CH];
 #pragma unroll
-  for (int t = 0; t < kDL; ++t) buf[g * D + part * kDL + t] = x[t];
-  __syncthreads();
-  float s = 0.f;
-  if (tid < D)
-    for (int i = 0; i < NT / G; ++i) s += buf[i * D + tid];
-  __syncthreads();
-  return s;
+  for (int u = 0; u < NC; ++u)
+#pragma unroll
+    for (int t = 0; t < CH; ++t) acc[u][t] = 0.f;
+  const char* base = x + static_cast<size_t>(r0) * D * sizeof(T) + c * 16;
+#pragma unroll 4
+  for (int i = kg; i < n; i += KG) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(i) * D * sizeof(T));
+    float e[CH];
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        e[2 * t] = bf16_lo(ww[t]);
+        e[2 * t + 1] = bf16_hi(ww[t]);
+      }
+    } else {
+      e[0] = __uint_as_float(w.x);
+      e[1] = __uint_as_float(w.y);
+      e[2] = __uint_as_float(w.z);
+      e[3] = __uint_as_float(w.w);
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const float cf = coef[u][i];
+#pragma unroll
+      for (int t = 0; t < CH; ++t) acc[u][t] = __builtin_fmaf(cf, e[t], acc[u][t]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+#pragma unroll
+    for (int t = 0; t < CH; ++t) red[kg * D + c * CH + t] = acc[u][t];
+    __syncthreads();
+    float s = 0.f;
+    if (tid < D)
+      for (int j = 0; j < KG; ++j) s += red[j * D + tid];
+    out[u] = s;
+    __syncthreads();
+  }
 }
 
-template <int NG>
-__device__ __forceinline__ float scalar_sum(const float* buf) {
-  float s = 0.f;
-  for (int i = 0; i < NG; ++i) s += buf[i];
-  return s;
+// Per-row dot products of one range: group g (G lanes) takes rows r0 + g,
+// r0 + g + NG, ...; f(i, r, part) runs for each with the group's lanes.
+template <int G, int NT, typename F>
+__device__ __forceinline__ void for_rows(int r0, int r1, F f) {
+  const int g = threadIdx.x / G, part = threadIdx.x % G;
+  for (int r = r0 + g; r < r1; r += NT / G) f(r - r0, r, part);
 }
 
-// Forward, row 0 against the keys of one range.
+// Forward, row 0 against the keys of one range.  Scores in base 2; the
+// range's (max, sum of exp, sum of exp V) are final or a partial.
 template <typename T, int D, int G, int NT>
 __global__ void __launch_bounds__(NT) fwd_cls_row_kernel(ClsArgs a) {
   using Gm = Geom<T, D, G>;
   using M = FragMath<T, Gm::kWPL>;
-  constexpr int NG = NT / G;
-  constexpr int C = 4;
-  __shared__ float s_m[NG];
-  __shared__ float s_l[NG];
-  __shared__ float s_buf[NG * D];
+  constexpr int KG = NT / (D * static_cast<int>(sizeof(T)) / 16);
+  __shared__ float s_w[kSplitRows];
+  __shared__ float s_red[KG * D];
   const int tid = threadIdx.x;
   const size_t slab = blockIdx.x / a.splits;
   const int sp = blockIdx.x % a.splits;
   const int N = a.N;
   const int k0 = sp * kSplitRows;
   const int k1 = min(N, k0 + kSplitRows);
-  const int g = tid / G, part = tid % G;
+  const int n = k1 - k0;
   const size_t base = slab * N * Gm::kRowBytes;
   uint32_t qf[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.q + base, part, qf);
-  float acc[Gm::kDL];
-#pragma unroll
-  for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  for (int c0 = k0 + g; c0 < k1; c0 += NG * C) {
-    float s[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int kk = c0 + c * NG;
-      s[c] = -INFINITY;
-      if (kk < k1) {
-        uint32_t kf[Gm::kWPL];
-        frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(kk) * Gm::kRowBytes, part, kf);
-        s[c] = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
-      }
-    }
-    float mc = s[0];
-#pragma unroll
-    for (int c = 1; c < C; ++c) mc = fmaxf(mc, s[c]);
-    const float mn = fmaxf(m, mc);  // finite: key c0 is in range
-    const float alpha = fast_exp2(m - mn);
-    l *= alpha;
-#pragma unroll
-    for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int kk = c0 + c * NG;
-      if (kk < k1) {
-        const float p = fast_exp2(s[c] - mn);
-        l += p;
-        uint32_t vf[Gm::kWPL];
-        frag_load_cached<T, D, G>(a.v + base + static_cast<size_t>(kk) * Gm::kRowBytes, part, vf);
-        M::axpy(acc, p, vf);
-      }
-    }
-    m = mn;
-  }
-  // Combine the groups: common maximum, rescaled sums.
-  if (part == 0) s_m[g] = m;
+  frag_load_cached<T, D, G>(a.q + base, tid % G, qf);
+  for_rows<G, NT>(k0, k1, [&](int i, int r, int part) {
+    uint32_t kf[Gm::kWPL];
+    frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(r) * Gm::kRowBytes, part, kf);
+    const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
+    if (part == 0) s_w[i] = s;
+  });
   __syncthreads();
-  float mx = -INFINITY;
-  for (int i = 0; i < NG; ++i) mx = fmaxf(mx, s_m[i]);  // group 0 always has a key
-  const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mx);
-#pragma unroll
-  for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
-  if (part == 0) s_l[g] = l * alpha;
-  const float o = groups_sum<D, G, NT>(s_buf, tid, acc);
-  const float lsum = scalar_sum<NG>(s_l);
+  float m = -INFINITY;
+  for (int i = tid; i < n; i += NT) m = fmaxf(m, s_w[i]);
+  m = block_max<NT>(m, s_red);
+  float l = 0.f;
+  for (int i = tid; i < n; i += NT) {
+    const float w = fast_exp2(s_w[i] - m);
+    s_w[i] = w;
+    l += w;
+  }
+  l = block_sum<NT>(l, s_red);  // (its barrier also publishes s_w)
+  const float* coef[1] = {s_w};
+  float o[1];
+  rows_wsum<T, D, NT, 1>(a.v + base, k0, n, coef, s_red, o);
   if (tid < D) {
     if (a.splits == 1) {
-      store_elem<T>(a.o + base, tid, o / lsum);
-      if (tid == 0) a.lse[slab * N] = (mx + fast_log2(lsum)) * kLn2;
+      store_elem<T>(a.o + base, tid, o[0] / l);
+      if (tid == 0) a.lse[slab * N] = (m + fast_log2(l)) * kLn2;
     } else {
       float* pp = a.part + (slab * a.splits + sp) * (D + 2);
-      pp[2 + tid] = o;
+      pp[2 + tid] = o[0];
       if (tid == 0) {
-        pp[0] = mx;
-        pp[1] = lsum;
+        pp[0] = m;
+        pp[1] = l;
       }
     }
   }
@@ -190,48 +231,50 @@ template <typename T, int D, int G, int NT>
 __global__ void __launch_bounds__(NT) bwd_cls_row_kernel(ClsArgs a) {
   using Gm = Geom<T, D, G>;
   using M = FragMath<T, Gm::kWPL>;
-  constexpr int NG = NT / G;
-  __shared__ float s_d[NG];
-  __shared__ float s_buf[NG * D];
+  constexpr int KG = NT / (D * static_cast<int>(sizeof(T)) / 16);
+  __shared__ float s_pdp[kSplitRows];
+  __shared__ float s_p[kSplitRows];
+  __shared__ float s_red[KG * D];
   const int tid = threadIdx.x;
   const size_t slab = blockIdx.x / a.splits;
   const int sp = blockIdx.x % a.splits;
   const int N = a.N;
   const int k0 = sp * kSplitRows;
   const int k1 = min(N, k0 + kSplitRows);
-  const int g = tid / G, part = tid % G;
+  const int n = k1 - k0;
   const size_t base = slab * N * Gm::kRowBytes;
   uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.q + base, part, qf);
-  frag_load_cached<T, D, G>(a.dout + base, part, dof);
+  frag_load_cached<T, D, G>(a.q + base, tid % G, qf);
+  frag_load_cached<T, D, G>(a.dout + base, tid % G, dof);
   const float lse2 = a.lse[slab * N] * kLog2e;
-  float acc_a[Gm::kDL], acc_b[Gm::kDL];
-#pragma unroll
-  for (int t = 0; t < Gm::kDL; ++t) acc_a[t] = acc_b[t] = 0.f;
-  float d = 0.f;
-  for (int kk = k0 + g; kk < k1; kk += NG) {
+  for_rows<G, NT>(k0, k1, [&](int i, int r, int part) {
     uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(kk) * Gm::kRowBytes, part, kf);
-    frag_load_cached<T, D, G>(a.v + base + static_cast<size_t>(kk) * Gm::kRowBytes, part, vf);
+    frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(r) * Gm::kRowBytes, part, kf);
+    frag_load_cached<T, D, G>(a.v + base + static_cast<size_t>(r) * Gm::kRowBytes, part, vf);
     const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
     const float dp = group_sum<G>(M::dot(dof, vf));
     const float p = fast_exp2(s - lse2);
-    d = __builtin_fmaf(p, dp, d);
-    M::axpy2(acc_a, p * dp, acc_b, p, kf);
-  }
-  if (part == 0) s_d[g] = d;
-  const float A = groups_sum<D, G, NT>(s_buf, tid, acc_a);
-  const float Bv = groups_sum<D, G, NT>(s_buf, tid, acc_b);
-  const float dsum = scalar_sum<NG>(s_d);
+    if (part == 0) {
+      s_pdp[i] = p * dp;
+      s_p[i] = p;
+    }
+  });
+  __syncthreads();
+  float d = 0.f;
+  for (int i = tid; i < n; i += NT) d += s_pdp[i];
+  d = block_sum<NT>(d, s_red);
+  const float* coef[2] = {s_pdp, s_p};
+  float ab[2];
+  rows_wsum<T, D, NT, 2>(a.k + base, k0, n, coef, s_red, ab);
   if (tid < D) {
     if (a.splits == 1) {
-      a.dq[slab * N * D + tid] = __builtin_fmaf(-dsum, Bv, A) * a.scale;
-      if (tid == 0) a.ws_d[slab * N] = dsum;
+      a.dq0[slab * D + tid] = __builtin_fmaf(-d, ab[1], ab[0]) * a.scale;
+      if (tid == 0) a.ws_d[slab * N] = d;
     } else {
       float* pp = a.part + (slab * a.splits + sp) * (2 * D + 1);
-      pp[1 + tid] = A;
-      pp[1 + D + tid] = Bv;
-      if (tid == 0) pp[0] = dsum;
+      pp[1 + tid] = ab[0];
+      pp[1 + D + tid] = ab[1];
+      if (tid == 0) pp[0] = d;
     }
   }
 }
@@ -248,7 +291,7 @@ __global__ void __launch_bounds__(D) bwd_cls_row_combine_kernel(ClsArgs a) {
     A += q[1 + tid];
     Bv += q[1 + D + tid];
   }
-  a.dq[slab * a.N * D + tid] = __builtin_fmaf(-dsum, Bv, A) * a.scale;
+  a.dq0[slab * D + tid] = __builtin_fmaf(-dsum, Bv, A) * a.scale;
   if (tid == 0) a.ws_d[slab * a.N] = dsum;
 }
 
@@ -257,44 +300,50 @@ template <typename T, int D, int G, int NT>
 __global__ void __launch_bounds__(NT) bwd_cls_col_kernel(ClsArgs a) {
   using Gm = Geom<T, D, G>;
   using M = FragMath<T, Gm::kWPL>;
-  constexpr int NG = NT / G;
-  __shared__ float s_buf[NG * D];
+  constexpr int KG = NT / (D * static_cast<int>(sizeof(T)) / 16);
+  __shared__ float s_p[kSplitRows];
+  __shared__ float s_ds[kSplitRows];
+  __shared__ float s_red[KG * D];
   const int tid = threadIdx.x;
   const size_t slab = blockIdx.x / a.splits;
   const int sp = blockIdx.x % a.splits;
   const int N = a.N;
   const int j0 = sp * kSplitRows;
   const int j1 = min(N, j0 + kSplitRows);
-  const int g = tid / G, part = tid % G;
+  const int n = j1 - j0;
   const size_t base = slab * N * Gm::kRowBytes;
   uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.k + base, part, kf);
-  frag_load_cached<T, D, G>(a.v + base, part, vf);
-  float dk[Gm::kDL], dv[Gm::kDL];
-#pragma unroll
-  for (int t = 0; t < Gm::kDL; ++t) dk[t] = dv[t] = 0.f;
-  for (int jj = j0 + g; jj < j1; jj += NG) {
+  frag_load_cached<T, D, G>(a.k + base, tid % G, kf);
+  frag_load_cached<T, D, G>(a.v + base, tid % G, vf);
+  for_rows<G, NT>(j0, j1, [&](int i, int r, int part) {
     uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.q + base + static_cast<size_t>(jj) * Gm::kRowBytes, part, qf);
-    frag_load_cached<T, D, G>(a.dout + base + static_cast<size_t>(jj) * Gm::kRowBytes, part, dof);
-    const float lse2 = a.lse[slab * N + jj] * kLog2e;
-    const float dj = a.ws_d[slab * N + jj];
+    frag_load_cached<T, D, G>(a.q + base + static_cast<size_t>(r) * Gm::kRowBytes, part, qf);
+    frag_load_cached<T, D, G>(a.dout + base + static_cast<size_t>(r) * Gm::kRowBytes, part, dof);
+    const float lse2 = a.lse[slab * N + r] * kLog2e;
+    const float dj = a.ws_d[slab * N + r];
     const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
     const float dp = group_sum<G>(M::dot(dof, vf));
     const float p = fast_exp2(s - lse2);
-    M::axpy(dv, p, dof);
-    M::axpy(dk, p * (dp - dj), qf);
-  }
-  const float sk = groups_sum<D, G, NT>(s_buf, tid, dk);
-  const float sv = groups_sum<D, G, NT>(s_buf, tid, dv);
+    if (part == 0) {
+      s_p[i] = p;
+      s_ds[i] = p * (dp - dj);
+    }
+  });
+  __syncthreads();
+  const float* cv[1] = {s_p};
+  const float* ck[1] = {s_ds};
+  float sv[1], sk[1];
+  rows_wsum<T, D, NT, 1>(a.dout + base, j0, n, cv, s_red, sv);
+  rows_wsum<T, D, NT, 1>(a.q + base, j0, n, ck, s_red, sk);
   if (tid < D) {
     if (a.splits == 1) {
-      a.dk[slab * N * D + tid] = sk * a.scale;
-      a.dv[slab * N * D + tid] = sv;
+      a.dk[slab * N * D + tid] = sk[0] * a.scale;
+      a.dv[slab * N * D + tid] = sv[0];
+      a.dq[slab * N * D + tid] = a.dq0[slab * D + tid];
     } else {
       float* pp = a.part + (slab * a.splits + sp) * (2 * D);
-      pp[tid] = sk;
-      pp[D + tid] = sv;
+      pp[tid] = sk[0];
+      pp[D + tid] = sv[0];
     }
   }
 }
@@ -311,6 +360,7 @@ __global__ void __launch_bounds__(D) bwd_cls_col_combine_kernel(ClsArgs a) {
   }
   a.dk[slab * a.N * D + tid] = sk * a.scale;
   a.dv[slab * a.N * D + tid] = sv;
+  a.dq[slab * a.N * D + tid] = a.dq0[slab * D + tid];
 }
 
 ClsArgs make_args(const Problem& p) {
@@ -389,7 +439,7 @@ int64_t fwd_cls_workspace_floats(const Problem& p) {
 int64_t bwd_cls_workspace_floats(const Problem& p) {
   const int s = cls_splits(p);
   const int64_t slabs = static_cast<int64_t>(p.B) * p.H;
-  return slabs * p.N + (s > 1 ? slabs * s * (2 * p.D + 1) : 0);
+  return slabs * (p.N + p.D) + (s > 1 ? slabs * s * (2 * p.D + 1) : 0);
 }
 
 hipError_t launch_fwd_cls(const Problem& p0, const void* q, const void* k, const void* v,
@@ -423,7 +473,8 @@ hipError_t launch_bwd_cls(const Problem& p0, const void* q, const void* k, const
   a.dk = dk;
   a.dv = dv;
   a.ws_d = ws;
-  a.part = ws + static_cast<size_t>(p.B) * p.H * p.N;
+  a.dq0 = ws + static_cast<size_t>(p.B) * p.H * p.N;
+  a.part = a.dq0 + static_cast<size_t>(p.B) * p.H * p.D;
   // Row 0 first: the key pass of the general kernels needs D_0.
   hipError_t e = bwd_row(p, a, stream);
   if (e != hipSuccess) return e;

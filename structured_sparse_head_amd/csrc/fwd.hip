@@ -301,7 +301,7 @@ bool fwd_slab_fits(const Problem& p) {
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, hipStream_t stream, Path path) {
-  if (path == Path::kAuto && !p.cls && fwd_slab_bf16_fits(p))
+  if (path == Path::kAuto && fwd_slab_bf16_fits(p))
     return launch_fwd_slab_bf16(p, q, k, v, o, lse, stream);
   if (path == Path::kAuto && !p.cls && fwd_tile_bf16_fits(p))
     return launch_fwd_tile_bf16(p, q, k, v, o, lse, stream);

@@ -31,6 +31,9 @@
 //    chunks of the next slab's Q, K and V in flight in registers; they are
 //    committed to LDS after the next barrier (Q too, so that no prefetch
 //    register is carried across the loop).
+//  * Class-token mask (CLS): a row j >= 1 whose distance j to token 0 is not
+//    a head distance scores key 0 as one more key, like the diagonal; row 0
+//    is replaced afterwards by the dense class-token row kernel.
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -192,7 +195,7 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int
 // One slab for an active wave (its first row is < N).  Lanes past the last
 // row repeat row N - 1 and store the same values, so the stores need no
 // branch and the memory wait counter stays exact around the loop.
-template <typename A>
+template <bool CLS, typename A>
 __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row, int part, int slot,
                                             int r0,
                                             const char* lds_k, const char* lds_v,
@@ -229,9 +232,17 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
     load_bf16_q(lds_k + part * 32, rr, kf);
     s0 = dot_q(qw, kf);
   }
+  float sc = -INFINITY;  // class-token column: key 0
+  if constexpr (CLS) {
+    u32x4 kf[2];
+    load_bf16_q(lds_k + part * 32, 0, kf);
+    const float t = dot_q(qw, kf);
+    sc = (rr >= 1 && !dist.has(rr, npos)) ? t : -INFINITY;
+  }
   float m = fmaxf(fmaxf(sp[0], sm[0]), fmaxf(sp[1], sm[1]));
   m = quad_max(fmaxf(m, fmaxf(sp[2], sm[2])));
   m = fmaxf(m, s0);
+  if constexpr (CLS) m = fmaxf(m, sc);
   // Pass 2: P = exp(scale (s - m)), accumulate P V in fp32.  A row with no
   // key in its support keeps l = 0 and is written as O = 0, LSE = -inf.
   const bool any = m != -INFINITY;
@@ -248,6 +259,13 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
     u32x4 vf[4];
     load_f32_q(lds_v + part * 64, rr, vf);
     const float p = fast_exp2(__builtin_fmaf(s0, c, -mc));
+    l += p;
+    axpy_q(o, p, vf);
+  }
+  if constexpr (CLS) {
+    u32x4 vf[4];
+    load_f32_q(lds_v + part * 64, 0, vf);
+    const float p = fast_exp2(__builtin_fmaf(sc, c, -mc));  // 0 for sc = -inf
     l += p;
     axpy_q(o, p, vf);
   }
@@ -271,7 +289,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   a.lse[grow] = lse;  // the row's four lanes write the same value
 }
 
-template <int MH>
+template <int MH, bool CLS>
 __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -308,7 +326,7 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
       __syncthreads();
       const int next = slab + gridDim.x;
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
-      attend_slab(a, slab, N, row, part, slot, r0, lds_k, lds_v, lds_q, pf);
+      attend_slab<CLS>(a, slab, N, row, part, slot, r0, lds_k, lds_v, lds_q, pf);
     }
   } else {
     for (; slab < a.slabs; slab += gridDim.x) {
@@ -324,7 +342,7 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   }
 }
 
-template <int MH>
+template <int MH, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                     float* lse, hipStream_t stream) {
   Args<MH> a;
@@ -340,7 +358,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
   a.blocks = plan_blocks(p.N, p.H, a.rec);
   const size_t lds = static_cast<size_t>(p.N) * (2 * kBf16Stride + kF32Stride);
-  auto kern = fwd_slab_bf16_kernel<MH>;
+  auto kern = fwd_slab_bf16_kernel<MH, CLS>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -360,8 +378,12 @@ bool fwd_slab_bf16_fits(const Problem& p) {
 
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream) {
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads>(p, q, k, v, o, lse, stream);
-  return launch_t<kMaxHeads>(p, q, k, v, o, lse, stream);
+  if (p.cls) {
+    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, true>(p, q, k, v, o, lse, stream);
+    return launch_t<kMaxHeads, true>(p, q, k, v, o, lse, stream);
+  }
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, false>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads, false>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace fibatt

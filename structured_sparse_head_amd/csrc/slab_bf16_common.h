@@ -174,6 +174,12 @@ struct Dist {
     const uint32_t w = i < 4 ? w0 : (i < 8 ? w1 : w2);
     return static_cast<int>((w >> (8 * (i & 3))) & 0xffu);
   }
+  // Whether j is one of the first n (wave-uniform) distances.
+  __device__ __forceinline__ bool has(int j, int n) const {
+    bool found = false;
+    for (int i = 0; i < n; ++i) found |= at(i) == j;
+    return found;
+  }
 };
 
 // Per-head record handed to the kernels in their arguments: bytes 0..11 are

@@ -267,6 +267,13 @@ CLS = [
     ("fp32 d128 N2", 1, 3, 2, 128, torch.float32, None, None),
     ("bf16 N2500 three ranges", 1, 3, 2500, 64, torch.bfloat16, None, None),
     ("fp32 d128 N1100 two ranges", 1, 2, 1100, 128, torch.float32, None, None),
+    # ViT kernels (bf16, d_h 64, N <= 197 for the backward, <= 256 forward)
+    ("bf16 N197 H12 B5", 5, 12, 197, 64, torch.bfloat16, None, None),
+    ("bf16 N150 diag windows", 2, 3, 150, 64, torch.bfloat16, ([0, 3, 5], [1, 3, 1]),
+     [150, 40, 3]),
+    ("bf16 N33 H17", 2, 17, 33, 64, torch.bfloat16, None, None),
+    ("bf16 N198 (ViT forward, general backward)", 1, 4, 198, 64, torch.bfloat16, None, None),
+    ("bf16 N256 H5", 1, 5, 256, 64, torch.bfloat16, None, None),
 ]
 
 
@@ -303,6 +310,7 @@ BLOCK = [
     ("fp32 ViT-B dims N197", 2, 197, 768, 12, torch.float32, False, False),
     ("bf16 ViT-B dims N197", 2, 197, 768, 12, torch.bfloat16, False, False),
     ("bf16 class token modified", 2, 197, 768, 12, torch.bfloat16, True, True),
+    ("bf16 class token", 2, 197, 768, 12, torch.bfloat16, True, False),
     ("fp32 d128 N300", 1, 300, 512, 4, torch.float32, False, False),
 ]
 # Tolerance of a whole layer, relative to the largest reference magnitude of

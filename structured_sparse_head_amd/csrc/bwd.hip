@@ -416,7 +416,7 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       float* ws, hipStream_t stream, Path path) {
   if (path == Path::kAuto && bwd_slab_bf16_fits(p))
     return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-  if (path == Path::kAuto && !p.cls && bwd_tile_bf16_fits(p))
+  if (path == Path::kAuto && bwd_tile_bf16_fits(p))
     return launch_bwd_tile_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
   if (p.dtype == DType::kBF16) {
     if (p.D == 64)

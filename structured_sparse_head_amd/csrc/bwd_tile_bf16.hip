@@ -89,7 +89,13 @@ __device__ __forceinline__ void frag_words(const u32x4 (&f)[2], uint32_t (&w)[8]
   w[4] = f[1].x; w[5] = f[1].y; w[6] = f[1].z; w[7] = f[1].w;
 }
 
-template <int MH, int KG, int NQ>
+// CLS (class-token mask): a row j >= 1 whose distance j to token 0 is not a
+// head distance pairs with token 0: as query (one more term of D_j and dQ_j
+// here) and as key (one more term of dK_j and dV_j from query 0 in the key
+// kernel, with the dense D_0 that the class-token row kernel left in the
+// workspace).  Row 0's D is that D_0; its dQ and key 0's dK and dV are
+// replaced by the dense class-token kernels afterwards.
+template <int MH, int KG, int NQ, bool CLS>
 __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -158,7 +164,17 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       dl = __builtin_fmaf(p, dp, dl);
     }
   }
-  const float dd = quad_sum4(dl);  // both halves of a row hold the same P, dP
+  float dd = quad_sum4(dl);  // both halves of a row hold the same P, dP
+  float pq = 0.f, dpq = 0.f;
+  if constexpr (CLS) {
+    u32x4 k0f[2], v0f[2];
+    load_row_q(kbase, k0f);
+    load_row_q(vbase, v0f);
+    const float s = halves_sum<NQ>(quad_sum4(dot_part(qw, k0f)));
+    dpq = halves_sum<NQ>(quad_sum4(dot_part(dw, v0f)));
+    pq = (rr >= 1 && !has_delta(s_deltas, nd, rr)) ? fast_exp2(__builtin_fmaf(s, a.c, -lse2)) : 0.f;
+    dd = rr == 0 ? a.ws[rbase] : __builtin_fmaf(pq, dpq, dd);  // row 0: the dense D_0
+  }
 
   // Pass 2: dQ = sum dS K / sqrt(d).
   float acc[16];
@@ -181,11 +197,16 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       }
     }
   }
+  if constexpr (CLS) {
+    u32x4 k0f[2];
+    load_row_q(kbase, k0f);
+    axpy_bf16(acc, pq * (dpq - dd), k0f);
+  }
   store_row_f32(a.dq + (rbase + rr) * G::kD + 64 * half, part, acc, a.scale);
   if (part == 0 && half == 0) a.ws[rbase + rr] = dd;
 }
 
-template <int MH, int NQ>
+template <int MH, int NQ, bool CLS>
 __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -260,17 +281,29 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
       axpy_bf16(dk, dsg[j], qf[j]);
     }
   }
+  if constexpr (CLS) {
+    u32x4 q0f[2], o0f[2];
+    load_row_q(qbase, q0f);
+    load_row_q(obase, o0f);
+    const float s = halves_sum<NQ>(quad_sum4(dot_part(kw, q0f)));
+    const float dp = halves_sum<NQ>(quad_sum4(dot_part(vw, o0f)));
+    const float p = (rr >= 1 && !has_delta(s_deltas, nd, rr))
+                        ? fast_exp2(__builtin_fmaf(s, a.c, -a.lse[rbase] * kLog2e))
+                        : 0.f;
+    axpy_bf16(dv, p, o0f);
+    axpy_bf16(dk, p * (dp - a.ws[rbase]), q0f);
+  }
   store_row_f32(a.dk + (rbase + rr) * G::kD + 64 * half, part, dk, a.scale);
   store_row_f32(a.dv + (rbase + rr) * G::kD + 64 * half, part, dv, 1.0f);
 }
 
-template <int MH, int KG, int NQ>
+template <int MH, int KG, int NQ, bool CLS>
 void launch_dq(const BwdTileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ>), dim3(grid), dim3(kTileThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
+                     stream, a);
 }
 
-template <int MH, int NQ>
+template <int MH, int NQ, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
                     float* ws, hipStream_t stream) {
@@ -300,14 +333,15 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_dq<MH, 4, NQ>(a, grid, stream);
+    launch_dq<MH, 4, NQ, CLS>(a, grid, stream);
   else if (groups <= 8)
-    launch_dq<MH, 8, NQ>(a, grid, stream);
+    launch_dq<MH, 8, NQ, CLS>(a, grid, stream);
   else if (groups <= 12)
-    launch_dq<MH, 12, NQ>(a, grid, stream);
+    launch_dq<MH, 12, NQ, CLS>(a, grid, stream);
   else
-    launch_dq<MH, (kMaxSigned + 3) / 4, NQ>(a, grid, stream);
-  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ>), dim3(grid), dim3(kTileThreads), 0, stream, a);
+    launch_dq<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, grid, stream);
+  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -317,17 +351,25 @@ bool bwd_tile_bf16_fits(const Problem& p) {
   return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
 }
 
+template <bool CLS>
+hipError_t launch_cls(const Problem& p, const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      float* ws, hipStream_t stream) {
+  if (p.D == 128) {
+    if (p.H <= kSmallHeads)
+      return launch_t<kSmallHeads, 2, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    return launch_t<kMaxHeads, 2, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  }
+  if (p.H <= kSmallHeads)
+    return launch_t<kSmallHeads, 1, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  return launch_t<kMaxHeads, 1, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+}
+
 hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
                                 float* dv, float* ws, hipStream_t stream) {
-  if (p.D == 128) {
-    if (p.H <= kSmallHeads)
-      return launch_t<kSmallHeads, 2>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    return launch_t<kMaxHeads, 2>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-  }
-  if (p.H <= kSmallHeads)
-    return launch_t<kSmallHeads, 1>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-  return launch_t<kMaxHeads, 1>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  return p.cls ? launch_cls<true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream)
+               : launch_cls<false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
 }
 
 }  // namespace fibatt

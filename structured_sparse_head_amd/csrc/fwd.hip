@@ -303,7 +303,7 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
                       float* lse, hipStream_t stream, Path path) {
   if (path == Path::kAuto && fwd_slab_bf16_fits(p))
     return launch_fwd_slab_bf16(p, q, k, v, o, lse, stream);
-  if (path == Path::kAuto && !p.cls && fwd_tile_bf16_fits(p))
+  if (path == Path::kAuto && fwd_tile_bf16_fits(p))
     return launch_fwd_tile_bf16(p, q, k, v, o, lse, stream);
   if (p.dtype == DType::kBF16) {
     if (p.D == 64) return launch_fwd_d<bf16_t, 64>(p, q, k, v, o, lse, stream, path);

@@ -29,6 +29,9 @@
 //    Pass 2 turns each lane's own scores into probabilities, broadcasts a
 //    group's four within the quad and accumulates P V in fp32.
 //  * Lanes past the last row repeat row N - 1 and write identical values.
+//  * Class-token mask (CLS): a row j >= 1 whose distance j to token 0 is not
+//    a head distance also scores key 0; row 0 is replaced afterwards by the
+//    dense class-token row kernel.
 #include "tile_bf16_common.h"
 
 namespace fibatt {
@@ -58,7 +61,7 @@ struct TileArgs {
 
 // KG: displacement groups of four the kernel holds scores for (at least
 // the largest head's count); smaller instantiations keep fewer registers.
-template <int MH, int KG, int NQ>
+template <int MH, int KG, int NQ, bool CLS>
 __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -132,6 +135,14 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
 #pragma unroll
   for (int g = 1; g < KG; ++g) m = fmaxf(m, s[g]);
   m = quad_max4(m);  // both halves of a row hold the same scores
+  float sc = -INFINITY;  // class-token column: key 0
+  if constexpr (CLS) {
+    u32x4 k0f[2];
+    load_row_q(kbase, k0f);
+    const float t = halves_sum<NQ>(quad_sum4(dot_part(qw, k0f)));
+    sc = (rr >= 1 && !has_delta(s_deltas, nd, rr)) ? t : -INFINITY;
+    m = fmaxf(m, sc);
+  }
 
   // Pass 2: P = exp(scale (s - m)), P V in fp32.  A row with no key in its
   // support keeps l = 0 and is written as O = 0, LSE = -inf.  A group's four
@@ -167,6 +178,13 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     }
   }
   l = quad_sum4(l);  // (the other half's l is the same)
+  if constexpr (CLS) {
+    u32x4 v0f[2];
+    load_row_q(vbase, v0f);
+    const float p = fast_exp2(__builtin_fmaf(sc, c, -mc));  // 0 for sc = -inf
+    l += p;
+    axpy_bf16(o, p, v0f);
+  }
   const float inv = any ? 1.0f / l : 0.f;
   uint32_t ow[8];
 #pragma unroll
@@ -183,13 +201,13 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     a.lse[static_cast<size_t>(slab) * N + rr] = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-template <int MH, int KG, int NQ>
+template <int MH, int KG, int NQ, bool CLS>
 void launch_kg(const TileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ>), dim3(grid), dim3(kTileThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
+                     stream, a);
 }
 
-template <int MH, int NQ>
+template <int MH, int NQ, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                     float* lse, hipStream_t stream) {
   TileArgs<MH> a;
@@ -213,13 +231,13 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_kg<MH, 4, NQ>(a, grid, stream);
+    launch_kg<MH, 4, NQ, CLS>(a, grid, stream);
   else if (groups <= 8)
-    launch_kg<MH, 8, NQ>(a, grid, stream);
+    launch_kg<MH, 8, NQ, CLS>(a, grid, stream);
   else if (groups <= 12)
-    launch_kg<MH, 12, NQ>(a, grid, stream);
+    launch_kg<MH, 12, NQ, CLS>(a, grid, stream);
   else
-    launch_kg<MH, (kMaxSigned + 3) / 4, NQ>(a, grid, stream);
+    launch_kg<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, grid, stream);
   return hipGetLastError();
 }
 
@@ -229,14 +247,21 @@ bool fwd_tile_bf16_fits(const Problem& p) {
   return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
 }
 
+template <bool CLS>
+hipError_t launch_cls(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t stream) {
+  if (p.D == 128) {
+    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 2, CLS>(p, q, k, v, o, lse, stream);
+    return launch_t<kMaxHeads, 2, CLS>(p, q, k, v, o, lse, stream);
+  }
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 1, CLS>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads, 1, CLS>(p, q, k, v, o, lse, stream);
+}
+
 hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream) {
-  if (p.D == 128) {
-    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 2>(p, q, k, v, o, lse, stream);
-    return launch_t<kMaxHeads, 2>(p, q, k, v, o, lse, stream);
-  }
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, 1>(p, q, k, v, o, lse, stream);
-  return launch_t<kMaxHeads, 1>(p, q, k, v, o, lse, stream);
+  return p.cls ? launch_cls<true>(p, q, k, v, o, lse, stream)
+               : launch_cls<false>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace fibatt

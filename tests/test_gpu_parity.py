@@ -274,6 +274,11 @@ CLS = [
     ("bf16 N33 H17", 2, 17, 33, 64, torch.bfloat16, None, None),
     ("bf16 N198 (ViT forward, general backward)", 1, 4, 198, 64, torch.bfloat16, None, None),
     ("bf16 N256 H5", 1, 5, 256, 64, torch.bfloat16, None, None),
+    # tile kernels (bf16, longer sequences)
+    ("bf16 N1569 H12 quarter windows", 1, 12, 1569, 64, torch.bfloat16, None,
+     [393 + 97 * h for h in range(12)]),
+    ("bf16 N4097 H4", 1, 4, 4097, 64, torch.bfloat16, None, None),
+    ("bf16 d128 N1500 H16", 1, 16, 1500, 128, torch.bfloat16, None, None),
 ]
 
 

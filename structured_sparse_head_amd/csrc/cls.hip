@@ -448,6 +448,10 @@ hipError_t launch_fwd_cls(const Problem& p0, const void* q, const void* k, const
   p.cls = true;
   hipError_t e = launch_fwd(p, q, k, v, o, lse, stream, path);
   if (e != hipSuccess) return e;
+  // launch_fwd picks the persistent ViT kernel first; that kernel computes
+  // the dense row itself when the sequence leaves it a wave without rows.
+  if (path == Path::kAuto && fwd_slab_bf16_fits(p) && fwd_slab_bf16_dense_row(p))
+    return hipSuccess;
   ClsArgs a = make_args(p);
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);

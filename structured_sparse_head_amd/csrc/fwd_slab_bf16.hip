@@ -32,8 +32,11 @@
 //    committed to LDS after the next barrier (Q too, so that no prefetch
 //    register is carried across the loop).
 //  * Class-token mask (CLS): a row j >= 1 whose distance j to token 0 is not
-//    a head distance scores key 0 as one more key, like the diagonal; row 0
-//    is replaced afterwards by the dense class-token row kernel.
+//    a head distance scores key 0 as one more key, like the diagonal.  Row 0
+//    attends every key: for N <= 240 at least one wave has no rows of its
+//    own, and the first such wave computes that dense row from the slab in
+//    LDS (the wave that owns row 0 then stores nothing for it); for longer
+//    sequences the dense class-token row kernel replaces row 0 afterwards.
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -192,6 +195,88 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int
   }
 }
 
+// Dense class-token row for one slab, by one wave: slot l % 16 of the lane
+// takes keys slot, slot + 16, ... (N <= 240: at most 15 each) with an online
+// softmax, with the same lane parts as a row block.  The slots are then
+// combined: a common maximum over the 16 slots (lane bits 0..3), the sums
+// rescaled to it, and a lane's P V fragment summed over the 16 lanes that
+// hold the same part, which are l ^ x for x in the span of 1, 2, 12 and 20
+// (flipping bits 2 and 3 together, or bits 2 and 4, keeps the part).
+constexpr int kDenseSlots = 15;
+
+__device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+template <typename A>
+__device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane,
+                                           const char* lds_k, const char* lds_v,
+                                           const char* lds_q, const Prefetch& pf) {
+  const int slot = lane & 15;
+  const int part = lane_part(lane);
+  uint32_t qw[8];
+  {
+    u32x4 qf[2];
+    load_bf16_q(lds_q + part * 32, 0, qf);
+    qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
+    qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
+  }
+  const float c = a.scale_log2;
+  float m = -INFINITY, l = 0.f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll 1
+  for (int t = 0; t < kDenseSlots; ++t) {  // uniform trip count; keys past N score -inf
+    const int k = slot + 16 * t;
+    const int kc = clamp_row(k, N);
+    u32x4 kf[2];
+    load_bf16_q(lds_k + part * 32, kc, kf);
+    const float x = dot_q(qw, kf);
+    const float sk = k < N ? x : -INFINITY;
+    const float mn = fmaxf(m, sk);
+    // A slot with no key yet (N < 16) keeps m = -inf: both exponentials
+    // would see -inf - (-inf), so they are chosen explicitly.
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2((m - mn) * c);
+    const float p = mn == -INFINITY ? 0.f : fast_exp2((sk - mn) * c);  // 0 for sk = -inf
+    u32x4 vf[4];
+    load_f32_q(lds_v + part * 64, kc, vf);
+    l = __builtin_fmaf(l, alpha, p);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] *= alpha;
+    axpy_q(o, p, vf);
+    m = mn;
+  }
+  float mw = m;
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) mw = fmaxf(mw, wave_xor(mw, x));  // key 0 exists: finite
+  const float sc = m == -INFINITY ? 0.f : fast_exp2((m - mw) * c);
+  l *= sc;
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) l += wave_xor(l, x);
+  constexpr int kSpan[4] = {1, 2, 12, 20};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] *= sc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] += wave_xor(o[e], kSpan[i]);
+  const float inv = 1.0f / l;
+  uint32_t w[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
+    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
+    w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  settle(pf);
+  if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
+    u32x4* orow = reinterpret_cast<u32x4*>(a.o + static_cast<size_t>(slab) * N * kRowBytes);
+    orow[part] = u32x4{w[0], w[1], w[2], w[3]};
+    orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
+    if (lane == 0) a.lse[static_cast<size_t>(slab) * N] = (mw * c + fast_log2(l)) * kLn2;
+  }
+}
+
 // One slab for an active wave (its first row is < N).  Lanes past the last
 // row repeat row N - 1 and store the same values, so the stores need no
 // branch and the memory wait counter stays exact around the loop.
@@ -284,9 +369,12 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   settle(pf);
   const size_t grow = static_cast<size_t>(slab) * N + rr;
   u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes);
-  orow[part] = u32x4{w[0], w[1], w[2], w[3]};
-  orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
-  a.lse[grow] = lse;  // the row's four lanes write the same value
+  // With the class-token mask row 0 is the dense wave's (N <= 240).
+  if (!(CLS && rr == 0 && N <= 16 * kDenseSlots)) {
+    orow[part] = u32x4{w[0], w[1], w[2], w[3]};
+    orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
+    a.lse[grow] = lse;  // the row's four lanes write the same value
+  }
 }
 
 template <int MH, bool CLS>
@@ -329,6 +417,8 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
       attend_slab<CLS>(a, slab, N, row, part, slot, r0, lds_k, lds_v, lds_q, pf);
     }
   } else {
+    // The first wave without rows computes the class-token row (N <= 240).
+    const bool dense = CLS && r0 == 16 * ((a.N + 15) / 16);
     for (; slab < a.slabs; slab += gridDim.x) {
       int N = a.N;
       asm volatile("" : "+s"(N));
@@ -338,6 +428,9 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
       __syncthreads();
       const int next = slab + gridDim.x;
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
+      if (dense)
+        dense_row0(a, slab, N, lane, smem, smem + N * kBf16Stride,
+                   smem + N * (kBf16Stride + kF32Stride), pf);
     }
   }
 }
@@ -371,6 +464,8 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
 }
 
 }  // namespace
+
+bool fwd_slab_bf16_dense_row(const Problem& p) { return p.N <= 16 * kDenseSlots; }
 
 bool fwd_slab_bf16_fits(const Problem& p) {
   return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kRowsF && records_fit(p);

@@ -50,6 +50,8 @@ bool fwd_slab_fits(const Problem& p);
 
 // Persistent forward for bf16, d_h = 64, N <= 256 (the default when it fits).
 bool fwd_slab_bf16_fits(const Problem& p);
+// Whether that kernel also computes the dense class-token row (N <= 240).
+bool fwd_slab_bf16_dense_row(const Problem& p);
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream);
 // Forward for bf16, d_h = 64 and any N, query tiles read from global memory

@@ -272,6 +272,9 @@ CLS = [
     ("bf16 N150 diag windows", 2, 3, 150, 64, torch.bfloat16, ([0, 3, 5], [1, 3, 1]),
      [150, 40, 3]),
     ("bf16 N33 H17", 2, 17, 33, 64, torch.bfloat16, None, None),
+    ("bf16 N13 (slots without keys)", 3, 4, 13, 64, torch.bfloat16, None, None),
+    ("bf16 N240 H6 (last fused size)", 1, 6, 240, 64, torch.bfloat16, None, None),
+    ("bf16 N241 H6", 1, 6, 241, 64, torch.bfloat16, None, None),
     ("bf16 N198 (ViT forward, general backward)", 1, 4, 198, 64, torch.bfloat16, None, None),
     ("bf16 N256 H5", 1, 5, 256, 64, torch.bfloat16, None, None),
     # tile kernels (bf16, longer sequences)

@@ -282,6 +282,8 @@ CLS = [
      [393 + 97 * h for h in range(12)]),
     ("bf16 N4097 H4", 1, 4, 4097, 64, torch.bfloat16, None, None),
     ("bf16 d128 N1500 H16", 1, 16, 1500, 128, torch.bfloat16, None, None),
+    ("bf16 N700 H20 modified", 1, 20, 700, 64, torch.bfloat16, "modified", None),
+    ("bf16 N120 H24 modified", 2, 24, 120, 64, torch.bfloat16, "modified", None),
 ]
 
 
@@ -295,6 +297,8 @@ def test_cls_mask(case, path):
     _set_path(path)
     try:
         inp = workloads.random_case(4321 + N, B, H, N, d, dtype)
+        if ab == "modified":
+            ab = fa.wythoff_rows(H, modified=True)
         a, b, w, F = _heads(H, N, w=w, ab=ab)
         gpu = _gpu_run(inp, a, b, w, cls=True)
         assert torch.isfinite(gpu["lse"]).all()
@@ -391,6 +395,11 @@ TABLES = [
      False),
     ("bf16 N197 exponential class token", 2, 197, 64, torch.bfloat16,
      [[1, 2, 4, 8, 16, 32, 64, 128], [6, 12, 24, 48, 96]], True),
+    ("bf16 N900 class token 18 heads", 1, 900, 64, torch.bfloat16,
+     [[3 * (h + 1) * 2 ** i for i in range(6) if 3 * (h + 1) * 2 ** i < 900] for h in range(18)],
+     True),
+    ("fp32 N70 class token random sets", 2, 70, 128, torch.float32,
+     [sorted(_rng_sets.choice(70, size=s, replace=False).tolist()) for s in (0, 3, 30)], True),
 ]
 
 

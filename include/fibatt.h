@@ -159,7 +159,8 @@ int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k,
  *
  * Workspace: fibatt_fwd_cls_workspace_floats(desc) fp32 elements (0 when N
  * <= 1024, and then `workspace` may be NULL), fibatt_bwd_cls_workspace_floats
- * (desc) for the backward (B*H*(N + d_h), plus partial sums when N > 1024).  Both
+ * (desc) for the backward (B*H*(N + d_h) + d_h, plus partial sums when
+ * N > 1024).  Both
  * return -1 for an invalid descriptor.  Contents on entry are ignored. */
 int64_t fibatt_fwd_cls_workspace_floats(const fibatt_desc* desc);
 int64_t fibatt_bwd_cls_workspace_floats(const fibatt_desc* desc);

@@ -42,9 +42,15 @@
 // met by query 0 (one more term of dK_j and dV_j).  The latter needs Q_0,
 // dO_0, LSE_0 and the dense D_0, which the class-token row kernel has left in
 // the workspace before this kernel runs; Q_0 and dO_0 are staged in LDS by
-// the lanes of row 0.  Row 0's own D is that dense D_0; its dQ and key 0's
-// dK and dV are replaced by the dense class-token kernels afterwards.  Every
-// D_j goes to the workspace for the column kernel.
+// the lanes of row 0.  Row 0's own D is that dense D_0.  Key 0 is met by
+// every query: each row leaves its pair with token 0, (P_j0, dS_j0 / sqrt(d)),
+// in LDS (or it is already a table entry when j is a head distance), and in
+// the key passes the first wave without rows of its own sums
+// dV_0 = sum_j P_j0 dO_j and dK_0 = sum_j dS_j0 Q_j / sqrt(d) from the fp32
+// Q and dO rows, and copies the row kernel's dQ_0 into place.  The lanes of
+// row 0 send their own dQ, dK and dV stores to a discard row instead.  The
+// class-token areas live in table rows no lane uses: lanes own table rows
+// below 16 ceil(N / 16) <= 208.
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -64,12 +70,14 @@ constexpr int kGroups = (kMaxPos + 3) / 4;   // distance groups of four in the q
 // the last sequence row own private rows.
 constexpr int kLdsPerRow = 2 * kBf16Stride + kF32Stride;  // >= 2 * kF32Stride
 constexpr int kTableBytes = kRowsB * kTableCols * 8;
-// Class-token mask: bf16 Q_0 and dO_0, then (P, dS / sqrt(d)) of every lane
-// group's row paired with query 0.
-constexpr int kStageBytes = 256 + kRowsB * 8;
 constexpr int kLdsMax = 160 * 1024;
-constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;                   // 201
-constexpr int kMaxRowsBwdCls = (kLdsMax - kTableBytes - kStageBytes) / kLdsPerRow;  // 197
+constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 201
+// Class-token areas, from table row kClsRow on: bf16 Q_0 and dO_0 (256
+// bytes), then per row its pair with query 0 as key ("side") and its pair
+// with key 0 as query ("colv"), (P, dS / sqrt(d)) each.
+constexpr int kClsRow = 16 * ((kMaxRowsBwd + 15) / 16);  // 208
+static_assert(kClsRow * kTableCols * 8 + 256 + 2 * kRowsB * 8 <= kTableBytes,
+              "class-token areas must fit in the unused table rows");
 
 template <int MH>
 struct Args {
@@ -82,6 +90,8 @@ struct Args {
   float* dk;
   float* dv;
   float* ws;    // class-token mask: D per row (D_0 read, every D_j written)
+  const float* dq0;  // class-token mask: row kernel's dQ_0 per slab
+  float* discard;    // class-token mask: 64 floats that row 0's own stores go to
   int H;
   int N;
   int slabs;
@@ -250,19 +260,24 @@ __device__ __forceinline__ void query_pass(const char* lds_k, const char* lds_v,
 }
 
 // dQ pass: dS = P (dP - D) from the row's table entries, acc += dS K; the
-// entry becomes (P, dS / sqrt(d)) for the key pass.
+// entry becomes (P, dS / sqrt(d)) for the key pass.  With the class-token
+// mask (colv set) the entry of displacement -row, whose key is token 0, is
+// also copied to colv[row].
 template <int SGN>
 __device__ __forceinline__ void dq_pass(const char* lds_kf, float2* tbl, Dist dist, int n, int row,
                                         int trow, int N, int part, float d, float scale, int base,
-                                        bool wr, float (&acc)[16]) {
+                                        bool wr, float (&acc)[16], float2* colv = nullptr) {
   float2* e0 = tbl + trow * kTableCols + base;
   for (int i = 0; i < n; ++i) {
+    const int f = dist.at(i);
     u32x4 kf[4];
-    load_f32_q(lds_kf + part * 64, clamp_row(row + SGN * dist.at(i), N), kf);
+    load_f32_q(lds_kf + part * 64, clamp_row(row + SGN * f, N), kf);
     const float2 e = e0[i];
     const float ds = e.x * (e.y - d);
     axpy_q(acc, ds, kf);
-    if (wr) e0[i] = make_float2(e.x, ds * scale);
+    const float2 r = make_float2(e.x, ds * scale);
+    if (wr) e0[i] = r;
+    if (SGN < 0 && colv && wr && f == row) colv[row] = r;
   }
 }
 
@@ -299,6 +314,67 @@ __device__ __forceinline__ void key_pass(const char* lds_x, const float2* tbl, D
   for (; i < n; ++i) step(i);
 }
 
+// Column 0 of the class-token mask for one slab, by one wave in the key
+// passes: slot l % 16 of the lane takes queries slot, slot + 16, ... (N <=
+// 208: at most 13 each) with the lane parts of a row block; each query's
+// (P_j0, dS_j0 / sqrt(d)) is in colv, left there by its row.  A lane's sums
+// are completed over the 16 lanes that hold the same part (lane l ^ x, x in
+// the span of 1, 2, 12 and 20), and the lanes of slot 0 store the row, and
+// copy dQ_0 into place.
+constexpr int kColSlots = kClsRow / 16;  // 13
+
+__device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+template <typename A>
+__device__ __forceinline__ void dense_col0(const A& a, int slab, int N, int lane, char* smem) {
+  const char* lds_q = smem;
+  const char* lds_do = smem + N * kF32Stride;
+  const float2* tbl = reinterpret_cast<const float2*>(smem + N * kLdsPerRow);
+  const float2* colv =
+      reinterpret_cast<const float2*>(reinterpret_cast<const char*>(tbl + kClsRow * kTableCols) +
+                                      256) + kRowsB;
+  const int slot = lane & 15;
+  const int part = lane_part(lane);
+  const size_t r0 = static_cast<size_t>(slab) * N * 64;
+  // One output row at a time (dV_0 from dO, then dK_0 from Q), to keep
+  // registers for the prefetch of the next slab.
+  auto column = [&](const char* lds_x, bool second, float* out) {
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 1
+    for (int t = 0; t < kColSlots; ++t) {
+      const int j = slot + 16 * t;
+      const int jc = clamp_row(j, N);
+      const float2 e = colv[jc];
+      const float w = j < N ? (second ? e.y : e.x) : 0.f;
+      u32x4 xb[4];
+      load_f32_q(lds_x + part * 64, jc, xb);
+      axpy_q(acc, w, xb);
+    }
+    constexpr int kSpan[4] = {1, 2, 12, 20};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += wave_xor(acc[e], kSpan[s]);
+    if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
+      float4* p = reinterpret_cast<float4*>(out + r0) + part;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        p[4 * t] = make_float4(acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]);
+    }
+  };
+  column(lds_do, false, a.dv);
+  column(lds_q, true, a.dk);
+  if (slot == 0) {
+    float4* pq = reinterpret_cast<float4*>(a.dq + r0) + part;
+    const float4* sq =
+        reinterpret_cast<const float4*>(a.dq0 + static_cast<size_t>(slab) * 64) + part;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pq[4 * t] = sq[4 * t];
+  }
+}
+
 template <int MH, bool CLS>
 __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -321,6 +397,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   // Waves whose rows all lie past the sequence only help stage the slabs;
   // they run a loop of their own with the same barriers.
   if (r0 >= a.N) {
+    // With the class-token mask the first wave without rows sums column 0.
+    const bool dense = CLS && r0 == 16 * ((a.N + 15) / 16);
     for (; slab < a.slabs; slab += gridDim.x) {
       int N = a.N;
       asm volatile("" : "+s"(N));
@@ -332,6 +410,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       settle(pf);
       __syncthreads();
       __syncthreads();
+      if (dense) dense_col0(a, slab, N, lane, smem);
     }
     return;
   }
@@ -349,8 +428,9 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     char* lds_q = smem;
     char* lds_do = smem + N * kF32Stride;
     float2* tbl = reinterpret_cast<float2*>(smem + N * kLdsPerRow);
-    char* lds_r0 = smem + N * kLdsPerRow + kTableBytes;  // CLS: Q_0 then dO_0, bf16
+    char* lds_r0 = reinterpret_cast<char*>(tbl + kClsRow * kTableCols);  // CLS: Q_0, dO_0
     float2* side = reinterpret_cast<float2*>(lds_r0 + 256);  // CLS: row's pair with query 0
+    float2* colv = side + kRowsB;                             // CLS: row's pair with key 0
     // Lanes past the last row repeat row N - 1 exactly (their extra terms
     // are exact zeros; their table rows are private), so every lane and wave
     // runs the same code and stores without branches: the memory wait
@@ -444,13 +524,19 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         load_bf16_q(lds_v + part * 32, 0, vb);
         const float s = dot_q(qw, kb);
         dpq = dot_q(dw, vb);
-        pq = need0 ? fast_exp2(__builtin_fmaf(s, a.c, -lse2)) : 0.f;
+        const float p0 = fast_exp2(__builtin_fmaf(s, a.c, -lse2));
+        pq = need0 ? p0 : 0.f;
         d = rr == 0 ? a.ws[r0g] : __builtin_fmaf(pq, dpq, d);  // row 0: the dense D_0
+        // This row's pair with key 0 for the column sum (a head distance's
+        // pair is copied from the table after the dQ pass instead).
+        if (wr && mine && (need0 || (rr == 0 && !has0)))
+          colv[rr] = make_float2(p0, p0 * (dpq - d) * a.scale);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqa[e] = 0.f;
       dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, dqa);
-      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, dqa);
+      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, dqa,
+                  CLS ? colv : nullptr);
       if (has0) {
         u32x4 kf[4];
         load_f32_q(lds_kf + part * 64, rr, kf);
@@ -458,6 +544,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         const float ds = e.x * (e.y - d);
         axpy_q(dqa, ds, kf);
         if (wr) tbl[row * kTableCols + z] = make_float2(e.x, ds * a.scale);
+        if (CLS && wr && rr == 0) colv[0] = make_float2(e.x, ds * a.scale);
       }
       if constexpr (CLS) {
         u32x4 kf[4];
@@ -481,7 +568,12 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       // Key k, displacement +f: query k - f exists while k >= f (f <= wl for
       // some key of the wave); displacement -f: query k + f < N.
       // dQ is written during the dV pass and dV during the dK pass.
-      const Pending pq{reinterpret_cast<float4*>(a.dq + grow * 64) + part, dqa, a.scale};
+      // With the class-token mask row 0's results come from elsewhere.
+      const bool drop = CLS && rr == 0;
+      float* dq_row = drop ? a.discard : a.dq + grow * 64;
+      float* dv_row = drop ? a.discard : a.dv + grow * 64;
+      float* dk_row = drop ? a.discard : a.dk + grow * 64;
+      const Pending pq{reinterpret_cast<float4*>(dq_row) + part, dqa, a.scale};
       float acc[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -497,7 +589,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         load_f32_q(lds_do + part * 64, 0, xb);
         axpy_q(acc, side[rr].x, xb);
       }
-      const Pending pv{reinterpret_cast<float4*>(a.dv + grow * 64) + part, acc, 1.0f};
+      const Pending pv{reinterpret_cast<float4*>(dv_row) + part, acc, 1.0f};
       float acc2[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc2[e] = 0.f;
@@ -513,7 +605,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         load_f32_q(lds_q + part * 64, 0, xb);
         axpy_q(acc2, side[rr].y, xb);
       }
-      float4* dk = reinterpret_cast<float4*>(a.dk + grow * 64) + part;
+      float4* dk = reinterpret_cast<float4*>(dk_row) + part;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         dk[4 * t] = make_float4(acc2[4 * t], acc2[4 * t + 1], acc2[4 * t + 2], acc2[4 * t + 3]);
@@ -524,7 +616,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
 template <int MH, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                    float* ws, hipStream_t stream) {
+                    float* ws, float* dq0, float* discard, hipStream_t stream) {
   Args<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
@@ -535,6 +627,8 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.dk = dk;
   a.dv = dv;
   a.ws = ws;
+  a.dq0 = dq0;
+  a.discard = discard;
   a.H = p.H;
   a.N = p.N;
   a.slabs = p.B * p.H;
@@ -542,12 +636,11 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.c = kLog2e * 0.125f;
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
   a.blocks = plan_blocks(p.N, p.H, a.rec);
-  constexpr int kStage = CLS ? kStageBytes : 0;
-  const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes + kStage;
+  const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes;
   auto kern = bwd_slab_bf16_kernel<MH, CLS>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (CLS ? kMaxRowsBwdCls : kMaxRowsBwd) * kLdsPerRow + kTableBytes + kStage);
+      kMaxRowsBwd * kLdsPerRow + kTableBytes);
   if (attr != hipSuccess) return attr;
   const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
@@ -558,21 +651,25 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
 }  // namespace
 
 bool bwd_slab_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= (p.cls ? kMaxRowsBwdCls : kMaxRowsBwd) &&
-         records_fit(p);
+  return p.dtype == DType::kBF16 && p.D == 64 && p.N <= kMaxRowsBwd && records_fit(p);
 }
 
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
-                                float* dv, float* ws, hipStream_t stream) {
+                                float* dv, float* ws, float* dq0, float* discard,
+                                hipStream_t stream) {
   if (p.cls) {
     if (p.H <= kSmallHeads)
-      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, dq0, discard,
+                                         stream);
+    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, dq0, discard,
+                                     stream);
   }
   if (p.H <= kSmallHeads)
-    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, nullptr, nullptr,
+                                        stream);
+  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, nullptr, nullptr,
+                                    stream);
 }
 
 }  // namespace fibatt

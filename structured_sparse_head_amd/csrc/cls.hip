@@ -16,7 +16,8 @@
 //    workspace, because the main kernels may write row 0 of dQ);
 //  * backward column 0: dV_0 = sum_j P_j0 dO_j, dK_0 = sum_j dS_j0 Q_j
 //    (launched last, with every D_j in the workspace; it also copies dQ_0
-//    into place).
+//    into place).  The persistent ViT backward kernel does this part
+//    itself, from the slab in LDS.
 // A slab's N rows are split into ranges of kSplitRows; one workgroup reduces
 // one range (each lane group walks every NG-th row of it and the groups are
 // combined in LDS in a fixed order), and with more than one range a second
@@ -439,7 +440,7 @@ int64_t fwd_cls_workspace_floats(const Problem& p) {
 int64_t bwd_cls_workspace_floats(const Problem& p) {
   const int s = cls_splits(p);
   const int64_t slabs = static_cast<int64_t>(p.B) * p.H;
-  return slabs * (p.N + p.D) + (s > 1 ? slabs * s * (2 * p.D + 1) : 0);
+  return slabs * (p.N + p.D) + p.D + (s > 1 ? slabs * s * (2 * p.D + 1) : 0);
 }
 
 hipError_t launch_fwd_cls(const Problem& p0, const void* q, const void* k, const void* v,
@@ -477,13 +478,16 @@ hipError_t launch_bwd_cls(const Problem& p0, const void* q, const void* k, const
   a.dk = dk;
   a.dv = dv;
   a.ws_d = ws;
-  a.dq0 = ws + static_cast<size_t>(p.B) * p.H * p.N;
-  a.part = a.dq0 + static_cast<size_t>(p.B) * p.H * p.D;
+  a.dq0 = cls_dq0(p, ws);
+  a.part = cls_discard(p, ws) + p.D;
   // Row 0 first: the key pass of the general kernels needs D_0.
   hipError_t e = bwd_row(p, a, stream);
   if (e != hipSuccess) return e;
   e = launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
   if (e != hipSuccess) return e;
+  // launch_bwd picks the persistent ViT kernel first; that kernel sums
+  // column 0 itself (and writes dQ_0).
+  if (path == Path::kAuto && bwd_slab_bf16_fits(p)) return hipSuccess;
   // Column 0 last: it needs every D_j.
   return bwd_col(p, a, stream);
 }

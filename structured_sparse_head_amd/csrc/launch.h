@@ -74,6 +74,14 @@ hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, 
 // Dense rows are reduced in ranges of kSplitRows rows per workgroup.
 constexpr int kSplitRows = 1024;
 int cls_splits(const Problem& p);
+// Backward workspace with the class-token mask: D per row [B*H*N], the row
+// kernel's dQ_0 per slab [B*H*D], one discard row [D], then range partials.
+inline float* cls_dq0(const Problem& p, float* ws) {
+  return ws + static_cast<size_t>(p.B) * p.H * p.N;
+}
+inline float* cls_discard(const Problem& p, float* ws) {
+  return cls_dq0(p, ws) + static_cast<size_t>(p.B) * p.H * p.D;
+}
 int64_t fwd_cls_workspace_floats(const Problem& p);
 int64_t bwd_cls_workspace_floats(const Problem& p);
 hipError_t launch_fwd_cls(const Problem& p, const void* q, const void* k, const void* v,
@@ -86,6 +94,7 @@ hipError_t launch_bwd_cls(const Problem& p, const void* q, const void* k, const 
 bool bwd_slab_bf16_fits(const Problem& p);
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
-                                float* dv, float* ws, hipStream_t stream);
+                                float* dv, float* ws, float* dq0, float* discard,
+                                hipStream_t stream);
 
 }  // namespace fibatt

@@ -180,6 +180,12 @@ struct Dist {
     for (int i = 0; i < n; ++i) found |= at(i) == j;
     return found;
   }
+  // Position of distance j among the first n, or -1.
+  __device__ __forceinline__ int index(int j, int n) const {
+    int k = -1;
+    for (int i = 0; i < n; ++i) k = at(i) == j ? i : k;
+    return k;
+  }
 };
 
 // Per-head record handed to the kernels in their arguments: bytes 0..11 are

@@ -260,11 +260,11 @@ def test_cls_entry_points_reject_bad_arguments():
 def test_cls_workspace_sizes():
     c = _Case()   # B=2, H=3, N=65, d_h=64: one range per slab
     assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(c.desc)) == 0
-    assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(c.desc)) == 2 * 3 * (65 + 64)
+    assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(c.desc)) == 2 * 3 * (65 + 64) + 64
     big = _Case(N=2049, w=[2049] * 3, d_h=128)   # three ranges of 1024 rows
     assert fa.lib().fibatt_fwd_cls_workspace_floats(ctypes.byref(big.desc)) == 6 * 3 * 130
     assert fa.lib().fibatt_bwd_cls_workspace_floats(ctypes.byref(big.desc)) == \
-        6 * (2049 + 128) + 6 * 3 * 257
+        6 * (2049 + 128) + 128 + 6 * 3 * 257
 
 
 # --------------------------------------------------------------------------

@@ -415,8 +415,7 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
                       float* ws, hipStream_t stream, Path path) {
   if (path == Path::kAuto && bwd_slab_bf16_fits(p))
-    return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws,
-                                p.cls ? cls_dq0(p, ws) : nullptr,
+    return launch_bwd_slab_bf16(p, q, k, v, lse, dout, dq, dk, dv,
                                 p.cls ? cls_discard(p, ws) : nullptr, stream);
   if (path == Path::kAuto && bwd_tile_bf16_fits(p))
     return launch_bwd_tile_bf16(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);

@@ -39,18 +39,18 @@
 // Class-token mask (CLS): a row j >= 1 whose distance j to token 0 is not a
 // head distance pairs with token 0 in both roles.  As query j it meets key 0
 // (one more term of D_j and dQ_j, with K_0 and V_0 from LDS); as key j it is
-// met by query 0 (one more term of dK_j and dV_j).  The latter needs Q_0,
-// dO_0, LSE_0 and the dense D_0, which the class-token row kernel has left in
-// the workspace before this kernel runs; Q_0 and dO_0 are staged in LDS by
-// the lanes of row 0.  Row 0's own D is that dense D_0.  Key 0 is met by
-// every query: each row leaves its pair with token 0, (P_j0, dS_j0 / sqrt(d)),
-// in LDS (or it is already a table entry when j is a head distance), and in
-// the key passes the first wave without rows of its own sums
-// dV_0 = sum_j P_j0 dO_j and dK_0 = sum_j dS_j0 Q_j / sqrt(d) from the fp32
-// Q and dO rows, and copies the row kernel's dQ_0 into place.  The lanes of
-// row 0 send their own dQ, dK and dV stores to a discard row instead.  The
-// class-token areas live in table rows no lane uses: lanes own table rows
-// below 16 ceil(N / 16) <= 208.
+// met by query 0 (one more term of dK_j and dV_j, from Q_0 and dO_0, which
+// the lanes of row 0 stage in LDS, and the dense D_0).  Row 0 and column 0
+// are dense, and two of the waves without rows of their own (there are at
+// least three for N <= 201) compute them from the slab in LDS: during the
+// query passes one takes row 0 (D_0, dQ_0 and row 0's table entries for the
+// key passes); during the key passes the other sums column 0,
+// dV_0 = sum_j P_j0 dO_j and dK_0 = sum_j dS_j0 Q_j / sqrt(d), from the fp32
+// Q and dO rows and each row's pair with token 0, which the rows leave in
+// LDS.  The lanes of row 0 then only stage Q_0 and dO_0: their table row is
+// a discard row and their dQ, dK and dV stores go to a discard row of the
+// workspace.  The class-token areas live in table rows no lane uses (lanes
+// own table rows below 16 ceil(N / 16) <= 208).
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -73,10 +73,14 @@ constexpr int kTableBytes = kRowsB * kTableCols * 8;
 constexpr int kLdsMax = 160 * 1024;
 constexpr int kMaxRowsBwd = (kLdsMax - kTableBytes) / kLdsPerRow;  // 201
 // Class-token areas, from table row kClsRow on: bf16 Q_0 and dO_0 (256
-// bytes), then per row its pair with query 0 as key ("side") and its pair
-// with key 0 as query ("colv"), (P, dS / sqrt(d)) each.
+// bytes), then per row its key-role pair with query 0, (P, dP) ("side"),
+// its pair with key 0 as query, (P, dS / sqrt(d)) ("colv"), D_0, and row 0's
+// (P, dP) per key.  Table row kDiscardRow takes the table writes of row 0's
+// own lanes.
 constexpr int kClsRow = 16 * ((kMaxRowsBwd + 15) / 16);  // 208
-static_assert(kClsRow * kTableCols * 8 + 256 + 2 * kRowsB * 8 <= kTableBytes,
+constexpr int kClsBytes = 256 + 2 * kRowsB * 8 + 16 + kRowsB * 8;
+constexpr int kDiscardRow = kRowsB - 1;
+static_assert(kClsRow * kTableCols * 8 + kClsBytes <= kDiscardRow * kTableCols * 8,
               "class-token areas must fit in the unused table rows");
 
 template <int MH>
@@ -89,9 +93,7 @@ struct Args {
   float* dq;
   float* dk;
   float* dv;
-  float* ws;    // class-token mask: D per row (D_0 read, every D_j written)
-  const float* dq0;  // class-token mask: row kernel's dQ_0 per slab
-  float* discard;    // class-token mask: 64 floats that row 0's own stores go to
+  float* discard;  // class-token mask: 64 floats that row 0's own lanes store to
   int H;
   int N;
   int slabs;
@@ -366,12 +368,104 @@ __device__ __forceinline__ void dense_col0(const A& a, int slab, int N, int lane
   };
   column(lds_do, false, a.dv);
   column(lds_q, true, a.dk);
-  if (slot == 0) {
-    float4* pq = reinterpret_cast<float4*>(a.dq + r0) + part;
-    const float4* sq =
-        reinterpret_cast<const float4*>(a.dq0 + static_cast<size_t>(slab) * 64) + part;
+}
+
+// Class-token LDS areas (see kClsRow).
+struct ClsLds {
+  float2* side;  // per row: (P, dP) with query 0
+  float2* colv;  // per row: (P, dS / sqrt(d)) with key 0
+  float* d0;     // D_0
+  float2* ppd;   // per key: (P_0k, dP_0k)
+  __device__ ClsLds(char* smem, int N) {
+    char* base = smem + N * kLdsPerRow + kClsRow * kTableCols * 8 + 256;
+    side = reinterpret_cast<float2*>(base);
+    colv = side + kRowsB;
+    d0 = reinterpret_cast<float*>(colv + kRowsB);
+    ppd = reinterpret_cast<float2*>(d0 + 4);
+  }
+};
+
+// Row 0 of the class-token mask for one slab, by one wave during the query
+// passes (same slots and parts as dense_col0): D_0 = sum_k P_0k dP_0k over
+// all keys, keeping each key's (P_0k, dP_0k) in LDS, then dQ_0 =
+// sum_k dS_0k K_k / sqrt(d) in a second sweep that also writes row 0's table
+// entries (P, dS / sqrt(d)) for the keys at head distances, the diagonal and
+// colv[0], and finally D_0 for the key passes.
+template <typename A>
+__device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane, char* smem) {
+  const char* lds_k = smem;
+  const char* lds_v = smem + N * kBf16Stride;
+  const char* lds_kf = smem + 2 * N * kBf16Stride;
+  float2* tbl = reinterpret_cast<float2*>(smem + N * kLdsPerRow);
+  const char* lds_r0 = reinterpret_cast<const char*>(tbl + kClsRow * kTableCols);
+  const ClsLds cl(smem, N);
+  const u32x4 rec = a.rec[slab % a.H];
+  const Dist dist{rec.x, rec.y, rec.z};
+  const int npos = static_cast<int>(rec.w & 0xffu);
+  const bool has0 = ((rec.w >> 8) & 0xffu) != 0;
+  const int slot = lane & 15;
+  const int part = lane_part(lane);
+  uint32_t q0w[8], d0w[8];
+  {
+    const u32x4 q0 = *reinterpret_cast<const u32x4*>(lds_r0 + part * 32);
+    const u32x4 q1 = *reinterpret_cast<const u32x4*>(lds_r0 + part * 32 + 16);
+    const u32x4 o0 = *reinterpret_cast<const u32x4*>(lds_r0 + 128 + part * 32);
+    const u32x4 o1 = *reinterpret_cast<const u32x4*>(lds_r0 + 144 + part * 32);
+    q0w[0] = q0.x; q0w[1] = q0.y; q0w[2] = q0.z; q0w[3] = q0.w;
+    q0w[4] = q1.x; q0w[5] = q1.y; q0w[6] = q1.z; q0w[7] = q1.w;
+    d0w[0] = o0.x; d0w[1] = o0.y; d0w[2] = o0.z; d0w[3] = o0.w;
+    d0w[4] = o1.x; d0w[5] = o1.y; d0w[6] = o1.z; d0w[7] = o1.w;
+  }
+  const float lse2 = a.lse[static_cast<size_t>(slab) * N] * kLog2e;
+  float d0 = 0.f;
+#pragma unroll 1
+  for (int t = 0; t < kColSlots; ++t) {
+    const int k = slot + 16 * t;
+    const int kc = clamp_row(k, N);
+    u32x4 kb[2], vb[2];
+    load_bf16_q(lds_k + part * 32, kc, kb);
+    load_bf16_q(lds_v + part * 32, kc, vb);
+    const float s = dot_q(q0w, kb);
+    const float dp = dot_q(d0w, vb);
+    const float p = k < N ? fast_exp2(__builtin_fmaf(s, a.c, -lse2)) : 0.f;
+    d0 = __builtin_fmaf(p, dp, d0);
+    if (part == 0) cl.ppd[k] = make_float2(p, dp);  // read back by this wave only
+  }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pq[4 * t] = sq[4 * t];
+  for (int x = 1; x < 16; x <<= 1) d0 += wave_xor(d0, x);
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 1
+  for (int t = 0; t < kColSlots; ++t) {
+    const int k = slot + 16 * t;
+    const float2 pp = cl.ppd[k];
+    const float ds = pp.x * (pp.y - d0);
+    u32x4 kf[4];
+    load_f32_q(lds_kf + part * 64, clamp_row(k, N), kf);
+    axpy_q(acc, ds, kf);
+    if (part == 0 && k < N) {  // one lane of the slot's four
+      const float2 e = make_float2(pp.x, ds * a.scale);
+      const int i = k >= 1 ? dist.index(k, npos) : -1;
+      if (i >= 0) tbl[i] = e;  // query 0, displacement +k: table row 0, column i
+      if (k == 0) {
+        cl.colv[0] = e;
+        if (has0) tbl[2 * kMaxPos] = e;
+      }
+    }
+  }
+  constexpr int kSpan[4] = {1, 2, 12, 20};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += wave_xor(acc[e], kSpan[s]);
+  if (lane == 0) *cl.d0 = d0;
+  if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
+    float4* pq = reinterpret_cast<float4*>(a.dq + static_cast<size_t>(slab) * N * 64) + part;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      pq[4 * t] = make_float4(acc[4 * t] * a.scale, acc[4 * t + 1] * a.scale,
+                              acc[4 * t + 2] * a.scale, acc[4 * t + 3] * a.scale);
   }
 }
 
@@ -397,8 +491,10 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   // Waves whose rows all lie past the sequence only help stage the slabs;
   // they run a loop of their own with the same barriers.
   if (r0 >= a.N) {
-    // With the class-token mask the first wave without rows sums column 0.
-    const bool dense = CLS && r0 == 16 * ((a.N + 15) / 16);
+    // With the class-token mask the first wave without rows sums column 0
+    // and the second one computes row 0.
+    const bool colw = CLS && r0 == 16 * ((a.N + 15) / 16);
+    const bool roww = CLS && r0 == 16 * ((a.N + 15) / 16 + 1);
     for (; slab < a.slabs; slab += gridDim.x) {
       int N = a.N;
       asm volatile("" : "+s"(N));
@@ -406,11 +502,16 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       commit_kv(smem, smem + N * kBf16Stride, smem + 2 * N * kBf16Stride, N, tid, pf);
       __syncthreads();
       const int next = slab + gridDim.x;
+      // (Row 0 before this wave's share of the next slab's loads, so the
+      // prefetch registers are free while it runs.)
+      // (Row 0 before this wave's share of the next slab's loads, so the
+      // prefetch registers are free while it runs.)
+      if (roww) dense_row0(a, slab, N, lane, smem);
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
       settle(pf);
       __syncthreads();
       __syncthreads();
-      if (dense) dense_col0(a, slab, N, lane, smem);
+      if (colw) dense_col0(a, slab, N, lane, smem);
     }
     return;
   }
@@ -431,6 +532,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     char* lds_r0 = reinterpret_cast<char*>(tbl + kClsRow * kTableCols);  // CLS: Q_0, dO_0
     float2* side = reinterpret_cast<float2*>(lds_r0 + 256);  // CLS: row's pair with query 0
     float2* colv = side + kRowsB;                             // CLS: row's pair with key 0
+    const float* d0slot = reinterpret_cast<const float*>(colv + kRowsB);  // CLS: D_0
     // Lanes past the last row repeat row N - 1 exactly (their extra terms
     // are exact zeros; their table rows are private), so every lane and wave
     // runs the same code and stores without branches: the memory wait
@@ -496,15 +598,16 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       const float dp0k = dot_q(d0w, vb);
       const float lse2_0 = a.lse[r0g] * kLog2e;
       const float pk = need0 ? fast_exp2(__builtin_fmaf(s0k, a.c, -lse2_0)) : 0.f;
-      if (wr) side[row] = make_float2(pk, pk * (dp0k - a.ws[r0g]) * a.scale);
+      if (wr) side[row] = make_float2(pk, dp0k);  // dS needs D_0: formed in the key pass
     }
+    // Row 0's own lanes write a discard table row (the row-0 wave owns row 0).
+    const int trow = CLS && row == 0 ? kDiscardRow : row;
     float dqa[16];
-    float drow = 0.f;  // D of this row (class-token mask: to the workspace)
     {
       float d = 0.f;
-      query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, row, N, part, slot, qw, dw, a.c, lse2, 0,
+      query_pass<+1>(lds_k, lds_v, tbl, dist, n_up, rr, trow, N, part, slot, qw, dw, a.c, lse2, 0,
                      d);
-      query_pass<-1>(lds_k, lds_v, tbl, dist, n_dn, rr, row, N, part, slot, qw, dw, a.c, lse2,
+      query_pass<-1>(lds_k, lds_v, tbl, dist, n_dn, rr, trow, N, part, slot, qw, dw, a.c, lse2,
                      kMaxPos, d);
       d = quad_sum(d);
       if (has0) {
@@ -514,7 +617,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         const float s = dot_q(qw, kb);
         const float dp = dot_q(dw, vb);
         const float p = fast_exp2(__builtin_fmaf(s, a.c, -lse2));
-        if (wr) tbl[row * kTableCols + z] = make_float2(p, dp);
+        if (wr) tbl[trow * kTableCols + z] = make_float2(p, dp);
         d = __builtin_fmaf(p, dp, d);
       }
       float pq = 0.f, dpq = 0.f;
@@ -526,38 +629,35 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
         dpq = dot_q(dw, vb);
         const float p0 = fast_exp2(__builtin_fmaf(s, a.c, -lse2));
         pq = need0 ? p0 : 0.f;
-        d = rr == 0 ? a.ws[r0g] : __builtin_fmaf(pq, dpq, d);  // row 0: the dense D_0
+        d = __builtin_fmaf(pq, dpq, d);
         // This row's pair with key 0 for the column sum (a head distance's
         // pair is copied from the table after the dQ pass instead).
-        if (wr && mine && (need0 || (rr == 0 && !has0)))
+        if (wr && mine && need0)
           colv[rr] = make_float2(p0, p0 * (dpq - d) * a.scale);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqa[e] = 0.f;
-      dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, row, N, part, d, a.scale, 0, wr, dqa);
-      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, row, N, part, d, a.scale, kMaxPos, wr, dqa,
+      dq_pass<+1>(lds_kf, tbl, dist, n_up, rr, trow, N, part, d, a.scale, 0, wr, dqa);
+      dq_pass<-1>(lds_kf, tbl, dist, n_dn, rr, trow, N, part, d, a.scale, kMaxPos, wr, dqa,
                   CLS ? colv : nullptr);
       if (has0) {
         u32x4 kf[4];
         load_f32_q(lds_kf + part * 64, rr, kf);
-        const float2 e = tbl[row * kTableCols + z];
+        const float2 e = tbl[trow * kTableCols + z];
         const float ds = e.x * (e.y - d);
         axpy_q(dqa, ds, kf);
-        if (wr) tbl[row * kTableCols + z] = make_float2(e.x, ds * a.scale);
-        if (CLS && wr && rr == 0) colv[0] = make_float2(e.x, ds * a.scale);
+        if (wr) tbl[trow * kTableCols + z] = make_float2(e.x, ds * a.scale);
       }
       if constexpr (CLS) {
         u32x4 kf[4];
         load_f32_q(lds_kf + part * 64, 0, kf);
         axpy_q(dqa, pq * (dpq - d), kf);
       }
-      drow = d;
     }
     // The next slab's loads (issued a whole pass ago) complete here, before
     // any store of this slab: the wait counter retires memory operations in
     // issue order, so no later wait has to drain this slab's stores.
     settle(pf);
-    if constexpr (CLS) a.ws[grow] = drow;  // the row's four lanes write the same value
     __syncthreads();  // K and V are no longer read; the table is complete
     if (mine) {
       store_f32_q_lds(lds_q, row, part, qw);
@@ -603,7 +703,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       if constexpr (CLS) {
         u32x4 xb[4];
         load_f32_q(lds_q + part * 64, 0, xb);
-        axpy_q(acc2, side[rr].y, xb);
+        const float2 e = side[rr];
+        axpy_q(acc2, e.x * (e.y - *d0slot) * a.scale, xb);
       }
       float4* dk = reinterpret_cast<float4*>(dk_row) + part;
 #pragma unroll
@@ -616,7 +717,7 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
 template <int MH, bool CLS>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                    float* ws, float* dq0, float* discard, hipStream_t stream) {
+                    float* discard, hipStream_t stream) {
   Args<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
@@ -626,8 +727,6 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.ws = ws;
-  a.dq0 = dq0;
   a.discard = discard;
   a.H = p.H;
   a.N = p.N;
@@ -656,20 +755,15 @@ bool bwd_slab_bf16_fits(const Problem& p) {
 
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
-                                float* dv, float* ws, float* dq0, float* discard,
-                                hipStream_t stream) {
+                                float* dv, float* discard, hipStream_t stream) {
   if (p.cls) {
     if (p.H <= kSmallHeads)
-      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, dq0, discard,
-                                         stream);
-    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, ws, dq0, discard,
-                                     stream);
+      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, discard, stream);
+    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, discard, stream);
   }
   if (p.H <= kSmallHeads)
-    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, nullptr, nullptr,
-                                        stream);
-  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, ws, nullptr, nullptr,
-                                    stream);
+    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, nullptr, stream);
+  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, nullptr, stream);
 }
 
 }  // namespace fibatt

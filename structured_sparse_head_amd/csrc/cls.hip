@@ -16,8 +16,9 @@
 //    workspace, because the main kernels may write row 0 of dQ);
 //  * backward column 0: dV_0 = sum_j P_j0 dO_j, dK_0 = sum_j dS_j0 Q_j
 //    (launched last, with every D_j in the workspace; it also copies dQ_0
-//    into place).  The persistent ViT backward kernel does this part
-//    itself, from the slab in LDS.
+//    into place).
+// The persistent ViT kernels do the dense parts themselves, from the slab in
+// LDS (forward for N <= 240, backward always).
 // A slab's N rows are split into ranges of kSplitRows; one workgroup reduces
 // one range (each lane group walks every NG-th row of it and the groups are
 // combined in LDS in a fixed order), and with more than one range a second
@@ -480,14 +481,14 @@ hipError_t launch_bwd_cls(const Problem& p0, const void* q, const void* k, const
   a.ws_d = ws;
   a.dq0 = cls_dq0(p, ws);
   a.part = cls_discard(p, ws) + p.D;
+  // The persistent ViT backward kernel computes row 0 and column 0 itself.
+  if (path == Path::kAuto && bwd_slab_bf16_fits(p))
+    return launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
   // Row 0 first: the key pass of the general kernels needs D_0.
   hipError_t e = bwd_row(p, a, stream);
   if (e != hipSuccess) return e;
   e = launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, ws, stream, path);
   if (e != hipSuccess) return e;
-  // launch_bwd picks the persistent ViT kernel first; that kernel sums
-  // column 0 itself (and writes dQ_0).
-  if (path == Path::kAuto && bwd_slab_bf16_fits(p)) return hipSuccess;
   // Column 0 last: it needs every D_j.
   return bwd_col(p, a, stream);
 }

@@ -94,7 +94,6 @@ hipError_t launch_bwd_cls(const Problem& p, const void* q, const void* k, const 
 bool bwd_slab_bf16_fits(const Problem& p);
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
-                                float* dv, float* ws, float* dq0, float* discard,
-                                hipStream_t stream);
+                                float* dv, float* discard, hipStream_t stream);
 
 }  // namespace fibatt

@@ -292,7 +292,16 @@ class FibottentionTable:
             _check(E_INVAL)
         return int(n)
 
+    def _shapes(self, *tensors):
+        for t in tensors:
+            if tuple(t.shape) != self.shape or t.dtype != self.dtype:
+                raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
+            if t.device != self._offs_dev.device:
+                raise ValueError(f"tensors must be on {self._offs_dev.device}, where the table is")
+
     def forward(self, q, k, v, o=None, lse=None, workspace=None, stream: Optional[int] = None):
+        """(o, lse) as Fibottention.forward."""
+        self._shapes(q, k, v)
         if o is None:
             o = torch.empty_like(q)
         if lse is None:
@@ -306,6 +315,8 @@ class FibottentionTable:
         return o, lse
 
     def backward(self, q, k, v, lse, do, workspace=None, stream: Optional[int] = None):
+        """fp32 (dq, dk, dv) as Fibottention.backward."""
+        self._shapes(q, k, v, do)
         dev = q.device
         dq, dk, dv = (torch.empty(self.shape, dtype=torch.float32, device=dev) for _ in range(3))
         if workspace is None:

@@ -312,3 +312,15 @@ def test_table_validation():
     big = _tdesc([0, 2], [1, 2], N=2049, d_h=128, cls=1)
     assert L.fibatt_fwd_table_workspace_floats(ctypes.byref(big)) == 2 * 3 * 130
     assert _fwd_t(big, ws=None) == fa.E_INVAL
+
+
+def test_table_binding_checks_shapes():
+    import torch
+    op = fa.FibottentionTable.__new__(fa.FibottentionTable)
+    op.shape, op.dtype = (2, 3, 65, 64), torch.float32
+    op._offs_dev = torch.zeros(1, dtype=torch.int32)  # a CPU stand-in for the device copy
+    with pytest.raises(ValueError):
+        op._shapes(torch.zeros(2, 3, 64, 64))
+    with pytest.raises(ValueError):
+        op._shapes(torch.zeros(2, 3, 65, 64, dtype=torch.bfloat16))
+    op._shapes(torch.zeros(2, 3, 65, 64))  # matching shape, dtype and device

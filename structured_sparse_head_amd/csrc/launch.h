@@ -31,9 +31,11 @@ inline int head_distances(const Problem& p, int h, int32_t* out) {
   return fib_offsets_gen(p.heads.a[h], p.heads.b[h], p.heads.lim[h], out, kMaxOffsets);
 }
 
-// LDS bytes a workgroup may use on the slab-resident paths (two workgroups
-// per CU fit in gfx950's 160 KiB).
-constexpr int kSlabLdsBudget = 80 * 1024;
+// LDS bytes a workgroup of the general slab-resident kernels may use: all
+// of gfx950's 160 KiB but the kernels' static arrays (fp32 ViT-B/16 slabs,
+// 2 N d_h 4 = 100 KB, fit; with the 80 KiB that allows two workgroups per CU
+// they fell back to the streaming kernels, 1.6x slower forward).
+constexpr int kSlabLdsBudget = 159 * 1024;
 
 // Which kernels a problem runs on; exposed so tests can force a variant.
 // kAuto picks the fastest variant whose constraints the problem meets.

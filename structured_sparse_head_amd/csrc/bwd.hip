@@ -369,13 +369,14 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes + 8 * static_cast<size_t>(p.N);
-    auto kern = bwd_slab_kernel<T, D, G, NT, MH, CLS>;
+    constexpr int NTS = 512;  // as the forward's slab kernel
+    auto kern = bwd_slab_kernel<T, D, G, NTS, MH, CLS>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         kSlabLdsBudget);
     if (attr != hipSuccess) return attr;
     a.tiles = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NT), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
   } else {
     const int per = NT / G;
     a.tiles = (p.N + per - 1) / per;

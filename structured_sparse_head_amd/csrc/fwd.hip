@@ -262,14 +262,17 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   if (path == Path::kSlab || (path == Path::kAuto && slab_ok)) {
     if (!slab_ok) return hipErrorInvalidValue;
     const size_t lds = 2 * static_cast<size_t>(p.N) * Gm::kRowBytes;
-    auto kern = fwd_slab_kernel<T, D, G, NT, C, MH, CLS>;
+    // One workgroup per CU holds a whole slab: 512 threads, so that a
+    // ViT-sized slab takes one pass of row groups.
+    constexpr int NTS = 512;
+    auto kern = fwd_slab_kernel<T, D, G, NTS, C, MH, CLS>;
     // Opt the kernel into the full slab budget once per process.
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         kSlabLdsBudget);
     if (attr != hipSuccess) return attr;
     a.tiles = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NT), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
   } else {
     const int rows = NT / G;
     a.tiles = (p.N + rows - 1) / rows;

@@ -34,7 +34,8 @@ inline int head_distances(const Problem& p, int h, int32_t* out) {
 // LDS bytes a workgroup of the general slab-resident kernels may use: all
 // of gfx950's 160 KiB but the kernels' static arrays (fp32 ViT-B/16 slabs,
 // 2 N d_h 4 = 100 KB, fit; with the 80 KiB that allows two workgroups per CU
-// they fell back to the streaming kernels, 1.6x slower forward).
+// they fell back to the streaming kernels).  With one workgroup per CU these
+// kernels run 512 threads.
 constexpr int kSlabLdsBudget = 159 * 1024;
 
 // Which kernels a problem runs on; exposed so tests can force a variant.

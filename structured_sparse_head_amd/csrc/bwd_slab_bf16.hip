@@ -577,8 +577,9 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     }
     constexpr int z = 2 * kMaxPos;  // table column of distance 0
     const bool wr = part == 0;      // table rows: row (private per lane group)
-    // Class-token mask: this row's pair with token 0 (query role: P and dP
-    // against key 0; key role: P and dS / sqrt(d) from query 0).
+    // Class-token mask: this row's pairs with token 0 (query role: P and dP
+    // against key 0, after the query passes; key role: P and dP from query
+    // 0, kept in side[] until the key passes know D_0).
     const bool need0 = CLS && rr >= 1 && !dist.has(rr, npos);
     const size_t r0g = static_cast<size_t>(slab) * N;  // row 0 of the slab
     if constexpr (CLS) {

@@ -81,6 +81,7 @@ int check_shape(int32_t B, int32_t H, int32_t N, int32_t d_h, int32_t dtype, fib
   p->N = N;
   p->D = d_h;
   p->dtype = dtype == FIBATT_BF16 ? fibatt::DType::kBF16 : fibatt::DType::kF32;
+  p->dense_layouts();
   return FIBATT_OK;
 }
 

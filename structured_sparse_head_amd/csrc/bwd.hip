@@ -29,6 +29,8 @@
 //    key-centric pass (dK, dV).  LSE and D of the slab stay in LDS.
 //  * stream: a query launch writes dQ and D (D to the workspace); a key
 //    launch then gathers dK and dV, reading shifted rows from global memory.
+#include <type_traits>
+
 #include "kernel_common.h"
 #include "launch.h"
 
@@ -51,8 +53,24 @@ struct BwdArgs {
   int tiles;         // row tiles per slab (stream variant)
   float scale_log2;  // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
+  Layout lq, lk, lv, ldo, ldq, ldk, ldv;
   HeadTableT<MH> ht;
 };
+
+// A slab's rows of one tensor: base pointer and byte stride.
+struct Rows {
+  char* base;
+  size_t rs;
+  __device__ char* row(int r) const { return base + static_cast<size_t>(r) * rs; }
+};
+
+template <typename T, typename P>
+__device__ __forceinline__ Rows slab_rows(P* ptr, const Layout& l, size_t slab, int H) {
+  constexpr int es = static_cast<int>(sizeof(T));
+  return Rows{reinterpret_cast<char*>(const_cast<typename std::remove_const<P>::type*>(ptr)) +
+                  l.slab_bytes(slab, H, es),
+              l.row_bytes(es)};
+}
 
 template <int DL>
 __device__ __forceinline__ void zero_acc(float (&acc)[DL]) {
@@ -177,16 +195,19 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
   const int part = tid % G;
-  const size_t base = slab * N * Gm::kRowBytes;
-  const size_t fbase = slab * N * D;  // fp32 outputs, elements
+  const Rows rq = slab_rows<T>(a.q, a.lq, slab, a.H), rk = slab_rows<T>(a.k, a.lk, slab, a.H);
+  const Rows rv = slab_rows<T>(a.v, a.lv, slab, a.H), rdo = slab_rows<T>(a.dout, a.ldo, slab, a.H);
+  const Rows rdq = slab_rows<float>(a.dq, a.ldq, slab, a.H);
+  const Rows rdk = slab_rows<float>(a.dk, a.ldk, slab, a.H);
+  const Rows rdv = slab_rows<float>(a.dv, a.ldv, slab, a.H);
   char* lds_a = smem;
   char* lds_b = smem + N * Gm::kRowBytes;
   float* s_lse2 = reinterpret_cast<float*>(smem + 2 * N * Gm::kRowBytes);
   float* s_d = s_lse2 + N;
 
   if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
-  stage_rows_lds<T, D, NT, false>(lds_a, a.k + base, N, tid);
-  stage_rows_lds<T, D, NT, false>(lds_b, a.v + base, N, tid);
+  stage_rows_lds<T, D, NT, false>(lds_a, rk.base, rk.rs, N, tid);
+  stage_rows_lds<T, D, NT, false>(lds_b, rv.base, rv.rs, N, tid);
   __syncthreads();
   const int nd = s_nd;
 
@@ -200,10 +221,9 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
       }
       continue;
     }
-    const size_t roff = base + static_cast<size_t>(j) * Gm::kRowBytes;
     uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.q + roff, part, qf);
-    frag_load_cached<T, D, G>(a.dout + roff, part, dof);
+    frag_load_cached<T, D, G>(rq.row(j), part, qf);
+    frag_load_cached<T, D, G>(rdo.row(j), part, dof);
     float acc_a[Gm::kDL], acc_b[Gm::kDL];
     zero_acc(acc_a);
     zero_acc(acc_b);
@@ -218,21 +238,20 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
       s_lse2[j] = lse2_j;
       if (CLS) a.ws[slab * N + j] = d_j;
     }
-    store_f32_frag_diff<Gm::kDL>(a.dq + fbase + static_cast<size_t>(j) * D, part, acc_a, d_j,
-                                 acc_b, a.scale);
+    store_f32_frag_diff<Gm::kDL>(reinterpret_cast<float*>(rdq.row(j)), part, acc_a, d_j, acc_b,
+                                 a.scale);
   }
   __syncthreads();
 
   // Key-centric pass: Q and dO replace K and V in LDS.
-  stage_rows_lds<T, D, NT, true>(lds_a, a.q + base, N, tid);
-  stage_rows_lds<T, D, NT, true>(lds_b, a.dout + base, N, tid);
+  stage_rows_lds<T, D, NT, true>(lds_a, rq.base, rq.rs, N, tid);
+  stage_rows_lds<T, D, NT, true>(lds_b, rdo.base, rdo.rs, N, tid);
   __syncthreads();
   for (int kr = tid / G; kr < N; kr += NT / G) {
     if (CLS && kr == 0) continue;
-    const size_t roff = base + static_cast<size_t>(kr) * Gm::kRowBytes;
     uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.k + roff, part, kf);
-    frag_load_cached<T, D, G>(a.v + roff, part, vf);
+    frag_load_cached<T, D, G>(rk.row(kr), part, kf);
+    frag_load_cached<T, D, G>(rv.row(kr), part, vf);
     float dk[Gm::kDL], dv[Gm::kDL];
     zero_acc(dk);
     zero_acc(dv);
@@ -245,8 +264,8 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
     dkdv_row<T, D, G>(kr, N, s_deltas, nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
     if (CLS && !has_delta(s_deltas, nd, kr))
       dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
-    store_f32_frag<Gm::kDL>(a.dk + fbase + static_cast<size_t>(kr) * D, part, dk, a.scale);
-    store_f32_frag<Gm::kDL>(a.dv + fbase + static_cast<size_t>(kr) * D, part, dv, 1.0f);
+    store_f32_frag<Gm::kDL>(reinterpret_cast<float*>(rdk.row(kr)), part, dk, a.scale);
+    store_f32_frag<Gm::kDL>(reinterpret_cast<float*>(rdv.row(kr)), part, dv, 1.0f);
   }
 }
 
@@ -267,28 +286,24 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   const int j = tile * (NT / G) + tid / G;
   if (j >= N || (CLS && j == 0)) return;
   const int part = tid % G;
-  const size_t base = slab * N * Gm::kRowBytes;
-  const char* ks = a.k + base;
-  const char* vs = a.v + base;
+  const Rows rk = slab_rows<T>(a.k, a.lk, slab, a.H), rv = slab_rows<T>(a.v, a.lv, slab, a.H);
   uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
-  frag_load_cached<T, D, G>(a.dout + base + static_cast<size_t>(j) * Gm::kRowBytes, part, dof);
+  frag_load_cached<T, D, G>(slab_rows<T>(a.q, a.lq, slab, a.H).row(j), part, qf);
+  frag_load_cached<T, D, G>(slab_rows<T>(a.dout, a.ldo, slab, a.H).row(j), part, dof);
   const float lse2_j = a.lse[slab * N + j] * kLog2e;
   float acc_a[Gm::kDL], acc_b[Gm::kDL];
   zero_acc(acc_a);
   zero_acc(acc_b);
-  auto lk = [&](int r, uint32_t(&f)[Gm::kWPL]) {
-    frag_load_cached<T, D, G>(ks + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-  };
-  auto lv = [&](int r, uint32_t(&f)[Gm::kWPL]) {
-    frag_load_cached<T, D, G>(vs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-  };
+  auto lk = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_cached<T, D, G>(rk.row(r), part, f); };
+  auto lv = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_cached<T, D, G>(rv.row(r), part, f); };
   float d_j =
       dq_row<T, D, G>(j, N, s_deltas, s_nd, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, lk, lv);
   if (CLS && !has_delta(s_deltas, s_nd, j))
     dq_key<T, D, G>(0, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, d_j, lk, lv);
   if (part == 0) a.ws[slab * N + j] = d_j;
-  store_f32_frag_diff<Gm::kDL>(a.dq + (slab * N + j) * D, part, acc_a, d_j, acc_b, a.scale);
+  store_f32_frag_diff<Gm::kDL>(
+      reinterpret_cast<float*>(slab_rows<float>(a.dq, a.ldq, slab, a.H).row(j)), part, acc_a, d_j,
+      acc_b, a.scale);
 }
 
 // Stream variant, key launch: dK and dV for a tile of key rows.
@@ -308,22 +323,16 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   const int kr = tile * (NT / G) + tid / G;
   if (kr >= N || (CLS && kr == 0)) return;
   const int part = tid % G;
-  const size_t base = slab * N * Gm::kRowBytes;
   const size_t rbase = slab * N;
-  const char* qs = a.q + base;
-  const char* dos = a.dout + base;
+  const Rows rq = slab_rows<T>(a.q, a.lq, slab, a.H), rdo = slab_rows<T>(a.dout, a.ldo, slab, a.H);
   uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(kr) * Gm::kRowBytes, part, kf);
-  frag_load_cached<T, D, G>(a.v + base + static_cast<size_t>(kr) * Gm::kRowBytes, part, vf);
+  frag_load_cached<T, D, G>(slab_rows<T>(a.k, a.lk, slab, a.H).row(kr), part, kf);
+  frag_load_cached<T, D, G>(slab_rows<T>(a.v, a.lv, slab, a.H).row(kr), part, vf);
   float dk[Gm::kDL], dv[Gm::kDL];
   zero_acc(dk);
   zero_acc(dv);
-  auto lq = [&](int r, uint32_t(&f)[Gm::kWPL]) {
-    frag_load_cached<T, D, G>(qs + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-  };
-  auto ldo = [&](int r, uint32_t(&f)[Gm::kWPL]) {
-    frag_load_cached<T, D, G>(dos + static_cast<size_t>(r) * Gm::kRowBytes, part, f);
-  };
+  auto lq = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_cached<T, D, G>(rq.row(r), part, f); };
+  auto ldo = [&](int r, uint32_t(&f)[Gm::kWPL]) { frag_load_cached<T, D, G>(rdo.row(r), part, f); };
   auto lrow = [&](int r, float& l2, float& dd) {
     l2 = a.lse[rbase + r] * kLog2e;
     dd = a.ws[rbase + r];
@@ -331,8 +340,10 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   dkdv_row<T, D, G>(kr, N, s_deltas, s_nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
   if (CLS && !has_delta(s_deltas, s_nd, kr))
     dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
-  store_f32_frag<Gm::kDL>(a.dk + (rbase + kr) * D, part, dk, a.scale);
-  store_f32_frag<Gm::kDL>(a.dv + (rbase + kr) * D, part, dv, 1.0f);
+  store_f32_frag<Gm::kDL>(
+      reinterpret_cast<float*>(slab_rows<float>(a.dk, a.ldk, slab, a.H).row(kr)), part, dk, a.scale);
+  store_f32_frag<Gm::kDL>(
+      reinterpret_cast<float*>(slab_rows<float>(a.dv, a.ldv, slab, a.H).row(kr)), part, dv, 1.0f);
 }
 
 // Each lane owns 64 bytes of an input row: the key-centric loop keeps two
@@ -363,6 +374,13 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
   a.N = p.N;
   a.scale = 1.0f / sqrtf(static_cast<float>(D));
   a.scale_log2 = kLog2e * a.scale;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.ldo = p.ldo;
+  a.ldq = p.ldq;
+  a.ldk = p.ldk;
+  a.ldv = p.ldv;
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const size_t slabs = static_cast<size_t>(p.B) * p.H;
   const bool slab_ok = bwd_slab_fits(p);

@@ -39,6 +39,7 @@ struct FwdArgs {
   int N;
   int tiles;          // query tiles per slab (stream variant)
   float scale_log2;   // log2(e) / sqrt(d)
+  Layout lq, lk, lv, lo;
   HeadTableT<MH> ht;
 };
 
@@ -58,11 +59,12 @@ template <typename T, int D, int G>
 struct GlobalKV {
   const char* k;  // slab base
   const char* v;
+  size_t rsk, rsv;  // row strides, bytes
   __device__ void load_k(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
-    frag_load_cached<T, D, G>(k + static_cast<size_t>(r) * Geom<T, D, G>::kRowBytes, part, f);
+    frag_load_cached<T, D, G>(k + static_cast<size_t>(r) * rsk, part, f);
   }
   __device__ void load_v(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
-    frag_load_cached<T, D, G>(v + static_cast<size_t>(r) * Geom<T, D, G>::kRowBytes, part, f);
+    frag_load_cached<T, D, G>(v + static_cast<size_t>(r) * rsv, part, f);
   }
 };
 
@@ -143,7 +145,9 @@ __device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, in
   using Gm = Geom<T, D, G>;
   const bool has = l > 0.f;
   const float inv = has ? 1.0f / l : 0.f;
-  u32x4* orow = reinterpret_cast<u32x4*>(a.o + (slab * a.N + j) * Gm::kRowBytes) + part * Gm::kCPL;
+  constexpr int es = static_cast<int>(sizeof(T));
+  u32x4* orow = reinterpret_cast<u32x4*>(a.o + a.lo.slab_bytes(slab, a.H, es) + j * a.lo.row_bytes(es)) +
+                part * Gm::kCPL;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int t = 0; t < Gm::kCPL; ++t) {
@@ -180,11 +184,15 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   const int h = static_cast<int>(slab % a.H);
   const int N = a.N;
   if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
-  const size_t base = slab * N * Gm::kRowBytes;
+  constexpr int es = static_cast<int>(sizeof(T));
   char* lds_k = smem;
   char* lds_v = smem + N * Gm::kRowBytes;
-  stage_rows_lds<T, D, NT, true>(lds_k, a.k + base, N, tid);
-  stage_rows_lds<T, D, NT, true>(lds_v, a.v + base, N, tid);
+  stage_rows_lds<T, D, NT, true>(lds_k, a.k + a.lk.slab_bytes(slab, a.H, es), a.lk.row_bytes(es),
+                                 N, tid);
+  stage_rows_lds<T, D, NT, true>(lds_v, a.v + a.lv.slab_bytes(slab, a.H, es), a.lv.row_bytes(es),
+                                 N, tid);
+  const char* qbase = a.q + a.lq.slab_bytes(slab, a.H, es);
+  const size_t rsq = a.lq.row_bytes(es);
   __syncthreads();
   const int nd = s_nd;
   const int part = tid % G;
@@ -192,7 +200,7 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   for (int j = tid / G; j < N; j += NT / G) {
     if (CLS && j == 0) continue;
     uint32_t qf[Gm::kWPL];
-    frag_load_global<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
+    frag_load_global<T, D, G>(qbase + static_cast<size_t>(j) * rsq, part, qf);
     float acc[Gm::kDL];
 #pragma unroll
     for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
@@ -220,10 +228,13 @@ __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   const int j = tile * (NT / G) + tid / G;
   if (j >= N || (CLS && j == 0)) return;
   const int part = tid % G;
-  const size_t base = slab * N * Gm::kRowBytes;
-  const GlobalKV<T, D, G> kv{a.k + base, a.v + base};
+  constexpr int es = static_cast<int>(sizeof(T));
+  const GlobalKV<T, D, G> kv{a.k + a.lk.slab_bytes(slab, a.H, es),
+                             a.v + a.lv.slab_bytes(slab, a.H, es), a.lk.row_bytes(es),
+                             a.lv.row_bytes(es)};
   uint32_t qf[Gm::kWPL];
-  frag_load_global<T, D, G>(a.q + base + static_cast<size_t>(j) * Gm::kRowBytes, part, qf);
+  frag_load_global<T, D, G>(a.q + a.lq.slab_bytes(slab, a.H, es) + j * a.lq.row_bytes(es), part,
+                            qf);
   float acc[Gm::kDL];
 #pragma unroll
   for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;
@@ -256,6 +267,10 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
   a.H = p.H;
   a.N = p.N;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const size_t slabs = static_cast<size_t>(p.B) * p.H;
   const bool slab_ok = fwd_slab_fits(p);

@@ -47,6 +47,18 @@ HeadTableT<MH> shrink_heads(const HeadTable& t, int H) {
   return r;
 }
 
+// Where a tensor's rows live: element (b, h, n, e) of a [B, H, N, D] view is
+// at sb b + sh h + sn n + e (elements; the D elements of a row contiguous).
+// A dense [B, H, N, D] tensor has sb = H N D, sh = N D, sn = D.
+struct Layout {
+  int64_t sb, sh, sn;
+  // Byte offset of row 0 of slab b H + h, and the byte stride of rows.
+  __host__ __device__ size_t slab_bytes(size_t slab, int H, int esize) const {
+    return (static_cast<size_t>(slab / H) * sb + static_cast<size_t>(slab % H) * sh) * esize;
+  }
+  __host__ __device__ size_t row_bytes(int esize) const { return static_cast<size_t>(sn) * esize; }
+};
+
 using bf16_t = uint16_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -140,24 +152,25 @@ __device__ __forceinline__ void frag_store_lds(char* base, int r, int part,
   }
 }
 
-// Copy `rows` rows of a dense [rows, D] tensor into LDS in the swizzled
-// layout.  Consecutive threads move consecutive 16-byte chunks, so the global
-// reads are fully coalesced.
+// Copy `rows` rows of D elements, `rs` bytes apart in global memory, into
+// LDS in the swizzled layout.  Consecutive threads move consecutive 16-byte
+// chunks, so the global reads are coalesced within each row.
 // kLastUse marks the final read of the data: those loads are issued
 // non-temporal so they do not displace lines that will be read again.
 template <typename T, int D, int NT, bool kLastUse>
-__device__ __forceinline__ void stage_rows_lds(char* lds, const char* src, int rows, int tid) {
+__device__ __forceinline__ void stage_rows_lds(char* lds, const char* src, size_t rs, int rows,
+                                               int tid) {
   using Gm = Geom<T, D, 1>;
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
   const int total = rows * Gm::kCPR;
   for (int idx = tid; idx < total; idx += NT) {
     const int r = idx / Gm::kCPR;
     const int c = idx % Gm::kCPR;
+    const u32x4* s = reinterpret_cast<const u32x4*>(src + r * rs) + c;
     u32x4 x;
     if constexpr (kLastUse) {
-      x = __builtin_nontemporal_load(s + idx);
+      x = __builtin_nontemporal_load(s);
     } else {
-      x = s[idx];
+      x = *s;
     }
     *reinterpret_cast<u32x4*>(lds + r * Gm::kRowBytes + lds_chunk<Gm::kCPR>(r, c) * 16) = x;
   }

@@ -19,6 +19,14 @@ struct Problem {
   HeadTable heads;
   const int32_t* host_table = nullptr;  // host copy of the table, or null
   bool cls = false;  // class-token mask: row and column 0 dense
+  // Row layouts of the tensors (dense [B, H, N, D] unless `strided`).
+  Layout lq, lk, lv, lo, ldo, ldq, ldk, ldv;
+  bool strided = false;
+  void dense_layouts() {
+    const Layout d{static_cast<int64_t>(H) * N * D, static_cast<int64_t>(N) * D, D};
+    lq = lk = lv = lo = ldo = ldq = ldk = ldv = d;
+    strided = false;
+  }
 };
 
 // Ascending distances of head h (at most kMaxOffsets are written).

@@ -173,9 +173,13 @@ def bench_block(args):
         x2 = [x.detach().reshape(B * N, C) for x in xs]
         ms_qkv = timed(lambda i: torch.mm(x2[i % R], layer.w_qkv), K)
         ms_out = timed(lambda i: torch.mm(x2[i % R], layer.w_z), K)
-        qkv = [layer.project_qkv(x.detach()) for x in xs[:2]]
+        # the sparse core as the layer runs it: strided head views of the
+        # fused projection in, O written in [B, N, H, d_h] order
+        heads = [[t[:, :, j].permute(0, 2, 1, 3) for j in range(3)]
+                 for t in (torch.mm(x, layer.w_qkv).view(B, N, 3, H, C // H) for x in x2[:2])]
+        o = torch.empty(B, N, H, C // H, dtype=dt, device=dev).permute(0, 2, 1, 3)
         op = fa.Fibottention(B, H, N, C // H, dt, layer.a, layer.b, layer.w, cls=args.cls)
-        ms_core = timed(lambda i: op.forward(*qkv[i % 2]), K)
+        ms_core = timed(lambda i: op.forward(*heads[i % 2], o=o), K)
     gemm_fwd_flops = 2 * B * N * C * 3 * C + 2 * B * N * C * C
     gemm_tflops = gemm_fwd_flops / ((ms_qkv + ms_out) * 1e-3) / 1e12
     line = {

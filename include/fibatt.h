@@ -153,9 +153,10 @@ int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k,
  * distance between two patches is the same as between their positions).
  * Pair (0, 0) is in the support.  Every row therefore has at least one key:
  * LSE is finite everywhere.  Same layouts, ownership and error behaviour as
- * fibatt_fwd / fibatt_bwd; the kernels are the general (not the bf16
- * ViT-shape) ones plus dense row-0 and column-0 reductions over the slab,
- * done in fixed order (bitwise reproducible).
+ * fibatt_fwd / fibatt_bwd.  Row 0 and column 0 are dense reductions over the
+ * slab done in fixed order (bitwise reproducible): inside the bf16 d_h = 64
+ * kernels for N <= 240 (forward) and N <= 201 (backward), by separate dense
+ * row/column kernels otherwise.
  *
  * Workspace: fibatt_fwd_cls_workspace_floats(desc) fp32 elements (0 when N
  * <= 1024, and then `workspace` may be NULL), fibatt_bwd_cls_workspace_floats
@@ -219,6 +220,52 @@ int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q,
                      const void* k, const void* v, const float* lse,
                      const void* dout, float* dq, float* dk, float* dv,
                      float* workspace, void* stream);
+
+/* Strided tensors.  Row n of head h of batch b of a tensor starts at
+ * element b*sb + h*sh + n*sn of its buffer (strides in elements of that
+ * tensor's own type); the row's d_h elements are contiguous.  The dense
+ * [B, H, N, d_h] layout is {H*N*d_h, N*d_h, d_h}; the Q of a fused QKV
+ * projection stored [B, N, 3, H, d_h] is {3*N*H*d_h, d_h, 3*H*d_h} at
+ * offset 0 (K at H*d_h, V at 2*H*d_h), and an output in [B, N, H, d_h]
+ * (ready for the output projection) is {N*H*d_h, d_h, H*d_h}.
+ * Requirements, checked on the host: strides >= 0, sn >= d_h, every stride
+ * times the element size a multiple of 16 bytes (with 16-byte aligned base
+ * pointers every row is then 16-byte aligned), and the largest element
+ * offset below 2^62.  Not checkable and left to the caller: the buffers hold
+ * every row, and distinct rows of an output do not overlap each other or
+ * any input.  LSE and the workspace stay dense [B, H, N]. */
+typedef struct {
+  int64_t sb, sh, sn;
+} fibatt_layout;
+
+/* Layouts of one call's tensors; the forward reads q, k, v, o and ignores
+ * the rest, the backward ignores o. */
+typedef struct {
+  fibatt_layout q, k, v, o, dout, dq, dk, dv;
+} fibatt_layouts;
+
+/* Forward and backward with strided tensors: otherwise as fibatt_fwd /
+ * fibatt_bwd (cls = 0) or fibatt_fwd_cls / fibatt_bwd_cls (cls = 1).
+ * Workspaces (fp32 elements): forward none with cls = 0 (may be NULL),
+ * fibatt_fwd_cls_workspace_floats(desc) with cls = 1 (0, and then NULL is
+ * allowed, whenever the tensors are strided); backward
+ * fibatt_bwd_workspace_floats(desc) (cls = 0) or
+ * fibatt_bwd_cls_workspace_floats(desc) (cls = 1).  The bf16
+ * d_h = 64 kernels for N <= 256 (forward) and N <= 201 (backward) read and
+ * write strided rows at full speed; other shapes run the general kernels
+ * (bf16 beyond those N is slower than with dense tensors).  Errors: as
+ * fibatt_fwd, plus E_INVAL for a bad layout or cls not 0/1, and
+ * E_UNSUPPORTED for cls = 1 outside N <= 240 (forward) or N <= 201
+ * (backward) with bf16 and d_h = 64. */
+int fibatt_fwd_strided(const fibatt_desc* desc, int32_t cls,
+                       const fibatt_layouts* layouts, const void* q,
+                       const void* k, const void* v, void* o, float* lse,
+                       float* workspace, void* stream);
+int fibatt_bwd_strided(const fibatt_desc* desc, int32_t cls,
+                       const fibatt_layouts* layouts, const void* q,
+                       const void* k, const void* v, const float* lse,
+                       const void* dout, float* dq, float* dk, float* dv,
+                       float* workspace, void* stream);
 
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */

@@ -16,8 +16,11 @@ from .fibatt import (  # noqa: F401
     MAX_HEADS,
     OK,
     FibattError,
+    Layout,
+    Layouts,
     Fibottention,
     FibottentionFunction,
+    FibottentionQKVFunction,
     FibottentionTable,
     backward,
     forward,

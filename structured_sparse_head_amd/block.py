@@ -5,8 +5,11 @@ i = 1..h (d_h = c / h) -> Z_i = sparse Fibottention attention of head i ->
 O = concat(Z_1..Z_h) W^Z.  The four projections are plain dense GEMMs and
 run through torch (hipBLASLt on MFMA); the sparse core is the HIP library
 behind ``fibatt_fwd`` / ``fibatt_bwd`` (or the class-token entry points), with
-its 1/sqrt(d_h) score scale.  Gradients of all of it come from torch
-autograd around ``FibottentionFunction``.
+its 1/sqrt(d_h) score scale.  The kernels read Q, K and V as strided views of
+the fused projection's output and write O straight into the [B, N, h, d_h]
+order the output projection reads (``FibottentionQKVFunction``), so the
+layer makes no head split or merge copies.  Gradients of the projections come
+from torch autograd around that function.
 
 Heads use Wythoff rows 1..h (or README Algorithm 2's modified pairs) and the
 windows interpolated between w_min and w_max (Fibottention paper, method
@@ -20,7 +23,7 @@ from typing import Optional
 
 import torch
 
-from .fibatt import FibottentionFunction, windows, wythoff_rows
+from .fibatt import FibottentionQKVFunction, windows, wythoff_rows
 
 
 class FibottentionAttention(torch.nn.Module):
@@ -51,18 +54,10 @@ class FibottentionAttention(torch.nn.Module):
             for p in (self.w_qkv, self.w_z):
                 p.copy_(torch.randn(p.shape, generator=generator, dtype=torch.float32) * std)
 
-    def project_qkv(self, x: torch.Tensor):
-        """Q, K, V as contiguous [B, h, N, d_h] tensors."""
-        B, N, c = x.shape
-        qkv = torch.mm(x.reshape(B * N, c), self.w_qkv)
-        qkv = qkv.view(B, N, 3, self.heads, self.d_h).permute(2, 0, 3, 1, 4)
-        return qkv[0].contiguous(), qkv[1].contiguous(), qkv[2].contiguous()
-
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         B, N, c = x.shape
         if N != self.n_tokens or c != self.dim:
             raise ValueError(f"expected [B, {self.n_tokens}, {self.dim}], got {tuple(x.shape)}")
-        q, k, v = self.project_qkv(x)
-        z = FibottentionFunction.apply(q, k, v, self.a, self.b, self.w, self.cls)
-        z = z.permute(0, 2, 1, 3).reshape(B * N, c)
-        return torch.mm(z, self.w_z).view(B, N, c)
+        qkv = torch.mm(x.reshape(B * N, c), self.w_qkv).view(B, N, 3, self.heads, self.d_h)
+        z = FibottentionQKVFunction.apply(qkv, self.a, self.b, self.w, self.cls)
+        return torch.mm(z.view(B * N, c), self.w_z).view(B, N, c)

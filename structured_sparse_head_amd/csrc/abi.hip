@@ -146,6 +146,65 @@ int check_ptr(const void* p, const char* name) {
   return FIBATT_OK;
 }
 
+// Validates one tensor's layout (strides in elements of esize bytes).
+int check_layout(const fibatt_layout& l, const char* name, const fibatt::Problem& p, int esize,
+                 fibatt::Layout* out) {
+  if (l.sb < 0 || l.sh < 0 || l.sn < 0)
+    return fail(FIBATT_E_INVAL, "layout of %s: strides must be >= 0", name);
+  if (l.sn < p.D)
+    return fail(FIBATT_E_INVAL, "layout of %s: sn = %lld must be >= d_h = %d", name,
+                static_cast<long long>(l.sn), p.D);
+  const int64_t unit = 16 / esize;
+  if (l.sb % unit || l.sh % unit || l.sn % unit)
+    return fail(FIBATT_E_INVAL, "layout of %s: strides must be multiples of %lld elements", name,
+                static_cast<long long>(unit));
+  // Largest element offset, with every term kept below 2^62.
+  const int64_t lim = int64_t{1} << 62;
+  const int64_t n[3] = {p.B - 1, p.H - 1, p.N - 1};
+  const int64_t st[3] = {l.sb, l.sh, l.sn};
+  int64_t end = p.D;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] && n[i] > (lim - end) / st[i])
+      return fail(FIBATT_E_INVAL, "layout of %s: offsets exceed 2^62 elements", name);
+    end += n[i] * st[i];
+  }
+  *out = fibatt::Layout{l.sb, l.sh, l.sn};
+  return FIBATT_OK;
+}
+
+bool same_layout(const fibatt::Layout& x, const fibatt::Layout& y) {
+  return x.sb == y.sb && x.sh == y.sh && x.sn == y.sn;
+}
+
+// Fills p's layouts (bf16 or fp32 inputs and O, fp32 gradients); p.strided
+// is set unless every layout is the dense one.
+int check_layouts(const fibatt_layouts* ls, bool bwd, fibatt::Problem* p) {
+  if (!ls) return fail(FIBATT_E_INVAL, "layouts is NULL");
+  const int es = p->dtype == fibatt::DType::kBF16 ? 2 : 4;
+  int rc;
+  if ((rc = check_layout(ls->q, "q", *p, es, &p->lq)) ||
+      (rc = check_layout(ls->k, "k", *p, es, &p->lk)) ||
+      (rc = check_layout(ls->v, "v", *p, es, &p->lv)))
+    return rc;
+  if (bwd) {
+    if ((rc = check_layout(ls->dout, "dout", *p, es, &p->ldo)) ||
+        (rc = check_layout(ls->dq, "dq", *p, 4, &p->ldq)) ||
+        (rc = check_layout(ls->dk, "dk", *p, 4, &p->ldk)) ||
+        (rc = check_layout(ls->dv, "dv", *p, 4, &p->ldv)))
+      return rc;
+  } else if ((rc = check_layout(ls->o, "o", *p, es, &p->lo))) {
+    return rc;
+  }
+  const fibatt::Layout d{static_cast<int64_t>(p->H) * p->N * p->D,
+                         static_cast<int64_t>(p->N) * p->D, p->D};
+  const fibatt::Layout* used[] = {&p->lq, &p->lk, &p->lv, bwd ? &p->ldo : &p->lo,
+                                  &p->ldq, &p->ldk, &p->ldv};
+  const int n_used = bwd ? 7 : 4;
+  p->strided = false;
+  for (int i = 0; i < n_used; ++i) p->strided |= !same_layout(*used[i], d);
+  return FIBATT_OK;
+}
+
 // Test hook: FIBATT_PATH=slab|stream forces a kernel variant (default auto).
 fibatt::Path path_from_env() {
   const char* s = std::getenv("FIBATT_PATH");
@@ -366,6 +425,70 @@ int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q, const void* k
             : fibatt::launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, workspace, s, path_from_env());
   if (e != hipSuccess)
     return fail(FIBATT_E_HIP, "fibatt_bwd_table launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fibatt_fwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layouts* layouts,
+                       const void* q, const void* k, const void* v, void* o, float* lse,
+                       float* workspace, void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if (cls != 0 && cls != 1) return fail(FIBATT_E_INVAL, "cls must be 0 or 1");
+  if ((rc = check_layouts(layouts, false, &p))) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
+    return rc;
+  if (cls && fibatt::fwd_cls_workspace_floats(p) > 0 && (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const fibatt::Path path = path_from_env();
+  hipError_t e;
+  if (cls) {
+    // Only the fused kernel computes the dense row on strided rows.
+    p.cls = true;
+    if (p.strided && !(path == fibatt::Path::kAuto && fibatt::fwd_slab_bf16_fits(p) &&
+                       fibatt::fwd_slab_bf16_dense_row(p)))
+      return fail(FIBATT_E_UNSUPPORTED,
+                  "strided tensors with cls = 1 need bf16, d_h = 64 and N <= 240 (forward)");
+    e = fibatt::launch_fwd_cls(p, q, k, v, o, lse, workspace, static_cast<hipStream_t>(stream),
+                               path);
+  } else {
+    e = fibatt::launch_fwd(p, q, k, v, o, lse, static_cast<hipStream_t>(stream), path);
+  }
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_fwd_strided launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fibatt_bwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layouts* layouts,
+                       const void* q, const void* k, const void* v, const float* lse,
+                       const void* dout, float* dq, float* dk, float* dv, float* workspace,
+                       void* stream) {
+  fibatt::Problem p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if (cls != 0 && cls != 1) return fail(FIBATT_E_INVAL, "cls must be 0 or 1");
+  if ((rc = check_layouts(layouts, true, &p))) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")) ||
+      (rc = check_ptr(workspace, "workspace")))
+    return rc;
+  const fibatt::Path path = path_from_env();
+  hipError_t e;
+  if (cls) {
+    p.cls = true;
+    if (p.strided && !(path == fibatt::Path::kAuto && fibatt::bwd_slab_bf16_fits(p)))
+      return fail(FIBATT_E_UNSUPPORTED,
+                  "strided tensors with cls = 1 need bf16, d_h = 64 and N <= 201 (backward)");
+    e = fibatt::launch_bwd_cls(p, q, k, v, lse, dout, dq, dk, dv, workspace,
+                               static_cast<hipStream_t>(stream), path);
+  } else {
+    e = fibatt::launch_bwd(p, q, k, v, lse, dout, dq, dk, dv, workspace,
+                           static_cast<hipStream_t>(stream), path);
+  }
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_bwd_strided launch: %s", hipGetErrorString(e));
   return ok();
 }
 

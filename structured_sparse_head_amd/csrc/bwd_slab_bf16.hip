@@ -51,6 +51,8 @@
 // a discard row and their dQ, dK and dV stores go to a discard row of the
 // workspace.  The class-token areas live in table rows no lane uses (lanes
 // own table rows below 16 ceil(N / 16) <= 208).
+#include <type_traits>
+
 #include "slab_bf16_common.h"
 
 namespace fibatt {
@@ -83,8 +85,11 @@ constexpr int kDiscardRow = kRowsB - 1;
 static_assert(kClsRow * kTableCols * 8 + kClsBytes <= kDiscardRow * kTableCols * 8,
               "class-token areas must fit in the unused table rows");
 
-template <int MH>
+// With STR the rows of every tensor follow their layouts (strided views,
+// e.g. of a fused QKV projection); without it they are dense [B, H, N, 64].
+template <int MH, bool STR>
 struct Args {
+  static constexpr bool kStrided = STR;
   const char* q;
   const char* k;
   const char* v;
@@ -100,8 +105,23 @@ struct Args {
   float c;      // log2(e) / sqrt(64)
   float scale;  // 1 / sqrt(64)
   uint64_t blocks;  // row block of wave w in bits 4 w .. 4 w + 3
+  Layout lq, lk, lv, ldo, ldq, ldk, ldv;
   u32x4 rec[MH];
 };
+
+// Address of row r of a slab of tensor x (layout l, ES-byte elements) for
+// either kind of arguments.
+template <int ES, typename T, typename A>
+__device__ __forceinline__ T* slab_row(const A& a, T* x, const Layout& l, size_t slab, int N,
+                                       int r) {
+  size_t off;
+  if constexpr (A::kStrided)
+    off = l.slab_bytes(slab, a.H, ES) + static_cast<size_t>(r) * l.row_bytes(ES);
+  else
+    off = (slab * static_cast<size_t>(N) + r) * (64 * ES);
+  using C = std::conditional_t<std::is_const<T>::value, const char, char>;
+  return reinterpret_cast<T*>(reinterpret_cast<C*>(x) + off);
+}
 
 // Writes this lane's 16 bf16 elements (packed in w, groups p, p + 4, p + 8,
 // p + 12) as fp32 to logical chunks 4 p .. 4 p + 3 of an LDS row.
@@ -132,21 +152,41 @@ struct Prefetch {
 template <typename A>
 __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, int tid, int row,
                                                int part, bool idle, Prefetch& pf) {
-  const size_t base = slab * static_cast<size_t>(N) * kRowBytes;
-  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
   const int last = idle ? 0 : N * (kRowBytes / 16) - 1;
-#pragma unroll
-  for (int c = 0; c < kChunksB; ++c) {
-    int idx = tid + c * kThreadsB;
-    idx = idx < last ? idx : last;
-    pf.k[c] = __builtin_nontemporal_load(ks + idx);
-    pf.v[c] = __builtin_nontemporal_load(vs + idx);
-  }
   const int r = idle ? 0 : (row < N ? row : N - 1);
-  const size_t off = base + static_cast<size_t>(r) * kRowBytes + part * 8;
-  const u32x2* qs = reinterpret_cast<const u32x2*>(a.q + off);
-  const u32x2* ds = reinterpret_cast<const u32x2*>(a.dout + off);
+  const char* qr;
+  const char* dr;
+  if constexpr (A::kStrided) {
+    const char* ks = slab_row<2>(a, a.k, a.lk, slab, N, 0);
+    const char* vs = slab_row<2>(a, a.v, a.lv, slab, N, 0);
+    const size_t rk = a.lk.row_bytes(2), rv = a.lv.row_bytes(2);
+#pragma unroll
+    for (int c = 0; c < kChunksB; ++c) {
+      int idx = tid + c * kThreadsB;
+      idx = idx < last ? idx : last;
+      const int kr = idx >> 3, ch = idx & 7;  // row, 16-byte chunk
+      pf.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + kr * rk) + ch);
+      pf.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + kr * rv) + ch);
+    }
+    qr = slab_row<2>(a, a.q, a.lq, slab, N, r);
+    dr = slab_row<2>(a, a.dout, a.ldo, slab, N, r);
+  } else {
+    const size_t base = slab * static_cast<size_t>(N) * kRowBytes;
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
+#pragma unroll
+    for (int c = 0; c < kChunksB; ++c) {
+      int idx = tid + c * kThreadsB;
+      idx = idx < last ? idx : last;
+      pf.k[c] = __builtin_nontemporal_load(ks + idx);
+      pf.v[c] = __builtin_nontemporal_load(vs + idx);
+    }
+    const size_t off = base + static_cast<size_t>(r) * kRowBytes;
+    qr = a.q + off;
+    dr = a.dout + off;
+  }
+  const u32x2* qs = reinterpret_cast<const u32x2*>(qr + part * 8);
+  const u32x2* ds = reinterpret_cast<const u32x2*>(dr + part * 8);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {  // group part + 4 m sits at byte 8 part + 32 m
     pf.q[m] = __builtin_nontemporal_load(qs + 4 * m);
@@ -337,10 +377,9 @@ __device__ __forceinline__ void dense_col0(const A& a, int slab, int N, int lane
                                       256) + kRowsB;
   const int slot = lane & 15;
   const int part = lane_part(lane);
-  const size_t r0 = static_cast<size_t>(slab) * N * 64;
   // One output row at a time (dV_0 from dO, then dK_0 from Q), to keep
   // registers for the prefetch of the next slab.
-  auto column = [&](const char* lds_x, bool second, float* out) {
+  auto column = [&](const char* lds_x, bool second, float* out, const Layout& l) {
     float acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -360,14 +399,14 @@ __device__ __forceinline__ void dense_col0(const A& a, int slab, int N, int lane
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] += wave_xor(acc[e], kSpan[s]);
     if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
-      float4* p = reinterpret_cast<float4*>(out + r0) + part;
+      float4* p = reinterpret_cast<float4*>(slab_row<4>(a, out, l, slab, N, 0)) + part;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         p[4 * t] = make_float4(acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]);
     }
   };
-  column(lds_do, false, a.dv);
-  column(lds_q, true, a.dk);
+  column(lds_do, false, a.dv, a.ldv);
+  column(lds_q, true, a.dk, a.ldk);
 }
 
 // Class-token LDS areas (see kClsRow).
@@ -461,7 +500,7 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
     for (int e = 0; e < 16; ++e) acc[e] += wave_xor(acc[e], kSpan[s]);
   if (lane == 0) *cl.d0 = d0;
   if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
-    float4* pq = reinterpret_cast<float4*>(a.dq + static_cast<size_t>(slab) * N * 64) + part;
+    float4* pq = reinterpret_cast<float4*>(slab_row<4>(a, a.dq, a.ldq, slab, N, 0)) + part;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       pq[4 * t] = make_float4(acc[4 * t] * a.scale, acc[4 * t + 1] * a.scale,
@@ -469,8 +508,8 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
   }
 }
 
-template <int MH, bool CLS>
-__global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
+template <int MH, bool CLS, bool STR>
+__global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH, STR> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -561,7 +600,6 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
     // Start the next slab's loads; they land while this slab is computed.
     const int next = slab + gridDim.x;
     issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
-    const size_t grow = static_cast<size_t>(slab) * N + rr;
     const u32x4 rec = a.rec[slab % a.H];
     const Dist dist{rec.x, rec.y, rec.z};
     const int npos = static_cast<int>(rec.w & 0xffu);
@@ -671,9 +709,9 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
       // dQ is written during the dV pass and dV during the dK pass.
       // With the class-token mask row 0's results come from elsewhere.
       const bool drop = CLS && rr == 0;
-      float* dq_row = drop ? a.discard : a.dq + grow * 64;
-      float* dv_row = drop ? a.discard : a.dv + grow * 64;
-      float* dk_row = drop ? a.discard : a.dk + grow * 64;
+      float* dq_row = drop ? a.discard : slab_row<4>(a, a.dq, a.ldq, slab, N, rr);
+      float* dv_row = drop ? a.discard : slab_row<4>(a, a.dv, a.ldv, slab, N, rr);
+      float* dk_row = drop ? a.discard : slab_row<4>(a, a.dk, a.ldk, slab, N, rr);
       const Pending pq{reinterpret_cast<float4*>(dq_row) + part, dqa, a.scale};
       float acc[16];
 #pragma unroll
@@ -715,11 +753,18 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH> a) {
   }
 }
 
-template <int MH, bool CLS>
+template <int MH, bool CLS, bool STR>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
                     float* discard, hipStream_t stream) {
-  Args<MH> a;
+  Args<MH, STR> a;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.ldo = p.ldo;
+  a.ldq = p.ldq;
+  a.ldk = p.ldk;
+  a.ldv = p.ldv;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
@@ -737,7 +782,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
   a.blocks = plan_blocks(p.N, p.H, a.rec);
   const size_t lds = static_cast<size_t>(p.N) * kLdsPerRow + kTableBytes;
-  auto kern = bwd_slab_bf16_kernel<MH, CLS>;
+  auto kern = bwd_slab_bf16_kernel<MH, CLS, STR>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       kMaxRowsBwd * kLdsPerRow + kTableBytes);
@@ -757,14 +802,18 @@ bool bwd_slab_bf16_fits(const Problem& p) {
 hipError_t launch_bwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,
                                 float* dv, float* discard, hipStream_t stream) {
-  if (p.cls) {
-    if (p.H <= kSmallHeads)
-      return launch_t<kSmallHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, discard, stream);
-    return launch_t<kMaxHeads, true>(p, q, k, v, lse, dout, dq, dk, dv, discard, stream);
+  const bool small = p.H <= kSmallHeads;
+#define FIBATT_BWD_SLAB(CLS, STR)                                                              \
+  return small ? launch_t<kSmallHeads, CLS, STR>(p, q, k, v, lse, dout, dq, dk, dv, discard,   \
+                                                 stream)                                       \
+               : launch_t<kMaxHeads, CLS, STR>(p, q, k, v, lse, dout, dq, dk, dv, discard, stream)
+  if (p.strided) {
+    if (p.cls) FIBATT_BWD_SLAB(true, true);
+    FIBATT_BWD_SLAB(false, true);
   }
-  if (p.H <= kSmallHeads)
-    return launch_t<kSmallHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, nullptr, stream);
-  return launch_t<kMaxHeads, false>(p, q, k, v, lse, dout, dq, dk, dv, nullptr, stream);
+  if (p.cls) FIBATT_BWD_SLAB(true, false);
+  FIBATT_BWD_SLAB(false, false);
+#undef FIBATT_BWD_SLAB
 }
 
 }  // namespace fibatt

@@ -52,8 +52,11 @@ constexpr int kGroups = (kMaxPos + 3) / 4;                       // distance gro
 // Per-head record: bytes 0..11 the ascending positive distances, byte 12
 // their count, byte 13 whether 0 is a distance.  Built on the host; with at
 // most 16 heads the whole table is 256 bytes of kernel arguments.
-template <int MH>
+// With STR the rows of Q, K, V and O follow their layouts (strided views,
+// e.g. of a fused QKV projection); without it they are dense [B, H, N, 64].
+template <int MH, bool STR>
 struct Args {
+  static constexpr bool kStrided = STR;
   const char* q;
   const char* k;
   const char* v;
@@ -64,8 +67,21 @@ struct Args {
   int slabs;
   float scale_log2;
   uint64_t blocks;  // row block of wave w in bits 4 w .. 4 w + 3
+  Layout lq, lk, lv, lo;
   u32x4 rec[MH];
 };
+
+// Byte address of row r of a slab of tensor x (layout l) for either kind
+// of arguments.
+template <typename A>
+__device__ __forceinline__ const char* slab_row(const A& a, const char* x, const Layout& l,
+                                                size_t slab, int N, int r) {
+  if constexpr (A::kStrided) {
+    return x + l.slab_bytes(slab, a.H, 2) + static_cast<size_t>(r) * l.row_bytes(2);
+  } else {
+    return x + (slab * static_cast<size_t>(N) + r) * kRowBytes;
+  }
+}
 
 struct Prefetch {
   u32x4 k[kChunksF];
@@ -80,18 +96,34 @@ struct Prefetch {
 template <typename A>
 __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, int tid, int row,
                                                int part, bool idle, Prefetch& pf) {
-  const size_t base = slab * static_cast<size_t>(N) * kRowBytes;
-  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
-  const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + base);
   const int last = idle ? 0 : N * (kRowBytes / 16) - 1;
+  if constexpr (A::kStrided) {
+    const char* ks = slab_row(a, a.k, a.lk, slab, N, 0);
+    const char* vs = slab_row(a, a.v, a.lv, slab, N, 0);
+    const char* qs = slab_row(a, a.q, a.lq, slab, N, 0);
+    const size_t rk = a.lk.row_bytes(2), rv = a.lv.row_bytes(2), rq = a.lq.row_bytes(2);
 #pragma unroll
-  for (int c = 0; c < kChunksF; ++c) {
-    int idx = tid + c * kThreadsF;
-    idx = idx < last ? idx : last;
-    pf.k[c] = __builtin_nontemporal_load(ks + idx);
-    pf.v[c] = __builtin_nontemporal_load(vs + idx);
-    pf.q[c] = __builtin_nontemporal_load(qs + idx);
+    for (int c = 0; c < kChunksF; ++c) {
+      int idx = tid + c * kThreadsF;
+      idx = idx < last ? idx : last;
+      const int r = idx >> 3, ch = idx & 7;  // row, 16-byte chunk
+      pf.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + r * rk) + ch);
+      pf.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + r * rv) + ch);
+      pf.q[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qs + r * rq) + ch);
+    }
+  } else {
+    const size_t base = slab * static_cast<size_t>(N) * kRowBytes;
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + base);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + base);
+    const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + base);
+#pragma unroll
+    for (int c = 0; c < kChunksF; ++c) {
+      int idx = tid + c * kThreadsF;
+      idx = idx < last ? idx : last;
+      pf.k[c] = __builtin_nontemporal_load(ks + idx);
+      pf.v[c] = __builtin_nontemporal_load(vs + idx);
+      pf.q[c] = __builtin_nontemporal_load(qs + idx);
+    }
   }
 }
 
@@ -270,7 +302,7 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
   }
   settle(pf);
   if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
-    u32x4* orow = reinterpret_cast<u32x4*>(a.o + static_cast<size_t>(slab) * N * kRowBytes);
+    u32x4* orow = reinterpret_cast<u32x4*>(const_cast<char*>(slab_row(a, a.o, a.lo, slab, N, 0)));
     orow[part] = u32x4{w[0], w[1], w[2], w[3]};
     orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
     if (lane == 0) a.lse[static_cast<size_t>(slab) * N] = (mw * c + fast_log2(l)) * kLn2;
@@ -368,7 +400,7 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   // commit after the next barrier waits for nothing.
   settle(pf);
   const size_t grow = static_cast<size_t>(slab) * N + rr;
-  u32x4* orow = reinterpret_cast<u32x4*>(a.o + grow * kRowBytes);
+  u32x4* orow = reinterpret_cast<u32x4*>(const_cast<char*>(slab_row(a, a.o, a.lo, slab, N, rr)));
   // With the class-token mask row 0 is the dense wave's (N <= 240).
   if (!(CLS && rr == 0 && N <= 16 * kDenseSlots)) {
     orow[part] = u32x4{w[0], w[1], w[2], w[3]};
@@ -377,8 +409,8 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   }
 }
 
-template <int MH, bool CLS>
-__global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
+template <int MH, bool CLS, bool STR>
+__global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH, STR> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -435,10 +467,14 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH> a) {
   }
 }
 
-template <int MH, bool CLS>
+template <int MH, bool CLS, bool STR>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, void* o,
                     float* lse, hipStream_t stream) {
-  Args<MH> a;
+  Args<MH, STR> a;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
@@ -451,7 +487,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   if (!pack_records(p, a.rec, MH)) return hipErrorInvalidValue;
   a.blocks = plan_blocks(p.N, p.H, a.rec);
   const size_t lds = static_cast<size_t>(p.N) * (2 * kBf16Stride + kF32Stride);
-  auto kern = fwd_slab_bf16_kernel<MH, CLS>;
+  auto kern = fwd_slab_bf16_kernel<MH, CLS, STR>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -473,12 +509,20 @@ bool fwd_slab_bf16_fits(const Problem& p) {
 
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream) {
-  if (p.cls) {
-    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, true>(p, q, k, v, o, lse, stream);
-    return launch_t<kMaxHeads, true>(p, q, k, v, o, lse, stream);
+  if (p.strided) {
+    if (p.cls) {
+      if (p.H <= kSmallHeads) return launch_t<kSmallHeads, true, true>(p, q, k, v, o, lse, stream);
+      return launch_t<kMaxHeads, true, true>(p, q, k, v, o, lse, stream);
+    }
+    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, false, true>(p, q, k, v, o, lse, stream);
+    return launch_t<kMaxHeads, false, true>(p, q, k, v, o, lse, stream);
   }
-  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, false>(p, q, k, v, o, lse, stream);
-  return launch_t<kMaxHeads, false>(p, q, k, v, o, lse, stream);
+  if (p.cls) {
+    if (p.H <= kSmallHeads) return launch_t<kSmallHeads, true, false>(p, q, k, v, o, lse, stream);
+    return launch_t<kMaxHeads, true, false>(p, q, k, v, o, lse, stream);
+  }
+  if (p.H <= kSmallHeads) return launch_t<kSmallHeads, false, false>(p, q, k, v, o, lse, stream);
+  return launch_t<kMaxHeads, false, false>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace fibatt

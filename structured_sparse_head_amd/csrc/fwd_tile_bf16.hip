@@ -244,7 +244,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
 }  // namespace
 
 bool fwd_tile_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
+  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128) && !p.strided;
 }
 
 template <bool CLS>

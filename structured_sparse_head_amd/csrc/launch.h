@@ -66,15 +66,15 @@ bool fwd_slab_bf16_dense_row(const Problem& p);
 hipError_t launch_fwd_slab_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream);
 // Forward for bf16, d_h = 64 and any N, query tiles read from global memory
-// (the default when the persistent kernel does not fit).
+// (the default for dense tensors when the persistent kernel does not fit).
 bool fwd_tile_bf16_fits(const Problem& p);
 hipError_t launch_fwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 void* o, float* lse, hipStream_t stream);
 bool bwd_slab_fits(const Problem& p);
 
 // Backward for bf16, d_h = 64 and any N on 64-row tiles (two launches; D
-// goes through the workspace); the default when the persistent kernel does
-// not fit.
+// goes through the workspace); the default for dense tensors when the
+// persistent kernel does not fit.
 bool bwd_tile_bf16_fits(const Problem& p);
 hipError_t launch_bwd_tile_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                 const float* lse, const void* dout, float* dq, float* dk,

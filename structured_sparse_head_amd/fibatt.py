@@ -27,7 +27,7 @@ EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fiba
             "fibatt_bwd_cls", "fibatt_fwd_cls_workspace_floats",
             "fibatt_bwd_cls_workspace_floats", "fibatt_fwd_table", "fibatt_bwd_table",
             "fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats",
-            "fibatt_last_error")
+            "fibatt_fwd_strided", "fibatt_bwd_strided", "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -62,6 +62,14 @@ class TableDesc(ctypes.Structure):
         ("offs", ctypes.POINTER(ctypes.c_int32)),
         ("offs_device", ctypes.c_void_p),
     ]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64)]
+
+
+class Layouts(ctypes.Structure):
+    _fields_ = [(n, Layout) for n in ("q", "k", "v", "o", "dout", "dq", "dk", "dv")]
 
 
 _lib = None
@@ -107,6 +115,12 @@ def lib() -> ctypes.CDLL:
     for name in ("fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats"):
         getattr(L, name).argtypes = [ctypes.POINTER(TableDesc)]
         getattr(L, name).restype = ctypes.c_int64
+    L.fibatt_fwd_strided.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                     ctypes.POINTER(Layouts)] + [vp] * 7
+    L.fibatt_fwd_strided.restype = ctypes.c_int
+    L.fibatt_bwd_strided.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
+                                     ctypes.POINTER(Layouts)] + [vp] * 10
+    L.fibatt_bwd_strided.restype = ctypes.c_int
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -178,6 +192,9 @@ class Fibottention:
     cls=True selects the class-token mask (fibatt_fwd_cls / fibatt_bwd_cls):
     token 0 attends, and is attended by, every token.
     Keeps the marshalled descriptor so repeated calls cost one ctypes call.
+    Tensors are [B, H, N, d_h]; contiguous ones go to fibatt_fwd / fibatt_bwd
+    (or the class-token pair), any other views with unit inner stride to
+    fibatt_fwd_strided / fibatt_bwd_strided with their strides.
     """
 
     def __init__(self, B: int, H: int, N: int, d_h: int, dtype: torch.dtype,
@@ -202,6 +219,16 @@ class Fibottention:
                 raise ValueError("tensors must be contiguous device tensors")
         return [None if t is None else t.data_ptr() for t in tensors]
 
+    @staticmethod
+    def _layout(t) -> Layout:
+        if not t.is_cuda or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("strided tensors must be 4-d device views with unit inner stride")
+        return Layout(t.stride(0), t.stride(1), t.stride(2))
+
+    @staticmethod
+    def _strided(*tensors) -> bool:
+        return any(t is not None and not t.is_contiguous() for t in tensors)
+
     def _floats(self, fn) -> int:
         n = fn(self._dp)
         if n < 0:
@@ -224,10 +251,23 @@ class Fibottention:
             if tuple(t.shape) != self.shape or t.dtype != self.dtype:
                 raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
         if o is None:
-            o = torch.empty_like(q)
+            o = torch.empty(self.shape, dtype=self.dtype, device=q.device)
         if lse is None:
             lse = torch.empty(self.shape[:3], dtype=torch.float32, device=q.device)
-        if self.cls:
+        if self._strided(q, k, v, o):
+            if tuple(o.shape) != self.shape or o.dtype != self.dtype:
+                raise ValueError(f"o must be {self.shape} {self.dtype}")
+            ls = Layouts()
+            ls.q, ls.k, ls.v, ls.o = (self._layout(t) for t in (q, k, v, o))
+            n = self.fwd_workspace_floats()
+            if workspace is None and n > 0:
+                workspace = torch.empty(n, dtype=torch.float32, device=q.device)
+            ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()] + \
+                self._args(lse, workspace)
+            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            _check(self._lib.fibatt_fwd_strided(self._dp, int(self.cls), ctypes.byref(ls), *ptrs,
+                                                s))
+        elif self.cls:
             n = self.fwd_workspace_floats()
             if workspace is None and n > 0:
                 workspace = torch.empty(n, dtype=torch.float32, device=q.device)
@@ -253,8 +293,20 @@ class Fibottention:
         dv = mk() if dv is None else dv
         if workspace is None:
             workspace = torch.empty(self.workspace_floats(), dtype=torch.float32, device=dev)
-        ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
         s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        if self._strided(q, k, v, do, dq, dk, dv):
+            for t in (dq, dk, dv):
+                if tuple(t.shape) != self.shape or t.dtype != torch.float32:
+                    raise ValueError(f"dq, dk, dv must be {self.shape} float32")
+            ls = Layouts()
+            ls.q, ls.k, ls.v, ls.dout, ls.dq, ls.dk, ls.dv = (
+                self._layout(t) for t in (q, k, v, do, dq, dk, dv))
+            ptrs = [t.data_ptr() for t in (q, k, v)] + self._args(lse) + \
+                [t.data_ptr() for t in (do, dq, dk, dv)] + self._args(workspace)
+            _check(self._lib.fibatt_bwd_strided(self._dp, int(self.cls), ctypes.byref(ls), *ptrs,
+                                                s))
+            return dq, dk, dv
+        ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
         fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
         _check(fn(self._dp, *ptrs, s))
         return dq, dk, dv
@@ -359,3 +411,57 @@ class FibottentionFunction(torch.autograd.Function):
         q, k, v, lse = ctx.saved_tensors
         dq, dk, dv = ctx.op.backward(q, k, v, lse, do.to(q.dtype).contiguous())
         return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
+
+
+class FibottentionQKVFunction(torch.autograd.Function):
+    """autograd wrapper over a fused projection: qkv [B, N, 3, H, d_h] (Q, K
+    and V of every head side by side, as X [W^Q | W^K | W^V] lays them out)
+    -> O [B, N, H, d_h], ready for the output projection.  The kernels read
+    and write the strided head views directly (fibatt_fwd_strided /
+    fibatt_bwd_strided), so no head split or merge copies are made; the
+    gradient comes back as one fp32 [B, N, 3, H, d_h] buffer.  Where the
+    library does not take strided tensors (the class-token mask beyond the
+    bf16 d_h = 64 kernels' sequence lengths) the views are copied to dense
+    tensors first."""
+
+    @staticmethod
+    def _heads(t):
+        return [t[:, :, i].permute(0, 2, 1, 3) for i in range(3)]
+
+    @staticmethod
+    def forward(ctx, qkv, a, b, w, cls=False):
+        B, N, three, H, d = qkv.shape
+        if three != 3 or not qkv.is_contiguous():
+            raise ValueError("qkv must be a contiguous [B, N, 3, H, d_h] tensor")
+        op = Fibottention(B, H, N, d, qkv.dtype, a, b, w, cls=cls)
+        q, k, v = FibottentionQKVFunction._heads(qkv)
+        o = torch.empty(B, N, H, d, dtype=qkv.dtype, device=qkv.device)
+        try:
+            _, lse = op.forward(q, k, v, o=o.permute(0, 2, 1, 3))
+        except FibattError as e:
+            if e.code != E_UNSUPPORTED:
+                raise
+            od, lse = op.forward(q.contiguous(), k.contiguous(), v.contiguous())
+            o.copy_(od.permute(0, 2, 1, 3))
+        ctx.op = op
+        ctx.save_for_backward(qkv, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        qkv, lse = ctx.saved_tensors
+        B, N, _, H, d = qkv.shape
+        q, k, v = FibottentionQKVFunction._heads(qkv)
+        do = do.to(qkv.dtype).contiguous().permute(0, 2, 1, 3)
+        g = torch.empty(B, N, 3, H, d, dtype=torch.float32, device=qkv.device)
+        dq, dk, dv = FibottentionQKVFunction._heads(g)
+        try:
+            ctx.op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
+        except FibattError as e:
+            if e.code != E_UNSUPPORTED:
+                raise
+            grads = ctx.op.backward(q.contiguous(), k.contiguous(), v.contiguous(), lse,
+                                    do.contiguous())
+            for dst, src in zip((dq, dk, dv), grads):
+                dst.copy_(src)
+        return g.to(qkv.dtype), None, None, None, None

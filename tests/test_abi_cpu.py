@@ -324,3 +324,116 @@ def test_table_binding_checks_shapes():
     with pytest.raises(ValueError):
         op._shapes(torch.zeros(2, 3, 65, 64, dtype=torch.bfloat16))
     op._shapes(torch.zeros(2, 3, 65, 64))  # matching shape, dtype and device
+
+
+# --------------------------------------------------------------------------
+# Strided entry points: layout validation (no launch)
+# --------------------------------------------------------------------------
+
+def _dense_layouts(B=2, H=3, N=65, d=64):
+    ls = fb.Layouts()
+    for name, _ in fb.Layouts._fields_:
+        setattr(ls, name, fb.Layout(H * N * d, N * d, d))
+    return ls
+
+
+def _fwd_s(desc, ls, cls=0, ptrs=None):
+    p = [GOOD] * 6 if ptrs is None else ptrs
+    return fa.lib().fibatt_fwd_strided(ctypes.byref(desc), cls,
+                                       ctypes.byref(ls) if ls is not None else None, *p, None)
+
+
+def _bwd_s(desc, ls, cls=0, ptrs=None):
+    p = [GOOD] * 9 if ptrs is None else ptrs
+    return fa.lib().fibatt_bwd_strided(ctypes.byref(desc), cls,
+                                       ctypes.byref(ls) if ls is not None else None, *p, None)
+
+
+@pytest.mark.parametrize("field,layout,msg", [
+    ("q", (-64, 64, 64), b"strides must be >= 0"),
+    ("k", (0, 0, 32), b"sn = 32 must be >= d_h"),
+    ("v", (4, 64, 64), b"multiples of 8"),      # bf16: 16 bytes = 8 elements
+    ("o", ((1 << 62) - 8, 64, 64), b"2^62"),
+])
+def test_strided_forward_rejects_bad_layouts(field, layout, msg):
+    c = _Case()
+    ls = _dense_layouts()
+    setattr(ls, field, fb.Layout(*layout))
+    assert _fwd_s(c.desc, ls) == fa.E_INVAL
+    assert msg in fa.lib().fibatt_last_error()
+
+
+@pytest.mark.parametrize("field,layout,msg", [
+    ("dout", (8, 64, 63), b"sn = 63"),
+    ("dq", (2, 64, 64), b"multiples of 4"),      # fp32 gradients: 4 elements
+    ("dk", (0, -1, 64), b">= 0"),
+    ("dv", (0, 1 << 60, 1 << 60), b"2^62"),
+])
+def test_strided_backward_rejects_bad_layouts(field, layout, msg):
+    c = _Case()
+    ls = _dense_layouts()
+    setattr(ls, field, fb.Layout(*layout))
+    assert _bwd_s(c.desc, ls) == fa.E_INVAL
+    assert msg in fa.lib().fibatt_last_error()
+
+
+def test_strided_layouts_of_unused_tensors_are_ignored():
+    c = _Case(dtype=fa.F32)
+    ls = _dense_layouts()
+    ls.o = fb.Layout(-1, -1, -1)       # the backward does not read o
+    ls.dq = fb.Layout(-1, -1, -1)      # the forward does not read dq, dk, dv, dout
+    ls.dout = fb.Layout(-1, -1, -1)
+    # both then fail on a later check (a NULL pointer), not on the layouts
+    assert _fwd_s(c.desc, _with(ls, o=fb.Layout(3 * 65 * 64, 65 * 64, 64)),
+                  ptrs=[GOOD, GOOD, GOOD, GOOD, None, GOOD]) == fa.E_INVAL
+    assert b"lse is NULL" in fa.lib().fibatt_last_error()
+    ls2 = _with(_dense_layouts(), o=fb.Layout(-1, -1, -1))
+    assert _bwd_s(c.desc, ls2, ptrs=[GOOD] * 8 + [None]) == fa.E_INVAL
+    assert b"workspace is NULL" in fa.lib().fibatt_last_error()
+
+
+def _with(ls, **kw):
+    out = fb.Layouts()
+    for name, _ in fb.Layouts._fields_:
+        setattr(out, name, kw.get(name, getattr(ls, name)))
+    return out
+
+
+def test_strided_entry_points_reject_bad_arguments():
+    c = _Case()
+    ls = _dense_layouts()
+    assert _fwd_s(c.desc, None) == fa.E_INVAL
+    assert _bwd_s(c.desc, None) == fa.E_INVAL
+    assert _fwd_s(c.desc, ls, cls=2) == fa.E_INVAL
+    assert _bwd_s(c.desc, ls, cls=-1) == fa.E_INVAL
+    for i in range(5):
+        p = [GOOD] * 6
+        p[i] = GOOD + 4
+        assert _fwd_s(c.desc, ls, ptrs=p) == fa.E_INVAL
+        assert b"aligned" in fa.lib().fibatt_last_error()
+    bad = _Case(w=[65, 66, 65])
+    assert _fwd_s(bad.desc, ls) == fa.E_INVAL
+
+
+def test_strided_class_token_only_on_fused_shapes():
+    # a fused QKV layout: [B, N, 3, H, d]
+    def qkv(B, H, N, d):
+        ls = _dense_layouts(B, H, N, d)
+        for name in ("q", "k", "v"):
+            setattr(ls, name, fb.Layout(3 * N * H * d, d, 3 * H * d))
+        for name in ("o", "dout", "dq", "dk", "dv"):
+            setattr(ls, name, fb.Layout(N * H * d, d, H * d))
+        return ls
+    for N, fwd_ok, bwd_ok in ((241, False, False), (240, None, False), (202, None, False)):
+        c = _Case(N=N, w=[N] * 3)
+        ls = qkv(2, 3, N, 64)
+        if fwd_ok is False:
+            assert _fwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
+            assert b"N <= 240" in fa.lib().fibatt_last_error()
+        assert _bwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
+        assert b"N <= 201" in fa.lib().fibatt_last_error()
+    for kw in (dict(dtype=fa.F32), dict(d_h=128)):
+        c = _Case(**kw)
+        ls = qkv(2, 3, 65, kw.get("d_h", 64))
+        assert _fwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
+        assert _bwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED

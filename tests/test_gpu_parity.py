@@ -328,6 +328,10 @@ BLOCK = [
     ("bf16 class token modified", 2, 197, 768, 12, torch.bfloat16, True, True),
     ("bf16 class token", 2, 197, 768, 12, torch.bfloat16, True, False),
     ("fp32 d128 N300", 1, 300, 512, 4, torch.float32, False, False),
+    # strided views on the general kernels; the class-token mask beyond the
+    # fused kernels' lengths goes through dense copies
+    ("bf16 d64 N300", 1, 300, 256, 4, torch.bfloat16, False, False),
+    ("bf16 class token d64 N300", 1, 300, 256, 4, torch.bfloat16, True, False),
 ]
 # Tolerance of a whole layer, relative to the largest reference magnitude of
 # each tensor: fp32 1e-4; bf16 2e-2 (Q, K, V, Z and O are each rounded to
@@ -371,6 +375,108 @@ def test_attention_layer(case):
     _say(f"    max-abs error / max(1, max |ref|): {rel}")
     for n, e in rel.items():
         assert e <= BLOCK_TOL[dtype], (n, e)
+
+
+STRIDED = [
+    # (name, B, H, N, d, dtype, cls, layout): "qkv" = Q, K, V as views of one
+    # [B, N, 3, H, d] buffer, O and dO [B, N, H, d], dQ/dK/dV views of one
+    # fp32 [B, N, 3, H, d] buffer; "padded" = every tensor a view of its own
+    # [B, H + 1, N, d + 16] buffer at head 1, element 8.
+    ("bf16 vit N197 H12 qkv", 2, 12, 197, 64, torch.bfloat16, False, "qkv"),
+    ("bf16 vit N197 H12 qkv cls", 2, 12, 197, 64, torch.bfloat16, True, "qkv"),
+    ("bf16 N201 H5 padded cls", 2, 5, 201, 64, torch.bfloat16, True, "padded"),
+    ("bf16 N33 H3 padded", 3, 3, 33, 64, torch.bfloat16, False, "padded"),
+    ("bf16 N1 H3 qkv cls", 2, 3, 1, 64, torch.bfloat16, True, "qkv"),
+    ("bf16 N13 H17 padded cls", 2, 17, 13, 64, torch.bfloat16, True, "padded"),
+    ("bf16 N240 H4 qkv", 1, 4, 240, 64, torch.bfloat16, False, "qkv"),
+    ("bf16 N256 H4 padded", 1, 4, 256, 64, torch.bfloat16, False, "padded"),
+    ("bf16 N600 H3 qkv", 1, 3, 600, 64, torch.bfloat16, False, "qkv"),
+    ("bf16 d128 N150 H3 padded", 1, 3, 150, 128, torch.bfloat16, False, "padded"),
+    ("fp32 N197 H4 qkv", 1, 4, 197, 64, torch.float32, False, "qkv"),
+    ("fp32 d128 N90 H3 padded", 2, 3, 90, 128, torch.float32, False, "padded"),
+    ("bf16 N2000 H2 qkv", 1, 2, 2000, 64, torch.bfloat16, False, "qkv"),
+]
+
+
+def _strided_views(kind, B, H, N, d, dtype, dev, count):
+    """`count` views of shape [B, H, N, d] and their backing buffers (NaN)."""
+    if kind == "qkv" and count == 3:
+        buf = torch.full((B, N, 3, H, d), float("nan"), dtype=dtype, device=dev)
+        return [buf[:, :, i].permute(0, 2, 1, 3) for i in range(3)], [buf]
+    if kind == "qkv":
+        bufs = [torch.full((B, N, H, d), float("nan"), dtype=dtype, device=dev)
+                for _ in range(count)]
+        return [t.permute(0, 2, 1, 3) for t in bufs], bufs
+    bufs = [torch.full((B, H + 1, N, d + 16), float("nan"), dtype=dtype, device=dev)
+            for _ in range(count)]
+    return [t[:, 1:, :, 8:8 + d] for t in bufs], bufs
+
+
+@pytest.mark.parametrize("case", STRIDED, ids=[c[0] for c in STRIDED])
+@pytest.mark.parametrize("path", [None, "slab", "stream"])
+def test_strided_tensors(case, path):
+    name, B, H, N, d, dtype, cls, kind = case
+    if path == "slab" and 2 * N * d * (2 if dtype == torch.bfloat16 else 4) + 8 * N > SLAB_LDS:
+        pytest.skip("shape exceeds the LDS slab budget; the slab variant rejects it")
+    if cls and path is not None:
+        pytest.skip("the class-token mask takes strided tensors in the fused kernels only")
+    _say(f"case: strided {name} B={B} H={H} N={N} d={d} {dtype} cls={cls} path={path}")
+    _set_path(path)
+    try:
+        dev = torch.device("cuda:0")
+        inp = workloads.random_case(777 + N, B, H, N, d, dtype)
+        a, b, w, F = _heads(H, N)
+        (q, k, v), in_bufs = _strided_views(kind, B, H, N, d, dtype, dev, 3)
+        (do,), do_bufs = _strided_views(kind, B, H, N, d, dtype, dev, 1)
+        for view, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
+            view.copy_(inp[n])
+        assert not q.is_contiguous() and q.data_ptr() % 16 == 0
+        (o,), o_bufs = _strided_views(kind, B, H, N, d, dtype, dev, 1)
+        (dq, dk, dv), g_bufs = _strided_views(kind, B, H, N, d, torch.float32, dev, 3)
+        op = fa.Fibottention(B, H, N, d, dtype, a, b, w, cls=cls)
+        _, lse = op.forward(q, k, v, o=o)
+        op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        gpu = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+        _compare(gpu, inp, F, TOL[dtype], cls=cls)
+        # nothing outside the output rows was written
+        for views, bufs in (((o,), o_bufs), ((dq, dk, dv), g_bufs)):
+            marks = [t.clone() for t in bufs]
+            for t in views:
+                t.fill_(0)
+            for t, m in zip(bufs, marks):
+                keep = t != 0
+                assert torch.isnan(m[keep]).all(), "a write outside the output rows"
+        # the same kernels on dense copies give the same bits
+        if path is not None or dtype == torch.float32 or (d == 64 and N <= 201):
+            dense = _gpu_run(inp, a, b, w, cls=cls)
+            for n in dense:
+                assert torch.equal(dense[n], gpu[n]), n
+    finally:
+        _set_path(None)
+
+
+def test_strided_class_token_beyond_fused_lengths_is_refused():
+    _say("case: strided class-token mask N=241 (forward) / N=202 (backward) refused")
+    dev = torch.device("cuda:0")
+    for N, fwd_refused in ((241, True), (202, False)):
+        a, b, w, F = _heads(3, N)
+        (q, k, v), _ = _strided_views("qkv", 1, 3, N, 64, torch.bfloat16, dev, 3)
+        for t in (q, k, v):
+            t.zero_()
+        (o,), _ = _strided_views("qkv", 1, 3, N, 64, torch.bfloat16, dev, 1)
+        op = fa.Fibottention(1, 3, N, 64, torch.bfloat16, a, b, w, cls=True)
+        if fwd_refused:
+            with pytest.raises(fa.FibattError) as ei:
+                op.forward(q, k, v, o=o)
+            assert ei.value.code == fa.E_UNSUPPORTED
+            continue
+        _, lse = op.forward(q, k, v, o=o)
+        (dq, dk, dv), _ = _strided_views("qkv", 1, 3, N, 64, torch.float32, dev, 3)
+        with pytest.raises(fa.FibattError) as ei:
+            op.backward(q, k, v, lse, o, dq=dq, dk=dk, dv=dv)
+        assert ei.value.code == fa.E_UNSUPPORTED
+    torch.cuda.synchronize()
 
 
 def _table(lists):

@@ -248,15 +248,11 @@ typedef struct {
  * fibatt_bwd (cls = 0) or fibatt_fwd_cls / fibatt_bwd_cls (cls = 1).
  * Workspaces (fp32 elements): forward none with cls = 0 (may be NULL),
  * fibatt_fwd_cls_workspace_floats(desc) with cls = 1 (0, and then NULL is
- * allowed, whenever the tensors are strided); backward
- * fibatt_bwd_workspace_floats(desc) (cls = 0) or
- * fibatt_bwd_cls_workspace_floats(desc) (cls = 1).  The bf16
- * d_h = 64 kernels for N <= 256 (forward) and N <= 201 (backward) read and
- * write strided rows at full speed; other shapes run the general kernels
- * (bf16 beyond those N is slower than with dense tensors).  Errors: as
- * fibatt_fwd, plus E_INVAL for a bad layout or cls not 0/1, and
- * E_UNSUPPORTED for cls = 1 outside N <= 240 (forward) or N <= 201
- * (backward) with bf16 and d_h = 64. */
+ * allowed, for N <= 1024); backward fibatt_bwd_workspace_floats(desc)
+ * (cls = 0) or fibatt_bwd_cls_workspace_floats(desc) (cls = 1).  Every
+ * kernel family reads and writes strided rows; the kernels chosen are the
+ * same as for dense tensors of that shape.  Errors: as fibatt_fwd, plus
+ * E_INVAL for a bad layout or cls not 0/1. */
 int fibatt_fwd_strided(const fibatt_desc* desc, int32_t cls,
                        const fibatt_layouts* layouts, const void* q,
                        const void* k, const void* v, void* o, float* lse,

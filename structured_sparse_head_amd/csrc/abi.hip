@@ -444,12 +444,6 @@ int fibatt_fwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layout
   const fibatt::Path path = path_from_env();
   hipError_t e;
   if (cls) {
-    // Only the fused kernel computes the dense row on strided rows.
-    p.cls = true;
-    if (p.strided && !(path == fibatt::Path::kAuto && fibatt::fwd_slab_bf16_fits(p) &&
-                       fibatt::fwd_slab_bf16_dense_row(p)))
-      return fail(FIBATT_E_UNSUPPORTED,
-                  "strided tensors with cls = 1 need bf16, d_h = 64 and N <= 240 (forward)");
     e = fibatt::launch_fwd_cls(p, q, k, v, o, lse, workspace, static_cast<hipStream_t>(stream),
                                path);
   } else {
@@ -477,10 +471,6 @@ int fibatt_bwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layout
   const fibatt::Path path = path_from_env();
   hipError_t e;
   if (cls) {
-    p.cls = true;
-    if (p.strided && !(path == fibatt::Path::kAuto && fibatt::bwd_slab_bf16_fits(p)))
-      return fail(FIBATT_E_UNSUPPORTED,
-                  "strided tensors with cls = 1 need bf16, d_h = 64 and N <= 201 (backward)");
     e = fibatt::launch_bwd_cls(p, q, k, v, lse, dout, dq, dk, dv, workspace,
                                static_cast<hipStream_t>(stream), path);
   } else {

@@ -48,8 +48,28 @@ struct BwdTileArgs {
   int chunk;
   float c;      // log2(e) / sqrt(d)
   float scale;  // 1 / sqrt(d)
+  Layout lq, lk, lv, ldo, ldq, ldk, ldv;  // row layouts (read only by the STR kernels)
   HeadTableT<MH> ht;
 };
+
+// Row r of a slab of bf16 tensor x: the layout's address with STR, else the
+// dense one (constant stride).
+template <bool STR, int kRowB>
+__device__ __forceinline__ const char* tile_row_ptr(const char* x, const Layout& l, size_t slab,
+                                                    int H, int N, int r) {
+  if constexpr (STR) return x + l.slab_bytes(slab, H, 2) + static_cast<size_t>(r) * l.row_bytes(2);
+  return x + (slab * static_cast<size_t>(N) + r) * kRowB;
+}
+
+// Row r of a slab of an fp32 output with D elements per row.
+template <bool STR, int D>
+__device__ __forceinline__ float* tile_row_f32(float* x, const Layout& l, size_t slab, int H,
+                                               int N, int r) {
+  if constexpr (STR)
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(x) + l.slab_bytes(slab, H, 4) +
+                                    static_cast<size_t>(r) * l.row_bytes(4));
+  return x + (slab * static_cast<size_t>(N) + r) * D;
+}
 
 // The head's signed displacements in LDS (thread 0 builds them), padded with
 // zeros to a whole last group; returns their count after a barrier.
@@ -95,7 +115,7 @@ __device__ __forceinline__ void frag_words(const u32x4 (&f)[2], uint32_t (&w)[8]
 // kernel, with the dense D_0 that the class-token row kernel left in the
 // workspace).  Row 0's D is that D_0; its dQ and key 0's dK and dV are
 // replaced by the dense class-token kernels afterwards.
-template <int MH, int KG, int NQ, bool CLS>
+template <int MH, int KG, int NQ, bool CLS, bool STR>
 __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -115,18 +135,18 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   const int row = tile * G::kRows + tile_row<NQ>(threadIdx.x);
   const int half = row_half<NQ>(threadIdx.x);
   const int rr = row < N ? row : N - 1;
-  const size_t base = static_cast<size_t>(slab) * N * kRowB;
   const size_t rbase = static_cast<size_t>(slab) * N;
   const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
-  const char* kbase = a.k + base + lofs;
-  const char* vbase = a.v + base + lofs;
+  const char* kbase = tile_row_ptr<STR, kRowB>(a.k, a.lk, slab, a.H, N, 0) + lofs;
+  const char* vbase = tile_row_ptr<STR, kRowB>(a.v, a.lv, slab, a.H, N, 0) + lofs;
+  const size_t rk = STR ? a.lk.row_bytes(2) : kRowB, rv = STR ? a.lv.row_bytes(2) : kRowB;
 
   uint32_t qw[8], dw[8];
   {
     u32x4 f[2];
-    load_row_q(a.q + base + static_cast<size_t>(rr) * kRowB + lofs, f);
+    load_row_q(tile_row_ptr<STR, kRowB>(a.q, a.lq, slab, a.H, N, rr) + lofs, f);
     frag_words(f, qw);
-    load_row_q(a.dout + base + static_cast<size_t>(rr) * kRowB + lofs, f);
+    load_row_q(tile_row_ptr<STR, kRowB>(a.dout, a.ldo, slab, a.H, N, rr) + lofs, f);
     frag_words(f, dw);
   }
   const float lse2 = a.lse[rbase + rr] * kLog2e;
@@ -144,9 +164,9 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       u32x4 kf[4][2], vf[4][2];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const size_t off = static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB;
-        load_row_q(kbase + off, kf[j]);
-        load_row_q(vbase + off, vf[j]);
+        const size_t r = static_cast<size_t>(clamp_row(rr + d[j], N));
+        load_row_q(kbase + r * rk, kf[j]);
+        load_row_q(vbase + r * rv, vf[j]);
       }
       float ps[4], pp[4];
 #pragma unroll
@@ -191,7 +211,7 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
       for (int j = 0; j < 4; ++j) {
         if (4 * g + j < nd) {
           u32x4 kf[2];
-          load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf);
+          load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rk, kf);
           axpy_bf16(acc, ds[j], kf);
         }
       }
@@ -202,11 +222,12 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
     load_row_q(kbase, k0f);
     axpy_bf16(acc, pq * (dpq - dd), k0f);
   }
-  store_row_f32(a.dq + (rbase + rr) * G::kD + 64 * half, part, acc, a.scale);
+  store_row_f32(tile_row_f32<STR, G::kD>(a.dq, a.ldq, slab, a.H, N, rr) + 64 * half, part, acc,
+                a.scale);
   if (part == 0 && half == 0) a.ws[rbase + rr] = dd;
 }
 
-template <int MH, int NQ, bool CLS>
+template <int MH, int NQ, bool CLS, bool STR>
 __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -226,18 +247,18 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
   const int row = tile * G::kRows + tile_row<NQ>(threadIdx.x);
   const int half = row_half<NQ>(threadIdx.x);
   const int rr = row < N ? row : N - 1;  // key row
-  const size_t base = static_cast<size_t>(slab) * N * kRowB;
   const size_t rbase = static_cast<size_t>(slab) * N;
   const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
-  const char* qbase = a.q + base + lofs;
-  const char* obase = a.dout + base + lofs;
+  const char* qbase = tile_row_ptr<STR, kRowB>(a.q, a.lq, slab, a.H, N, 0) + lofs;
+  const char* obase = tile_row_ptr<STR, kRowB>(a.dout, a.ldo, slab, a.H, N, 0) + lofs;
+  const size_t rq = STR ? a.lq.row_bytes(2) : kRowB, ro = STR ? a.ldo.row_bytes(2) : kRowB;
 
   uint32_t kw[8], vw[8];
   {
     u32x4 f[2];
-    load_row_q(a.k + base + static_cast<size_t>(rr) * kRowB + lofs, f);
+    load_row_q(tile_row_ptr<STR, kRowB>(a.k, a.lk, slab, a.H, N, rr) + lofs, f);
     frag_words(f, kw);
-    load_row_q(a.v + base + static_cast<size_t>(rr) * kRowB + lofs, f);
+    load_row_q(tile_row_ptr<STR, kRowB>(a.v, a.lv, slab, a.H, N, rr) + lofs, f);
     frag_words(f, vw);
   }
   float dk[16], dv[16];
@@ -259,9 +280,9 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
     u32x4 qf[4][2], of[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const size_t off = static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB;
-      load_row_q(qbase + off, qf[j]);
-      load_row_q(obase + off, of[j]);
+      const size_t r = static_cast<size_t>(clamp_row(rr + d[j], N));
+      load_row_q(qbase + r * rq, qf[j]);
+      load_row_q(obase + r * ro, of[j]);
     }
     float ps[4], pp[4];
 #pragma unroll
@@ -293,14 +314,20 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
     axpy_bf16(dv, p, o0f);
     axpy_bf16(dk, p * (dp - a.ws[rbase]), q0f);
   }
-  store_row_f32(a.dk + (rbase + rr) * G::kD + 64 * half, part, dk, a.scale);
-  store_row_f32(a.dv + (rbase + rr) * G::kD + 64 * half, part, dv, 1.0f);
+  store_row_f32(tile_row_f32<STR, G::kD>(a.dk, a.ldk, slab, a.H, N, rr) + 64 * half, part, dk,
+                a.scale);
+  store_row_f32(tile_row_f32<STR, G::kD>(a.dv, a.ldv, slab, a.H, N, rr) + 64 * half, part, dv,
+                1.0f);
 }
 
 template <int MH, int KG, int NQ, bool CLS>
-void launch_dq(const BwdTileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
-                     stream, a);
+void launch_dq(const BwdTileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
+  if (strided)
+    hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, a);
 }
 
 template <int MH, int NQ, bool CLS>
@@ -321,6 +348,13 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.N = p.N;
   a.scale = 1.0f / sqrtf(static_cast<float>(Geo<NQ>::kD));
   a.c = kLog2e * a.scale;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.ldo = p.ldo;
+  a.ldq = p.ldq;
+  a.ldk = p.ldk;
+  a.ldv = p.ldv;
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const long long slabs = static_cast<long long>(p.B) * p.H;
   a.tiles = (p.N + Geo<NQ>::kRows - 1) / Geo<NQ>::kRows;
@@ -333,22 +367,26 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_dq<MH, 4, NQ, CLS>(a, grid, stream);
+    launch_dq<MH, 4, NQ, CLS>(a, p.strided, grid, stream);
   else if (groups <= 8)
-    launch_dq<MH, 8, NQ, CLS>(a, grid, stream);
+    launch_dq<MH, 8, NQ, CLS>(a, p.strided, grid, stream);
   else if (groups <= 12)
-    launch_dq<MH, 12, NQ, CLS>(a, grid, stream);
+    launch_dq<MH, 12, NQ, CLS>(a, p.strided, grid, stream);
   else
-    launch_dq<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, grid, stream);
-  hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
-                     stream, a);
+    launch_dq<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, p.strided, grid, stream);
+  if (p.strided)
+    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS, true>), dim3(grid), dim3(kTileThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS, false>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool bwd_tile_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128) && !p.strided;
+  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
 }
 
 template <bool CLS>

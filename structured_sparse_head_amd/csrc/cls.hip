@@ -45,11 +45,22 @@ struct ClsArgs {
   float* ws_d;   // D per row, [slabs, N]
   float* dq0;    // dQ of row 0 per slab, [slabs, D], copied into dq last
   float* part;   // per-range partials
+  int H;
   int N;
   int splits;    // ranges per slab
   float scale_log2;
   float scale;
+  Layout lq, lk, lv, lo, ldo, ldq, ldk, ldv;  // row layouts of the tensors
 };
+
+// Row r of slab `slab` of tensor x (layout l, es-byte elements).
+__device__ __forceinline__ const char* lrow(const char* x, const Layout& l, size_t slab, int H,
+                                            int es, int r) {
+  return x + l.slab_bytes(slab, H, es) + static_cast<size_t>(r) * l.row_bytes(es);
+}
+__device__ __forceinline__ float* lrow_f32(float* x, const Layout& l, size_t slab, int H) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(x) + l.slab_bytes(slab, H, 4));
+}
 
 // Lane-group width for the per-row dot products: 64 bytes of a row per lane.
 template <typename T, int D>
@@ -90,14 +101,16 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-// Weighted sums of n rows of x (row-major [rows, D] in T, rows r0 ..):
-// out_c[e] = sum_i coef_c[i] x_{r0 + i}[e] for NC coefficient arrays (LDS).
+// Weighted sums of n rows of x (rows of D elements of T, rs bytes apart,
+// rows r0 ..): out_c[e] = sum_i coef_c[i] x_{r0 + i}[e] for NC coefficient
+// arrays (LDS).
 // Each thread takes one 16-byte chunk of a row and every KG-th row; the KG
 // partial sums of an element are added in order.  Thread e < D gets element
 // e; `red` holds KG * D floats.
 template <typename T, int D, int NT, int NC>
-__device__ __forceinline__ void rows_wsum(const char* x, int r0, int n, const float* const* coef,
-                                          float* red, float (&out)[NC]) {
+__device__ __forceinline__ void rows_wsum(const char* x, size_t rs, int r0, int n,
+                                          const float* const* coef, float* red,
+                                          float (&out)[NC]) {
   constexpr int CH = 16 / static_cast<int>(sizeof(T));  // elements per chunk
   constexpr int CPR = D / CH;                           // chunks per row
   constexpr int KG = NT / CPR;                          // row groups
@@ -108,10 +121,10 @@ __device__ __forceinline__ void rows_wsum(const char* x, int r0, int n, const fl
   for (int u = 0; u < NC; ++u)
 #pragma unroll
     for (int t = 0; t < CH; ++t) acc[u][t] = 0.f;
-  const char* base = x + static_cast<size_t>(r0) * D * sizeof(T) + c * 16;
+  const char* base = x + static_cast<size_t>(r0) * rs + c * 16;
 #pragma unroll 4
   for (int i = kg; i < n; i += KG) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(i) * D * sizeof(T));
+    const u32x4 w = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(i) * rs);
     float e[CH];
     if constexpr (sizeof(T) == 2) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -170,12 +183,14 @@ __global__ void __launch_bounds__(NT) fwd_cls_row_kernel(ClsArgs a) {
   const int k0 = sp * kSplitRows;
   const int k1 = min(N, k0 + kSplitRows);
   const int n = k1 - k0;
-  const size_t base = slab * N * Gm::kRowBytes;
+  constexpr int es = sizeof(T);
+  const char* ks = lrow(a.k, a.lk, slab, a.H, es, 0);
+  const size_t rk = a.lk.row_bytes(es);
   uint32_t qf[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.q + base, tid % G, qf);
+  frag_load_cached<T, D, G>(lrow(a.q, a.lq, slab, a.H, es, 0), tid % G, qf);
   for_rows<G, NT>(k0, k1, [&](int i, int r, int part) {
     uint32_t kf[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(r) * Gm::kRowBytes, part, kf);
+    frag_load_cached<T, D, G>(ks + static_cast<size_t>(r) * rk, part, kf);
     const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
     if (part == 0) s_w[i] = s;
   });
@@ -192,10 +207,11 @@ __global__ void __launch_bounds__(NT) fwd_cls_row_kernel(ClsArgs a) {
   l = block_sum<NT>(l, s_red);  // (its barrier also publishes s_w)
   const float* coef[1] = {s_w};
   float o[1];
-  rows_wsum<T, D, NT, 1>(a.v + base, k0, n, coef, s_red, o);
+  rows_wsum<T, D, NT, 1>(lrow(a.v, a.lv, slab, a.H, es, 0), a.lv.row_bytes(es), k0, n, coef,
+                         s_red, o);
   if (tid < D) {
     if (a.splits == 1) {
-      store_elem<T>(a.o + base, tid, o[0] / l);
+      store_elem<T>(const_cast<char*>(lrow(a.o, a.lo, slab, a.H, es, 0)), tid, o[0] / l);
       if (tid == 0) a.lse[slab * N] = (m + fast_log2(l)) * kLn2;
     } else {
       float* pp = a.part + (slab * a.splits + sp) * (D + 2);
@@ -222,8 +238,7 @@ __global__ void __launch_bounds__(D) fwd_cls_combine_kernel(ClsArgs a) {
     lsum = __builtin_fmaf(pp[s * (D + 2) + 1], w, lsum);
     o = __builtin_fmaf(pp[s * (D + 2) + 2 + tid], w, o);
   }
-  const size_t row_bytes = static_cast<size_t>(D) * sizeof(T);
-  store_elem<T>(a.o + slab * a.N * row_bytes, tid, o / lsum);
+  store_elem<T>(const_cast<char*>(lrow(a.o, a.lo, slab, a.H, sizeof(T), 0)), tid, o / lsum);
   if (tid == 0) a.lse[slab * a.N] = (mx + fast_log2(lsum)) * kLn2;
 }
 
@@ -244,15 +259,18 @@ __global__ void __launch_bounds__(NT) bwd_cls_row_kernel(ClsArgs a) {
   const int k0 = sp * kSplitRows;
   const int k1 = min(N, k0 + kSplitRows);
   const int n = k1 - k0;
-  const size_t base = slab * N * Gm::kRowBytes;
+  constexpr int es = sizeof(T);
+  const char* ks = lrow(a.k, a.lk, slab, a.H, es, 0);
+  const char* vs = lrow(a.v, a.lv, slab, a.H, es, 0);
+  const size_t rk = a.lk.row_bytes(es), rv = a.lv.row_bytes(es);
   uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.q + base, tid % G, qf);
-  frag_load_cached<T, D, G>(a.dout + base, tid % G, dof);
+  frag_load_cached<T, D, G>(lrow(a.q, a.lq, slab, a.H, es, 0), tid % G, qf);
+  frag_load_cached<T, D, G>(lrow(a.dout, a.ldo, slab, a.H, es, 0), tid % G, dof);
   const float lse2 = a.lse[slab * N] * kLog2e;
   for_rows<G, NT>(k0, k1, [&](int i, int r, int part) {
     uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.k + base + static_cast<size_t>(r) * Gm::kRowBytes, part, kf);
-    frag_load_cached<T, D, G>(a.v + base + static_cast<size_t>(r) * Gm::kRowBytes, part, vf);
+    frag_load_cached<T, D, G>(ks + static_cast<size_t>(r) * rk, part, kf);
+    frag_load_cached<T, D, G>(vs + static_cast<size_t>(r) * rv, part, vf);
     const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
     const float dp = group_sum<G>(M::dot(dof, vf));
     const float p = fast_exp2(s - lse2);
@@ -267,7 +285,7 @@ __global__ void __launch_bounds__(NT) bwd_cls_row_kernel(ClsArgs a) {
   d = block_sum<NT>(d, s_red);
   const float* coef[2] = {s_pdp, s_p};
   float ab[2];
-  rows_wsum<T, D, NT, 2>(a.k + base, k0, n, coef, s_red, ab);
+  rows_wsum<T, D, NT, 2>(ks, rk, k0, n, coef, s_red, ab);
   if (tid < D) {
     if (a.splits == 1) {
       a.dq0[slab * D + tid] = __builtin_fmaf(-d, ab[1], ab[0]) * a.scale;
@@ -313,14 +331,17 @@ __global__ void __launch_bounds__(NT) bwd_cls_col_kernel(ClsArgs a) {
   const int j0 = sp * kSplitRows;
   const int j1 = min(N, j0 + kSplitRows);
   const int n = j1 - j0;
-  const size_t base = slab * N * Gm::kRowBytes;
+  constexpr int es = sizeof(T);
+  const char* qs = lrow(a.q, a.lq, slab, a.H, es, 0);
+  const char* ds = lrow(a.dout, a.ldo, slab, a.H, es, 0);
+  const size_t rq = a.lq.row_bytes(es), rd = a.ldo.row_bytes(es);
   uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-  frag_load_cached<T, D, G>(a.k + base, tid % G, kf);
-  frag_load_cached<T, D, G>(a.v + base, tid % G, vf);
+  frag_load_cached<T, D, G>(lrow(a.k, a.lk, slab, a.H, es, 0), tid % G, kf);
+  frag_load_cached<T, D, G>(lrow(a.v, a.lv, slab, a.H, es, 0), tid % G, vf);
   for_rows<G, NT>(j0, j1, [&](int i, int r, int part) {
     uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-    frag_load_cached<T, D, G>(a.q + base + static_cast<size_t>(r) * Gm::kRowBytes, part, qf);
-    frag_load_cached<T, D, G>(a.dout + base + static_cast<size_t>(r) * Gm::kRowBytes, part, dof);
+    frag_load_cached<T, D, G>(qs + static_cast<size_t>(r) * rq, part, qf);
+    frag_load_cached<T, D, G>(ds + static_cast<size_t>(r) * rd, part, dof);
     const float lse2 = a.lse[slab * N + r] * kLog2e;
     const float dj = a.ws_d[slab * N + r];
     const float s = group_sum<G>(M::dot(qf, kf)) * a.scale_log2;
@@ -335,13 +356,13 @@ __global__ void __launch_bounds__(NT) bwd_cls_col_kernel(ClsArgs a) {
   const float* cv[1] = {s_p};
   const float* ck[1] = {s_ds};
   float sv[1], sk[1];
-  rows_wsum<T, D, NT, 1>(a.dout + base, j0, n, cv, s_red, sv);
-  rows_wsum<T, D, NT, 1>(a.q + base, j0, n, ck, s_red, sk);
+  rows_wsum<T, D, NT, 1>(ds, rd, j0, n, cv, s_red, sv);
+  rows_wsum<T, D, NT, 1>(qs, rq, j0, n, ck, s_red, sk);
   if (tid < D) {
     if (a.splits == 1) {
-      a.dk[slab * N * D + tid] = sk[0] * a.scale;
-      a.dv[slab * N * D + tid] = sv[0];
-      a.dq[slab * N * D + tid] = a.dq0[slab * D + tid];
+      lrow_f32(a.dk, a.ldk, slab, a.H)[tid] = sk[0] * a.scale;
+      lrow_f32(a.dv, a.ldv, slab, a.H)[tid] = sv[0];
+      lrow_f32(a.dq, a.ldq, slab, a.H)[tid] = a.dq0[slab * D + tid];
     } else {
       float* pp = a.part + (slab * a.splits + sp) * (2 * D);
       pp[tid] = sk[0];
@@ -360,14 +381,23 @@ __global__ void __launch_bounds__(D) bwd_cls_col_combine_kernel(ClsArgs a) {
     sk += pp[s * 2 * D + tid];
     sv += pp[s * 2 * D + D + tid];
   }
-  a.dk[slab * a.N * D + tid] = sk * a.scale;
-  a.dv[slab * a.N * D + tid] = sv;
-  a.dq[slab * a.N * D + tid] = a.dq0[slab * D + tid];
+  lrow_f32(a.dk, a.ldk, slab, a.H)[tid] = sk * a.scale;
+  lrow_f32(a.dv, a.ldv, slab, a.H)[tid] = sv;
+  lrow_f32(a.dq, a.ldq, slab, a.H)[tid] = a.dq0[slab * D + tid];
 }
 
 ClsArgs make_args(const Problem& p) {
   ClsArgs a{};
+  a.H = p.H;
   a.N = p.N;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
+  a.ldo = p.ldo;
+  a.ldq = p.ldq;
+  a.ldk = p.ldk;
+  a.ldv = p.ldv;
   a.splits = cls_splits(p);
   a.scale = 1.0f / sqrtf(static_cast<float>(p.D));
   a.scale_log2 = kLog2e * a.scale;

@@ -56,12 +56,14 @@ struct TileArgs {
   int per_xcd;  // tile order: see tile_of_block
   int chunk;
   float scale_log2;
+  Layout lq, lk, lv, lo;  // row layouts (read only by the STR kernels)
   HeadTableT<MH> ht;
 };
 
 // KG: displacement groups of four the kernel holds scores for (at least
 // the largest head's count); smaller instantiations keep fewer registers.
-template <int MH, int KG, int NQ, bool CLS>
+// STR: rows follow the layouts (else dense [B, H, N, d_h], constant strides).
+template <int MH, int KG, int NQ, bool CLS, bool STR>
 __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH> a) {
   using G = Geo<NQ>;
   constexpr int kRowB = G::kRowB;
@@ -89,16 +91,18 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   const int rr = row < N ? row : N - 1;
   const size_t base = static_cast<size_t>(slab) * N * kRowB;
   const int lofs = half * 128 + part * 16;  // this lane's bytes in a row
-  const char* kbase = a.k + base + lofs;
-  const char* vbase = a.v + base + lofs;
+  // Slab starts and row strides (bytes) of the four tensors.
+  const size_t rk = STR ? a.lk.row_bytes(2) : kRowB, rv = STR ? a.lv.row_bytes(2) : kRowB;
+  const char* kbase = (STR ? a.k + a.lk.slab_bytes(slab, a.H, 2) : a.k + base) + lofs;
+  const char* vbase = (STR ? a.v + a.lv.slab_bytes(slab, a.H, 2) : a.v + base) + lofs;
 
   uint32_t qw[8];
   {
+    const char* qrow = STR ? a.q + a.lq.slab_bytes(slab, a.H, 2) + rr * a.lq.row_bytes(2)
+                           : a.q + base + static_cast<size_t>(rr) * kRowB;
     u32x4 qf[2];
-    qf[0] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(a.q + base + static_cast<size_t>(rr) * kRowB + lofs));
-    qf[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        a.q + base + static_cast<size_t>(rr) * kRowB + lofs + 64));
+    qf[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + lofs));
+    qf[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + lofs + 64));
     qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
     qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
@@ -114,7 +118,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
                       __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, kf[g][j]);
+      load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rk, kf[g][j]);
   };
   if (0 < nd) load_k(0);
 #pragma unroll
@@ -162,7 +166,7 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
                       __builtin_amdgcn_readfirstlane(d4.z), __builtin_amdgcn_readfirstlane(d4.w)};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      load_row_q(vbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * kRowB, vf[g][j]);
+      load_row_q(vbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rv, vf[g][j]);
   };
   if (0 < nd) load_v(0);
 #pragma unroll
@@ -194,7 +198,8 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     ow[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
-  char* orow = a.o + base + static_cast<size_t>(rr) * kRowB + lofs;
+  char* orow = (STR ? a.o + a.lo.slab_bytes(slab, a.H, 2) + rr * a.lo.row_bytes(2)
+                    : a.o + base + static_cast<size_t>(rr) * kRowB) + lofs;
   *reinterpret_cast<u32x4*>(orow) = u32x4{ow[0], ow[1], ow[2], ow[3]};
   *reinterpret_cast<u32x4*>(orow + 64) = u32x4{ow[4], ow[5], ow[6], ow[7]};
   if (part == 0 && half == 0)
@@ -202,9 +207,13 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
 }
 
 template <int MH, int KG, int NQ, bool CLS>
-void launch_kg(const TileArgs<MH>& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS>), dim3(grid), dim3(kTileThreads), 0,
-                     stream, a);
+void launch_kg(const TileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
+  if (strided)
+    hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, a);
 }
 
 template <int MH, int NQ, bool CLS>
@@ -219,6 +228,10 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.H = p.H;
   a.N = p.N;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(Geo<NQ>::kD));
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
   a.ht = shrink_heads<MH>(p.heads, p.H);
   const long long slabs = static_cast<long long>(p.B) * p.H;
   a.tiles = (p.N + Geo<NQ>::kRows - 1) / Geo<NQ>::kRows;
@@ -231,20 +244,20 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
-    launch_kg<MH, 4, NQ, CLS>(a, grid, stream);
+    launch_kg<MH, 4, NQ, CLS>(a, p.strided, grid, stream);
   else if (groups <= 8)
-    launch_kg<MH, 8, NQ, CLS>(a, grid, stream);
+    launch_kg<MH, 8, NQ, CLS>(a, p.strided, grid, stream);
   else if (groups <= 12)
-    launch_kg<MH, 12, NQ, CLS>(a, grid, stream);
+    launch_kg<MH, 12, NQ, CLS>(a, p.strided, grid, stream);
   else
-    launch_kg<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, grid, stream);
+    launch_kg<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, p.strided, grid, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool fwd_tile_bf16_fits(const Problem& p) {
-  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128) && !p.strided;
+  return p.dtype == DType::kBF16 && (p.D == 64 || p.D == 128);
 }
 
 template <bool CLS>

@@ -419,10 +419,7 @@ class FibottentionQKVFunction(torch.autograd.Function):
     -> O [B, N, H, d_h], ready for the output projection.  The kernels read
     and write the strided head views directly (fibatt_fwd_strided /
     fibatt_bwd_strided), so no head split or merge copies are made; the
-    gradient comes back as one fp32 [B, N, 3, H, d_h] buffer.  Where the
-    library does not take strided tensors (the class-token mask beyond the
-    bf16 d_h = 64 kernels' sequence lengths) the views are copied to dense
-    tensors first."""
+    gradient comes back as one fp32 [B, N, 3, H, d_h] buffer."""
 
     @staticmethod
     def _heads(t):
@@ -436,13 +433,7 @@ class FibottentionQKVFunction(torch.autograd.Function):
         op = Fibottention(B, H, N, d, qkv.dtype, a, b, w, cls=cls)
         q, k, v = FibottentionQKVFunction._heads(qkv)
         o = torch.empty(B, N, H, d, dtype=qkv.dtype, device=qkv.device)
-        try:
-            _, lse = op.forward(q, k, v, o=o.permute(0, 2, 1, 3))
-        except FibattError as e:
-            if e.code != E_UNSUPPORTED:
-                raise
-            od, lse = op.forward(q.contiguous(), k.contiguous(), v.contiguous())
-            o.copy_(od.permute(0, 2, 1, 3))
+        _, lse = op.forward(q, k, v, o=o.permute(0, 2, 1, 3))
         ctx.op = op
         ctx.save_for_backward(qkv, lse)
         return o
@@ -455,13 +446,5 @@ class FibottentionQKVFunction(torch.autograd.Function):
         do = do.to(qkv.dtype).contiguous().permute(0, 2, 1, 3)
         g = torch.empty(B, N, 3, H, d, dtype=torch.float32, device=qkv.device)
         dq, dk, dv = FibottentionQKVFunction._heads(g)
-        try:
-            ctx.op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
-        except FibattError as e:
-            if e.code != E_UNSUPPORTED:
-                raise
-            grads = ctx.op.backward(q.contiguous(), k.contiguous(), v.contiguous(), lse,
-                                    do.contiguous())
-            for dst, src in zip((dq, dk, dv), grads):
-                dst.copy_(src)
+        ctx.op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
         return g.to(qkv.dtype), None, None, None, None

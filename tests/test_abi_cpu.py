@@ -413,27 +413,3 @@ def test_strided_entry_points_reject_bad_arguments():
         assert b"aligned" in fa.lib().fibatt_last_error()
     bad = _Case(w=[65, 66, 65])
     assert _fwd_s(bad.desc, ls) == fa.E_INVAL
-
-
-def test_strided_class_token_only_on_fused_shapes():
-    # a fused QKV layout: [B, N, 3, H, d]
-    def qkv(B, H, N, d):
-        ls = _dense_layouts(B, H, N, d)
-        for name in ("q", "k", "v"):
-            setattr(ls, name, fb.Layout(3 * N * H * d, d, 3 * H * d))
-        for name in ("o", "dout", "dq", "dk", "dv"):
-            setattr(ls, name, fb.Layout(N * H * d, d, H * d))
-        return ls
-    for N, fwd_ok, bwd_ok in ((241, False, False), (240, None, False), (202, None, False)):
-        c = _Case(N=N, w=[N] * 3)
-        ls = qkv(2, 3, N, 64)
-        if fwd_ok is False:
-            assert _fwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
-            assert b"N <= 240" in fa.lib().fibatt_last_error()
-        assert _bwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
-        assert b"N <= 201" in fa.lib().fibatt_last_error()
-    for kw in (dict(dtype=fa.F32), dict(d_h=128)):
-        c = _Case(**kw)
-        ls = qkv(2, 3, 65, kw.get("d_h", 64))
-        assert _fwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED
-        assert _bwd_s(c.desc, ls, cls=1) == fa.E_UNSUPPORTED

@@ -395,6 +395,12 @@ STRIDED = [
     ("fp32 N197 H4 qkv", 1, 4, 197, 64, torch.float32, False, "qkv"),
     ("fp32 d128 N90 H3 padded", 2, 3, 90, 128, torch.float32, False, "padded"),
     ("bf16 N2000 H2 qkv", 1, 2, 2000, 64, torch.bfloat16, False, "qkv"),
+    # class-token mask beyond the fused kernels: dense row/column kernels
+    ("bf16 N241 H4 qkv cls", 1, 4, 241, 64, torch.bfloat16, True, "qkv"),
+    ("bf16 N1100 H2 qkv cls (two ranges)", 1, 2, 1100, 64, torch.bfloat16, True, "qkv"),
+    ("bf16 d128 N300 H3 padded cls", 1, 3, 300, 128, torch.bfloat16, True, "padded"),
+    ("fp32 d128 N300 H2 padded cls", 1, 2, 300, 128, torch.float32, True, "padded"),
+    ("fp32 N65 H3 qkv cls", 2, 3, 65, 64, torch.float32, True, "qkv"),
 ]
 
 
@@ -418,8 +424,6 @@ def test_strided_tensors(case, path):
     name, B, H, N, d, dtype, cls, kind = case
     if path == "slab" and 2 * N * d * (2 if dtype == torch.bfloat16 else 4) + 8 * N > SLAB_LDS:
         pytest.skip("shape exceeds the LDS slab budget; the slab variant rejects it")
-    if cls and path is not None:
-        pytest.skip("the class-token mask takes strided tensors in the fused kernels only")
     _say(f"case: strided {name} B={B} H={H} N={N} d={d} {dtype} cls={cls} path={path}")
     _set_path(path)
     try:
@@ -448,35 +452,11 @@ def test_strided_tensors(case, path):
                 keep = t != 0
                 assert torch.isnan(m[keep]).all(), "a write outside the output rows"
         # the same kernels on dense copies give the same bits
-        if path is not None or dtype == torch.float32 or (d == 64 and N <= 201):
-            dense = _gpu_run(inp, a, b, w, cls=cls)
-            for n in dense:
-                assert torch.equal(dense[n], gpu[n]), n
+        dense = _gpu_run(inp, a, b, w, cls=cls)
+        for n in dense:
+            assert torch.equal(dense[n], gpu[n]), n
     finally:
         _set_path(None)
-
-
-def test_strided_class_token_beyond_fused_lengths_is_refused():
-    _say("case: strided class-token mask N=241 (forward) / N=202 (backward) refused")
-    dev = torch.device("cuda:0")
-    for N, fwd_refused in ((241, True), (202, False)):
-        a, b, w, F = _heads(3, N)
-        (q, k, v), _ = _strided_views("qkv", 1, 3, N, 64, torch.bfloat16, dev, 3)
-        for t in (q, k, v):
-            t.zero_()
-        (o,), _ = _strided_views("qkv", 1, 3, N, 64, torch.bfloat16, dev, 1)
-        op = fa.Fibottention(1, 3, N, 64, torch.bfloat16, a, b, w, cls=True)
-        if fwd_refused:
-            with pytest.raises(fa.FibattError) as ei:
-                op.forward(q, k, v, o=o)
-            assert ei.value.code == fa.E_UNSUPPORTED
-            continue
-        _, lse = op.forward(q, k, v, o=o)
-        (dq, dk, dv), _ = _strided_views("qkv", 1, 3, N, 64, torch.float32, dev, 3)
-        with pytest.raises(fa.FibattError) as ei:
-            op.backward(q, k, v, lse, o, dq=dq, dk=dk, dv=dv)
-        assert ei.value.code == fa.E_UNSUPPORTED
-    torch.cuda.synchronize()
 
 
 def _table(lists):

@@ -331,6 +331,8 @@ def main():
         "bwd": {"mean_us": bwd_ms * 1e3, "bytes": bwd_bytes,
                 "gbps": bwd_bytes / (bwd_ms * 1e-3) / 1e9},
     }
+    for kv in kernels.values():  # fraction of the 8 TB/s HBM peak, per pass
+        kv["hbm_frac"] = kv["gbps"] / HBM_PEAK_GBPS
     dom = "bwd" if bwd_ms >= fwd_ms else "fwd"
     ach = kernels[dom]["gbps"]
     step_s = ms_step * 1e-3

@@ -166,8 +166,8 @@ __device__ __forceinline__ void commit_prefetch(char* lds_k, char* lds_v, char* 
 // requested before the current dot product so LDS latency overlaps
 // arithmetic.
 template <int SGN>
-__device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, int row, int part,
-                                           int slot, int N, const uint32_t (&qw)[8],
+__device__ __forceinline__ void scores_dir(const RowSpan& ks, Dist dist, int n,
+                                           int row, int slot, int N, const uint32_t (&qw)[8],
                                            float (&s)[kGroups]) {
   // One fragment variable per distance (not a two-entry ring): a fragment
   // loaded under a condition then merges with nothing, so the compiler
@@ -175,7 +175,7 @@ __device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, 
   u32x4 kf[kMaxPos][2];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) s[g] = -INFINITY;
-  if (n > 0) load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(0), N), kf[0]);
+  if (n > 0) load_bf16_at(ks.at(SGN * dist.at(0) * kBf16Stride), kf[0]);
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     if (4 * g < n) {
@@ -185,8 +185,7 @@ __device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, 
         const int i = 4 * g + j;
         pd[j] = 0.f;
         if (i < n) {
-          if (i + 1 < n)
-            load_bf16_q(lds_k + part * 32, clamp_row(row + SGN * dist.at(i + 1), N), kf[i + 1]);
+          if (i + 1 < n) load_bf16_at(ks.at(SGN * dist.at(i + 1) * kBf16Stride), kf[i + 1]);
           pd[j] = dot_part(qw, kf[i]);
         }
       }
@@ -203,8 +202,8 @@ __device__ __forceinline__ void scores_dir(const char* lds_k, Dist dist, int n, 
 // a group into a probability, then the group's four are gathered to every
 // lane of the row.  l collects this lane's own probabilities only.
 template <int SGN>
-__device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int n, int row,
-                                               int part, int N, float c, float mc,
+__device__ __forceinline__ void accumulate_dir(const RowSpan& vs, Dist dist, int n, float c,
+                                               float mc,
                                                const float (&s)[kGroups], float& l,
                                                float (&o)[16]) {
 #pragma unroll
@@ -219,7 +218,7 @@ __device__ __forceinline__ void accumulate_dir(const char* lds_v, Dist dist, int
         const int i = 4 * g + j;
         if (i < n) {
           u32x4 vf[4];
-          load_f32_q(lds_v + part * 64, clamp_row(row + SGN * dist.at(i), N), vf);
+          load_f32_at(vs.at(SGN * dist.at(i) * kF32Stride), vf);
           axpy_q(o, p[j], vf);
         }
       }
@@ -341,8 +340,11 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   // Pass 1: raw scores Q_j . K_k for every signed displacement (one per
   // lane and group of four distances; the diagonal in every lane).
   float sp[kGroups], sm[kGroups];
-  scores_dir<+1>(lds_k, dist, n_plus, rr, part, slot, N, qw, sp);
-  scores_dir<-1>(lds_k, dist, n_minus, rr, part, slot, N, qw, sm);
+  {
+    const RowSpan ks(lds_k, kBf16Stride, 32, part, rr, N);
+    scores_dir<+1>(ks, dist, n_plus, rr, slot, N, qw, sp);
+    scores_dir<-1>(ks, dist, n_minus, rr, slot, N, qw, sm);
+  }
   float s0 = -INFINITY;
   if (has0) {
     u32x4 kf[2];
@@ -369,8 +371,11 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
   float o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
-  accumulate_dir<+1>(lds_v, dist, n_plus, rr, part, N, c, mc, sp, l, o);
-  accumulate_dir<-1>(lds_v, dist, n_minus, rr, part, N, c, mc, sm, l, o);
+  {
+    const RowSpan vs(lds_v, kF32Stride, 64, part, rr, N);
+    accumulate_dir<+1>(vs, dist, n_plus, c, mc, sp, l, o);
+    accumulate_dir<-1>(vs, dist, n_minus, c, mc, sm, l, o);
+  }
   l = quad_sum(l);
   if (has0) {
     u32x4 vf[4];

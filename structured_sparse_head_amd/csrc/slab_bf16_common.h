@@ -76,6 +76,36 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Byte offset of a shifted row fragment: base + delta clamped into [lo, hi]
+// (the lane's fragment of the slab's first and last rows).  One asm block:
+// the add and the clamp take two VALU instructions.
+__device__ __forceinline__ int shifted_off(int base, int delta, int lo, int hi) {
+  int c;
+  asm("v_add_u32 %0, %1, %2\n\tv_med3_i32 %0, %0, %3, %4"
+      : "=&v"(c)
+      : "s"(delta), "v"(base), "v"(lo), "v"(hi));
+  return c;
+}
+
+// LDS byte address of a pointer into LDS.
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ int lds_addr(const char* p) {
+  return static_cast<int>(reinterpret_cast<uintptr_t>((lds_cchar*)p));
+}
+
+// LDS addresses of this lane's fragment of its own row and of the slab's
+// first and last rows, for rows of `stride` bytes starting at `region` and
+// lanes that read `frag` bytes at `frag * part`.
+struct RowSpan {
+  int base, lo, hi;
+  __device__ __forceinline__ RowSpan(const char* region, int stride, int frag, int part, int row,
+                                     int N)
+      : base(lds_addr(region) + frag * part + row * stride),
+        lo(lds_addr(region) + frag * part),
+        hi(lds_addr(region) + frag * part + (N - 1) * stride) {}
+  __device__ __forceinline__ int at(int delta) const { return shifted_off(base, delta, lo, hi); }
+};
+
 // This lane's quarter (16 bf16 = 32 bytes) of bf16 LDS row r; `base` already
 // points at the lane's part of row 0 (array base + 32 p).
 __device__ __forceinline__ void load_bf16_q(const char* base, int r, u32x4 (&f)[2]) {
@@ -92,17 +122,30 @@ __device__ __forceinline__ void load_f32_q(const char* base, int r, u32x4 (&f)[4
   for (int t = 0; t < 4; ++t) f[t] = q[t];
 }
 
+// The same fragments at an LDS byte address.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ void load_bf16_at(int addr, u32x4 (&f)[2]) {
+  lds_u32x4* q = (lds_u32x4*)static_cast<uintptr_t>(static_cast<uint32_t>(addr));
+  f[0] = q[0];
+  f[1] = q[1];
+}
+__device__ __forceinline__ void load_f32_at(int addr, u32x4 (&f)[4]) {
+  lds_u32x4* q = (lds_u32x4*)static_cast<uintptr_t>(static_cast<uint32_t>(addr));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) f[t] = q[t];
+}
+
 // This lane's part of the dot product of two bf16 rows (16 elements),
 // accumulated in fp32.
 __device__ __forceinline__ float dot_part(const uint32_t (&a)[8], const u32x4 (&b)[2]) {
-  float acc[4] = {dot2_first(a[0], b[0].x), dot2_first(a[1], b[0].y), dot2_first(a[2], b[0].z),
-                  dot2_first(a[3], b[0].w)};
-  const uint32_t bw[4] = {b[1].x, b[1].y, b[1].z, b[1].w};
+  const uint32_t bw[8] = {b[0].x, b[0].y, b[0].z, b[0].w, b[1].x, b[1].y, b[1].z, b[1].w};
+  float acc[2] = {dot2_first(a[0], bw[0]), dot2_first(a[1], bw[1])};
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    acc[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[4 + u]),
-                                             __builtin_bit_cast(bf16x2_t, bw[u]), acc[u], false);
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  for (int u = 2; u < 8; ++u)
+    acc[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[u]),
+                                                 __builtin_bit_cast(bf16x2_t, bw[u]), acc[u & 1],
+                                                 false);
+  return acc[0] + acc[1];
 }
 
 // Full 64-element dot product of two bf16 rows split over the row's four

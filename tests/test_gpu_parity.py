@@ -404,6 +404,31 @@ STRIDED = [
 ]
 
 
+@pytest.mark.parametrize("cls", [False, True])
+@pytest.mark.parametrize("shape", [(3, 12, 197, 64, torch.bfloat16), (2, 3, 300, 128, torch.bfloat16),
+                                   (2, 2, 90, 64, torch.float32)],
+                         ids=["bf16 vit", "bf16 d128 N300", "fp32 N90"])
+def test_strided_batch_broadcast_keys_values(shape, cls):
+    """K and V shared by every batch entry: expanded views with batch stride 0."""
+    B, H, N, d, dtype = shape
+    _say(f"case: strided K/V broadcast over the batch B={B} H={H} N={N} d={d} {dtype} cls={cls}")
+    dev = torch.device("cuda:0")
+    inp = workloads.random_case(31 + N, B, H, N, d, dtype)
+    k1, v1 = inp["k"][:1].to(dev), inp["v"][:1].to(dev)
+    k, v = k1.expand(B, -1, -1, -1), v1.expand(B, -1, -1, -1)
+    assert k.stride(0) == 0
+    inp = dict(inp, k=k1.expand(B, -1, -1, -1).cpu().contiguous(),
+               v=v1.expand(B, -1, -1, -1).cpu().contiguous())
+    a, b, w, F = _heads(H, N)
+    q, do = inp["q"].to(dev), inp["do"].to(dev)
+    op = fa.Fibottention(B, H, N, d, dtype, a, b, w, cls=cls)
+    o, lse = op.forward(q, k, v)
+    dq, dk, dv = op.backward(q, k, v, lse, do)
+    torch.cuda.synchronize()
+    gpu = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    _compare(gpu, inp, F, TOL[dtype], cls=cls)
+
+
 def _strided_views(kind, B, H, N, d, dtype, dev, count):
     """`count` views of shape [B, H, N, d] and their backing buffers (NaN)."""
     if kind == "qkv" and count == 3:

@@ -293,7 +293,6 @@ class Fibottention:
         dv = mk() if dv is None else dv
         if workspace is None:
             workspace = torch.empty(self.workspace_floats(), dtype=torch.float32, device=dev)
-        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
         if self._strided(q, k, v, do, dq, dk, dv):
             for t in (dq, dk, dv):
                 if tuple(t.shape) != self.shape or t.dtype != torch.float32:
@@ -303,10 +302,12 @@ class Fibottention:
                 self._layout(t) for t in (q, k, v, do, dq, dk, dv))
             ptrs = [t.data_ptr() for t in (q, k, v)] + self._args(lse) + \
                 [t.data_ptr() for t in (do, dq, dk, dv)] + self._args(workspace)
+            s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
             _check(self._lib.fibatt_bwd_strided(self._dp, int(self.cls), ctypes.byref(ls), *ptrs,
                                                 s))
             return dq, dk, dv
         ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
+        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
         fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
         _check(fn(self._dp, *ptrs, s))
         return dq, dk, dv

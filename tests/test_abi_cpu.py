@@ -217,6 +217,25 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(2, 3, 65, 64)
     with pytest.raises(ValueError):
         op.forward(q, q, q, o=q, lse=torch.zeros(2, 3, 65))
+    # strided views of host memory are refused too, before any library call
+    qkv = torch.zeros(2, 65, 3, 3, 64)
+    v = qkv[:, :, 0].permute(0, 2, 1, 3)
+    assert not v.is_contiguous()
+    with pytest.raises(ValueError):
+        op.forward(v, v, v, o=q, lse=torch.zeros(2, 3, 65))
+    with pytest.raises(ValueError):
+        op.backward(v, v, v, torch.zeros(2, 3, 65), v, dq=q, dk=q, dv=q,
+                    workspace=torch.zeros(2 * 3 * 65))
+
+
+def test_qkv_function_rejects_bad_layouts():
+    import torch
+    with pytest.raises(ValueError):
+        fa.FibottentionQKVFunction.apply(torch.zeros(2, 65, 2, 3, 64), [1, 4, 6], [2, 7, 10],
+                                         [65] * 3, False)
+    with pytest.raises(ValueError):   # not contiguous
+        fa.FibottentionQKVFunction.apply(torch.zeros(2, 3, 65, 3, 64).transpose(1, 2),
+                                         [1, 4, 6], [2, 7, 10], [65] * 3, False)
 
 
 # --------------------------------------------------------------------------

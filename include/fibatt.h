@@ -21,9 +21,11 @@
  *    fibatt_last_error() (per calling thread) and no output is written and no
  *    GPU work is enqueued.
  *  - Tensor layout: Q, K, V, O, dO, dQ, dK, dV are dense row-major
- *    [B, H, N, d_h] (head-major slabs of N rows of d_h elements); LSE and the
- *    backward workspace are [B, H, N].  Every tensor pointer must be 16-byte
- *    aligned and outputs must not alias inputs or each other.
+ *    [B, H, N, d_h] (head-major slabs of N rows of d_h elements), except in
+ *    fibatt_fwd_strided / fibatt_bwd_strided, which take per-tensor row
+ *    strides; LSE and the backward workspace are [B, H, N].  Every tensor
+ *    pointer must be 16-byte aligned and outputs must not alias inputs or
+ *    each other.
  *  - Ownership: the caller allocates and frees every buffer (device memory
  *    for tensors, host memory for the per-head parameter arrays).  The library
  *    allocates no device memory and keeps no state between calls.

@@ -28,8 +28,7 @@ Sources (page titles; no other material is used):
   dot-product attention softmax(Q K^T / sqrt(d)) V, which fixes the
   1/sqrt(d_h) scale.
 
-Readings taken where the pages are garbled or silent (each one is listed in
-DESIGN.md as well):
+Readings taken where the pages are garbled or silent:
 
 R1  Row i of the Wythoff array is the standard one: first term
     floor(floor(i*phi)*phi), second term floor(floor(i*phi)*phi^2).  Only this

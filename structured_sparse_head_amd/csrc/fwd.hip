@@ -245,10 +245,10 @@ __global__ void __launch_bounds__(NT) fwd_stream_kernel(FwdArgs<MH> a) {
   finish_row<T, D, G>(a, slab, j, part, acc, m, l);
 }
 
-// Lane-group width per (dtype, d): each lane owns 128 bytes of a row.
+// Lane-group width per (dtype, d): each lane owns 64 bytes of a row.
 template <typename T, int D>
 constexpr int fwd_group() {
-  return (D * static_cast<int>(sizeof(T))) / 128;
+  return (D * static_cast<int>(sizeof(T))) / 64;
 }
 
 template <typename T, int D, int MH, bool CLS>

@@ -185,6 +185,20 @@ def offsets(N: int, a, b, w) -> Tuple[np.ndarray, np.ndarray]:
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
+# torch's current HIP stream of a device as a raw handle.  The direct query
+# (which torch's own generated code uses) costs well under a microsecond;
+# building a Stream object costs about 2 us per call, which matters for
+# small problems.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream(device) -> int:
+    device = torch.device(device)
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None
+                           else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
+
 
 class Fibottention:
     """A fixed problem shape (B, H, N, d_h, dtype) and per-head (a, b, w).
@@ -264,7 +278,7 @@ class Fibottention:
                 workspace = torch.empty(n, dtype=torch.float32, device=q.device)
             ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()] + \
                 self._args(lse, workspace)
-            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            s = _current_stream(q.device) if stream is None else stream
             _check(self._lib.fibatt_fwd_strided(self._dp, int(self.cls), ctypes.byref(ls), *ptrs,
                                                 s))
         elif self.cls:
@@ -272,11 +286,11 @@ class Fibottention:
             if workspace is None and n > 0:
                 workspace = torch.empty(n, dtype=torch.float32, device=q.device)
             ptrs = self._args(q, k, v, o, lse, workspace)
-            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            s = _current_stream(q.device) if stream is None else stream
             _check(self._lib.fibatt_fwd_cls(self._dp, *ptrs, s))
         else:
             ptrs = self._args(q, k, v, o, lse)
-            s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+            s = _current_stream(q.device) if stream is None else stream
             _check(self._lib.fibatt_fwd(self._dp, *ptrs, s))
         return o, lse
 
@@ -302,12 +316,12 @@ class Fibottention:
                 self._layout(t) for t in (q, k, v, do, dq, dk, dv))
             ptrs = [t.data_ptr() for t in (q, k, v)] + self._args(lse) + \
                 [t.data_ptr() for t in (do, dq, dk, dv)] + self._args(workspace)
-            s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+            s = _current_stream(dev) if stream is None else stream
             _check(self._lib.fibatt_bwd_strided(self._dp, int(self.cls), ctypes.byref(ls), *ptrs,
                                                 s))
             return dq, dk, dv
         ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
-        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        s = _current_stream(dev) if stream is None else stream
         fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
         _check(fn(self._dp, *ptrs, s))
         return dq, dk, dv
@@ -363,7 +377,7 @@ class FibottentionTable:
         if workspace is None and n > 0:
             workspace = torch.empty(n, dtype=torch.float32, device=q.device)
         ptrs = self._args(q, k, v, o, lse, workspace)
-        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        s = _current_stream(q.device) if stream is None else stream
         _check(self._lib.fibatt_fwd_table(self._dp, *ptrs, s))
         return o, lse
 
@@ -376,7 +390,7 @@ class FibottentionTable:
             n = self._floats(self._lib.fibatt_bwd_table_workspace_floats)
             workspace = torch.empty(n, dtype=torch.float32, device=dev)
         ptrs = self._args(q, k, v, lse, do, dq, dk, dv, workspace)
-        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        s = _current_stream(dev) if stream is None else stream
         _check(self._lib.fibatt_bwd_table(self._dp, *ptrs, s))
         return dq, dk, dv
 

@@ -206,13 +206,21 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   float* s_d = s_lse2 + N;
 
   if (tid == 0) build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
+  // The first query row's Q and dO are requested before the staging
+  // barrier, so their latency overlaps it.
+  const int j0 = tid / G;
+  uint32_t qf0[Gm::kWPL], dof0[Gm::kWPL];
+  if (j0 < N) {
+    frag_load_cached<T, D, G>(rq.row(j0), part, qf0);
+    frag_load_cached<T, D, G>(rdo.row(j0), part, dof0);
+  }
   stage_rows_lds<T, D, NT, false>(lds_a, rk.base, rk.rs, N, tid);
   stage_rows_lds<T, D, NT, false>(lds_b, rv.base, rv.rs, N, tid);
   __syncthreads();
   const int nd = s_nd;
 
   // Query-centric pass: D_j and dQ_j.
-  for (int j = tid / G; j < N; j += NT / G) {
+  for (int j = j0; j < N; j += NT / G) {
     const float lse2_j = a.lse[slab * N + j] * kLog2e;
     if (CLS && j == 0) {
       if (part == 0) {
@@ -222,8 +230,16 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
       continue;
     }
     uint32_t qf[Gm::kWPL], dof[Gm::kWPL];
-    frag_load_cached<T, D, G>(rq.row(j), part, qf);
-    frag_load_cached<T, D, G>(rdo.row(j), part, dof);
+    if (j == j0) {
+#pragma unroll
+      for (int u = 0; u < Gm::kWPL; ++u) {
+        qf[u] = qf0[u];
+        dof[u] = dof0[u];
+      }
+    } else {
+      frag_load_cached<T, D, G>(rq.row(j), part, qf);
+      frag_load_cached<T, D, G>(rdo.row(j), part, dof);
+    }
     float acc_a[Gm::kDL], acc_b[Gm::kDL];
     zero_acc(acc_a);
     zero_acc(acc_b);
@@ -241,17 +257,32 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
     store_f32_frag_diff<Gm::kDL>(reinterpret_cast<float*>(rdq.row(j)), part, acc_a, d_j, acc_b,
                                  a.scale);
   }
+  // The first key row's K and V come from LDS while they are still there.
+  const int k0 = tid / G;
+  uint32_t kf0[Gm::kWPL], vf0[Gm::kWPL];
+  if (k0 < N) {
+    frag_load_lds<T, D, G>(lds_a, k0, part, kf0);
+    frag_load_lds<T, D, G>(lds_b, k0, part, vf0);
+  }
   __syncthreads();
 
   // Key-centric pass: Q and dO replace K and V in LDS.
   stage_rows_lds<T, D, NT, true>(lds_a, rq.base, rq.rs, N, tid);
   stage_rows_lds<T, D, NT, true>(lds_b, rdo.base, rdo.rs, N, tid);
   __syncthreads();
-  for (int kr = tid / G; kr < N; kr += NT / G) {
+  for (int kr = k0; kr < N; kr += NT / G) {
     if (CLS && kr == 0) continue;
     uint32_t kf[Gm::kWPL], vf[Gm::kWPL];
-    frag_load_cached<T, D, G>(rk.row(kr), part, kf);
-    frag_load_cached<T, D, G>(rv.row(kr), part, vf);
+    if (kr == k0) {
+#pragma unroll
+      for (int u = 0; u < Gm::kWPL; ++u) {
+        kf[u] = kf0[u];
+        vf[u] = vf0[u];
+      }
+    } else {
+      frag_load_cached<T, D, G>(rk.row(kr), part, kf);
+      frag_load_cached<T, D, G>(rv.row(kr), part, vf);
+    }
     float dk[Gm::kDL], dv[Gm::kDL];
     zero_acc(dk);
     zero_acc(dv);

@@ -193,14 +193,24 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
                                  N, tid);
   const char* qbase = a.q + a.lq.slab_bytes(slab, a.H, es);
   const size_t rsq = a.lq.row_bytes(es);
+  const int part = tid % G;
+  // The first row's Q is requested before the staging barrier, so its
+  // latency overlaps it.
+  const int j0 = tid / G;
+  uint32_t qf0[Gm::kWPL];
+  if (j0 < N) frag_load_global<T, D, G>(qbase + static_cast<size_t>(j0) * rsq, part, qf0);
   __syncthreads();
   const int nd = s_nd;
-  const int part = tid % G;
   const LdsKV<T, D, G> kv{lds_k, lds_v};
-  for (int j = tid / G; j < N; j += NT / G) {
+  for (int j = j0; j < N; j += NT / G) {
     if (CLS && j == 0) continue;
     uint32_t qf[Gm::kWPL];
-    frag_load_global<T, D, G>(qbase + static_cast<size_t>(j) * rsq, part, qf);
+    if (j == j0) {
+#pragma unroll
+      for (int u = 0; u < Gm::kWPL; ++u) qf[u] = qf0[u];
+    } else {
+      frag_load_global<T, D, G>(qbase + static_cast<size_t>(j) * rsq, part, qf);
+    }
     float acc[Gm::kDL];
 #pragma unroll
     for (int t = 0; t < Gm::kDL; ++t) acc[t] = 0.f;

@@ -127,7 +127,6 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
-  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   const int N = a.N;
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;
@@ -141,15 +140,17 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   const char* vbase = tile_row_ptr<STR, kRowB>(a.v, a.lv, slab, a.H, N, 0) + lofs;
   const size_t rk = STR ? a.lk.row_bytes(2) : kRowB, rv = STR ? a.lv.row_bytes(2) : kRowB;
 
+  // The lane's own rows are requested before the displacement list is
+  // built, so their latency overlaps it.
+  u32x4 qf[2], df[2];
+  load_row_q(tile_row_ptr<STR, kRowB>(a.q, a.lq, slab, a.H, N, rr) + lofs, qf);
+  load_row_q(tile_row_ptr<STR, kRowB>(a.dout, a.ldo, slab, a.H, N, rr) + lofs, df);
+  const float lse_r = a.lse[rbase + rr];
+  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   uint32_t qw[8], dw[8];
-  {
-    u32x4 f[2];
-    load_row_q(tile_row_ptr<STR, kRowB>(a.q, a.lq, slab, a.H, N, rr) + lofs, f);
-    frag_words(f, qw);
-    load_row_q(tile_row_ptr<STR, kRowB>(a.dout, a.ldo, slab, a.H, N, rr) + lofs, f);
-    frag_words(f, dw);
-  }
-  const float lse2 = a.lse[rbase + rr] * kLog2e;
+  frag_words(qf, qw);
+  frag_words(df, dw);
+  const float lse2 = lse_r * kLog2e;
 
   // Pass 1: P and dP, one pair per lane and group; D = sum P dP.
   float pw[KG], dpw[KG];
@@ -239,7 +240,6 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
   const int slab = w / a.tiles;
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
-  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   const int N = a.N;
   const int lane = threadIdx.x & 63;
   const int part = lane & 3;
@@ -253,14 +253,15 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
   const char* obase = tile_row_ptr<STR, kRowB>(a.dout, a.ldo, slab, a.H, N, 0) + lofs;
   const size_t rq = STR ? a.lq.row_bytes(2) : kRowB, ro = STR ? a.ldo.row_bytes(2) : kRowB;
 
+  // The lane's own rows are requested before the displacement list is
+  // built, so their latency overlaps it.
+  u32x4 kf0[2], vf0[2];
+  load_row_q(tile_row_ptr<STR, kRowB>(a.k, a.lk, slab, a.H, N, rr) + lofs, kf0);
+  load_row_q(tile_row_ptr<STR, kRowB>(a.v, a.lv, slab, a.H, N, rr) + lofs, vf0);
+  const int nd = stage_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
   uint32_t kw[8], vw[8];
-  {
-    u32x4 f[2];
-    load_row_q(tile_row_ptr<STR, kRowB>(a.k, a.lk, slab, a.H, N, rr) + lofs, f);
-    frag_words(f, kw);
-    load_row_q(tile_row_ptr<STR, kRowB>(a.v, a.lv, slab, a.H, N, rr) + lofs, f);
-    frag_words(f, vw);
-  }
+  frag_words(kf0, kw);
+  frag_words(vf0, vw);
   float dk[16], dv[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {

@@ -76,12 +76,6 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   const int tile = w - slab * a.tiles;
   const int h = slab % a.H;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
-    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;  // a whole last group
-  }
-  __syncthreads();
-  const int nd = s_nd;
   const int N = a.N;
   const int lane = tid & 63;
   const int part = lane & 3;
@@ -96,16 +90,24 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
   const char* kbase = (STR ? a.k + a.lk.slab_bytes(slab, a.H, 2) : a.k + base) + lofs;
   const char* vbase = (STR ? a.v + a.lv.slab_bytes(slab, a.H, 2) : a.v + base) + lofs;
 
-  uint32_t qw[8];
+  // The lane's Q row is requested before the displacement list is built, so
+  // its latency overlaps it.
+  u32x4 qf[2];
   {
     const char* qrow = STR ? a.q + a.lq.slab_bytes(slab, a.H, 2) + rr * a.lq.row_bytes(2)
                            : a.q + base + static_cast<size_t>(rr) * kRowB;
-    u32x4 qf[2];
     qf[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + lofs));
     qf[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + lofs + 64));
-    qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
-    qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
+  if (tid == 0) {
+    build_deltas(a.ht, h, s_dist, s_deltas, &s_nd);
+    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;  // a whole last group
+  }
+  __syncthreads();
+  const int nd = s_nd;
+  uint32_t qw[8];
+  qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
+  qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
 
   // Pass 1: scores, one per lane and group of four displacements.  The next
   // group's rows are requested before this group's dot products; one

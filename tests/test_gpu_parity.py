@@ -332,6 +332,8 @@ BLOCK = [
     # fused kernels' lengths goes through dense copies
     ("bf16 d64 N300", 1, 300, 256, 4, torch.bfloat16, False, False),
     ("bf16 class token d64 N300", 1, 300, 256, 4, torch.bfloat16, True, False),
+    # video-token length at ViT-B width: tile kernels on strided views
+    ("bf16 ViT-B dims N1569 class token", 1, 1569, 768, 12, torch.bfloat16, True, False),
 ]
 # Tolerance of a whole layer, relative to the largest reference magnitude of
 # each tensor: fp32 1e-4; bf16 2e-2 (Q, K, V, Z and O are each rounded to

@@ -406,6 +406,38 @@ STRIDED = [
 ]
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 197, 64, torch.bfloat16), (2, 2, 300, 64, torch.bfloat16),
+                                   (2, 2, 90, 64, torch.float32)],
+                         ids=["bf16 vit kernels", "bf16 tile kernels", "fp32 general kernels"])
+def test_strided_offsets_beyond_4gib(shape):
+    """Q, O and dQ are views whose second batch entry starts 2^31 + 64
+    elements into its buffer (over 4 GiB of bf16): row addresses need 64 bits."""
+    B, H, N, d, dtype = shape
+    _say(f"case: strided batch stride 2^31 + 64 elements B={B} H={H} N={N} d={d} {dtype}")
+    dev = torch.device("cuda:0")
+    inp = workloads.random_case(4 + N, B, H, N, d, dtype)
+    a, b, w, F = _heads(H, N)
+    sb = (1 << 31) + 64
+
+    def far_view(dt):
+        buf = torch.empty(sb + H * N * d, dtype=dt, device=dev)
+        return torch.as_strided(buf, (B, H, N, d), (sb, N * d, d, 1))
+
+    q, o = far_view(dtype), far_view(dtype)
+    q.copy_(inp["q"])
+    k, v, do = (inp[n].to(dev) for n in ("k", "v", "do"))
+    op = fa.Fibottention(B, H, N, d, dtype, a, b, w)
+    _, lse = op.forward(q, k, v, o=o)
+    dq = far_view(torch.float32)
+    dk, dv = (torch.empty(B, H, N, d, device=dev) for _ in range(2))
+    op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    gpu = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    del q, o, dq
+    torch.cuda.empty_cache()
+    _compare(gpu, inp, F, TOL[dtype])
+
+
 @pytest.mark.parametrize("cls", [False, True])
 @pytest.mark.parametrize("shape", [(3, 12, 197, 64, torch.bfloat16), (2, 3, 300, 128, torch.bfloat16),
                                    (2, 2, 90, 64, torch.float32)],

@@ -438,6 +438,32 @@ def test_strided_offsets_beyond_4gib(shape):
     _compare(gpu, inp, F, TOL[dtype])
 
 
+def test_dense_tensors_beyond_4gib():
+    """ViT-B/16 slabs with B = 14400: each bf16 tensor holds 2.18e9 elements
+    (4.36 GB, more than 2^31 elements), so the last batch entries sit beyond
+    4 GiB.  Inputs come from torch's seeded GPU generator; the oracle checks
+    the first, a middle and the last batch entry."""
+    B, H, N, d = 14400, 12, 197, 64
+    _say(f"case: dense tensors beyond 4 GiB B={B} H={H} N={N} d={d} bf16")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(14400)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g, device=dev, dtype=torch.float32)
+                   .to(torch.bfloat16) for _ in range(4))
+    assert q.numel() * 2 > (1 << 32)
+    a, b, w, F = _heads(H, N)
+    op = fa.Fibottention(B, H, N, d, torch.bfloat16, a, b, w)
+    o, lse = op.forward(q, k, v)
+    dq, dk, dv = op.backward(q, k, v, lse, do)
+    torch.cuda.synchronize()
+    sel = [0, B // 2, B - 1]
+    inp = {n: t[sel].cpu() for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    gpu = {n: t[sel].cpu() for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk),
+                                        ("dv", dv))}
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    _compare(gpu, inp, F, TOL[torch.bfloat16])
+
+
 @pytest.mark.parametrize("cls", [False, True])
 @pytest.mark.parametrize("shape", [(3, 12, 197, 64, torch.bfloat16), (2, 3, 300, 128, torch.bfloat16),
                                    (2, 2, 90, 64, torch.float32)],

@@ -13,7 +13,7 @@ from .fibottention import (  # noqa: F401
     dense_backward,
     dense_forward,
     fib_offsets,
-    fib_sequence_alg1,
+    fib_term,
     fib_successor,
     forward,
     offset_table,

@@ -22,8 +22,9 @@ Sources (page titles; no other material is used):
   array choice of (a_i, b_i), the per-head support Omega_i (eq. (3)) and the
   window interpolation between w_min and w_max.
 * The project README of Charlotte-CharMLab/Fibottention: Algorithm 1
-  (generalized Fibonacci sequence under a window constraint) and Algorithm 3
-  (masked scores -> row softmax -> weighted sum of values).
+  (generalized Fibonacci sequence under a window constraint), Algorithm 2
+  (Wythoff rows, the modified pairs) and Algorithm 3 (masked scores -> row
+  softmax -> weighted sum of values).
 * "Dilated Neighborhood Attention Transformer", background section: scaled
   dot-product attention softmax(Q K^T / sqrt(d)) V, which fixes the
   1/sqrt(d_h) scale.
@@ -40,9 +41,12 @@ R1  Row i of the Wythoff array is the standard one: first term
 R2  Head i (1-based) of a layer uses Wythoff row i; tensor head h (0-based)
     uses row h + 1.
 R3  Offsets of a head are the distinct terms f of Fib(a, b) with f <= w and
-    f <= N - 1, produced by Algorithm 1's loop and then filtered by the set
-    definition (the loop alone can overshoot w by one term).  They are used
-    symmetrically: (j, k) is in the support iff |j - k| is an offset.
+    f <= N - 1: the support set's definition (README Algorithm 1 builds the
+    same sequence by repeated sums and stops after the first term that
+    reaches w, which can overshoot w by one term; the set definition keeps
+    only f <= w).  The oracle takes the terms from their closed form
+    f_n = a F_{n-2} + b F_{n-1}.  They are used symmetrically: (j, k) is in
+    the support iff |j - k| is an offset.
 R4  Off-support scores are -inf (excluded from the softmax); on-support
     scores are Q_j . K_k / sqrt(d_h).  The README's 0/1 multiplicative mask
     and the paper's sign/abs form are read as this.
@@ -161,27 +165,54 @@ def wythoff_rows(h: int, modified: bool = False) -> Tuple[np.ndarray, np.ndarray
 
 
 # ---------------------------------------------------------------------------
-# Offsets (README Algorithm 1; paper's definition of Omega_w^{Fib(a,b)})
+# Offsets (paper's definition of Omega_w^{Fib(a,b)}; the sequence of README
+# Algorithm 1)
 # ---------------------------------------------------------------------------
 
 
-def fib_sequence_alg1(a: int, b: int, w: int) -> List[int]:
-    """README Algorithm 1: start from [a, b] and append the sum of the last
-    two terms while the last term is below w."""
-    if a < 0 or b < 1:
-        raise ValueError("need a >= 0 and b >= 1 (a = b = 0 never terminates)")
-    seq = [a, b]
-    while seq[-1] < w:
-        seq.append(seq[-1] + seq[-2])
-    return seq
+def _fibonacci(n: int) -> int:
+    """Standard Fibonacci number F_n for n >= -1 (F_-1 = 1, F_0 = 0, F_1 = 1)."""
+    if n == -1:
+        return 1
+    x, y = 0, 1
+    for _ in range(n):
+        x, y = y, x + y
+    return x
+
+
+def fib_term(a: int, b: int, n: int) -> int:
+    """Term n >= 1 of the generalized Fibonacci sequence Fib(a, b) (first term
+    a, second term b, each later term the sum of the two before it), in
+    closed form: f_n = a F_{n-2} + b F_{n-1}."""
+    if n < 1:
+        raise ValueError("terms are numbered from 1")
+    return a * _fibonacci(n - 2) + b * _fibonacci(n - 1)
 
 
 def fib_offsets(a: int, b: int, w: int, n_tokens: int) -> List[int]:
-    """Distinct non-negative distances of one head, ascending (R3, R7)."""
+    """Distinct non-negative distances of one head, ascending (R3, R7): the
+    members of Fib(a, b) that are at most w (the support set's window) and at
+    most N - 1 (no pair is further apart).
+
+    With a >= 0 and b >= 1 the terms from the second on never decrease
+    (f_{n+1} = f_n + f_{n-1} >= f_n) and grow without bound, so the members
+    up to the limit are f_1 (if small enough) and f_2, f_3, ... up to the
+    first term beyond the limit."""
+    if a < 0 or b < 1:
+        raise ValueError("need a >= 0 and b >= 1 (a = b = 0 gives no sequence)")
     if n_tokens < 1 or w < 1:
         raise ValueError("need N >= 1 and w >= 1")
     limit = min(w, n_tokens - 1)
-    return sorted({f for f in fib_sequence_alg1(a, b, w) if f <= limit})
+    members = set()
+    n = 1
+    while True:
+        f = fib_term(a, b, n)
+        if n >= 2 and f > limit:
+            break
+        if f <= limit:
+            members.add(f)
+        n += 1
+    return sorted(members)
 
 
 def offset_table(n_tokens: int, a: Sequence[int], b: Sequence[int],

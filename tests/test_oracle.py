@@ -39,8 +39,31 @@ def test_wythoff_rows_match_floor_formula_in_decimal():
 
 def test_wythoff_row1_is_fibonacci():
     a, b = oracle.wythoff_row(1)
-    seq = oracle.fib_sequence_alg1(a, b, 100)
-    assert seq[:10] == [1, 2, 3, 5, 8, 13, 21, 34, 55, 89]
+    assert [oracle.fib_term(a, b, n) for n in range(1, 11)] == [1, 2, 3, 5, 8, 13, 21, 34, 55, 89]
+
+
+def test_fib_term_closed_form_matches_the_recurrence():
+    # The closed form a F_{n-2} + b F_{n-1} against the defining recurrence
+    # (first term a, second b, then sums of the two before), run here.
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        a, b = int(rng.integers(0, 10 ** 6)), int(rng.integers(1, 10 ** 6))
+        x, y = a, b
+        for n in range(1, 60):
+            assert oracle.fib_term(a, b, n) == x, (a, b, n)
+            x, y = y, x + y
+
+
+def test_fib_offsets_window_and_duplicates():
+    # The window is inclusive and keeps no term above it (the first term that
+    # reaches w is kept only when it equals w); repeated terms count once.
+    assert oracle.fib_offsets(1, 2, 10, 100) == [1, 2, 3, 5, 8]
+    assert oracle.fib_offsets(1, 2, 13, 100) == [1, 2, 3, 5, 8, 13]
+    assert oracle.fib_offsets(1, 2, 100, 9) == [1, 2, 3, 5, 8]        # N - 1 = 8
+    assert oracle.fib_offsets(0, 1, 20, 100) == [0, 1, 2, 3, 5, 8, 13]  # 1 appears twice
+    assert oracle.fib_offsets(3, 3, 20, 100) == [3, 6, 9, 15]          # 3, 3, 6, 9, 15, 24
+    assert oracle.fib_offsets(7, 2, 10, 100) == [2, 7, 9]              # first term above the second
+    assert oracle.fib_offsets(50, 1, 40, 100) == [1]                   # 50, 1, 51, ...
 
 
 def test_wythoff_rows_partition_the_positive_integers():
@@ -52,10 +75,9 @@ def test_wythoff_rows_partition_the_positive_integers():
     seen = {}
     for i in range(1, R + 1):
         a, b = oracle.wythoff_row(i)
-        for x in oracle.fib_sequence_alg1(a, b, limit):
-            if x <= limit:
-                assert x not in seen, (x, i, seen.get(x))
-                seen[x] = i
+        for x in oracle.fib_offsets(a, b, limit, limit + 1):
+            assert x not in seen, (x, i, seen.get(x))
+            seen[x] = i
     assert sorted(seen) == list(range(1, limit + 1))
 
 
@@ -68,7 +90,7 @@ def test_wythoff_first_column_is_mex_and_gap_is_floor_i_phi():
             mex += 1
         assert a == mex
         assert b - a == _floor_phi_decimal(i)
-        used.update(oracle.fib_sequence_alg1(a, b, 10 ** 6))
+        used.update(oracle.fib_offsets(a, b, 10 ** 6, 10 ** 6 + 1))
 
 
 # --------------------------------------------------------------------------
@@ -207,10 +229,31 @@ def test_wythoff_modified_offsets_extend_the_row():
 
 
 def test_window_sizes_interpolate():
-    assert oracle.window_sizes(12, 5, 65) == [5 + (60 * i) // 11 for i in range(12)]
-    ws = oracle.window_sizes(12, 5, 65)
-    assert ws[0] == 5 and ws[-1] == 65 and ws == sorted(ws)
+    assert oracle.window_sizes(12, 5, 65)[0] == 5
+    assert oracle.window_sizes(12, 5, 65)[-1] == 65
     assert oracle.window_sizes(1, 5, 65) == [65]
+
+
+def _floor_sum(m: int, n: int) -> int:
+    """sum_{k=0}^{n} floor(k m / n) by the reciprocity identity
+    sum_{k=0}^{n-1} floor(k m / n) = ((m - 1)(n - 1) + gcd(m, n) - 1) / 2,
+    plus the last term k = n, which is m."""
+    return ((m - 1) * (n - 1) + math.gcd(m, n) - 1) // 2 + m
+
+
+@pytest.mark.parametrize("h", [2, 3, 5, 7, 12, 16, 33])
+def test_window_sizes_steps_and_sum(h):
+    # Independent pins of the linear interpolation between w_min and w_max:
+    # consecutive windows differ by floor or ceil of (w_max - w_min)/(h - 1),
+    # and the sum of the floors equals a number-theoretic closed form.
+    for w_min, w_max in [(1, 1), (5, 65), (49, 197), (1, 4097), (100, 65536), (3, 10), (7, 8)]:
+        ws = oracle.window_sizes(h, w_min, w_max)
+        d = w_max - w_min
+        lo, hi = d // (h - 1), -(-d // (h - 1))
+        assert ws[0] == w_min and ws[-1] == w_max and len(ws) == h
+        assert all(lo <= y - x <= hi for x, y in zip(ws, ws[1:]))
+        if d > 0:
+            assert sum(ws) == h * w_min + _floor_sum(d, h - 1)
 
 
 # --------------------------------------------------------------------------

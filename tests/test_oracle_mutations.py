@@ -103,7 +103,11 @@ def test_window_overshoot_is_caught(monkeypatch):
     # Algorithm 1's raw output keeps the first term >= w; forgetting the
     # set definition's |j-k| <= w filter must be caught.
     def overshoot(a, b, w, n):
-        return sorted({f for f in fo.fib_sequence_alg1(a, b, w) if f <= n - 1})
+        terms, k = [], 1
+        while not terms or terms[-1] < w or k <= 2:
+            terms.append(fo.fib_term(a, b, k))
+            k += 1
+        return sorted({f for f in terms if f <= n - 1})
 
     monkeypatch.setattr(oracle, "fib_offsets", overshoot)
     _expect_pin_failure(pins.test_offsets_brute_force_membership, 300, 20, "small")
@@ -164,3 +168,14 @@ def test_block_missing_value_projection_gradient_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "block_backward", bad)
     _expect_pin_failure(pins.test_block_matches_torch_autograd_fp64, False)
+
+
+def test_window_round_instead_of_floor_is_caught(monkeypatch):
+    # interpolation that rounds to nearest instead of flooring
+    def rounded(h, w_min, w_max):
+        if h == 1:
+            return [w_max]
+        return [w_min + int(round((w_max - w_min) * (i - 1) / (h - 1))) for i in range(1, h + 1)]
+
+    monkeypatch.setattr(oracle, "window_sizes", rounded)
+    _expect_pin_failure(pins.test_window_sizes_steps_and_sum, 7)

@@ -1,4 +1,8 @@
-"""Build libfibatt.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libfibatt.so (HIP kernels + C ABI) for gfx950, in-tree.
+
+The kernels and the entry points that launch them are compiled with hipcc;
+the host layer (csrc/host.cpp: validation, Wythoff rows, windows, offset
+table, workspace sizes) is plain C++ and is compiled with the host compiler.
 
 Usage: python -m structured_sparse_head_amd.build   (or build() from Python).
 Objects go to structured_sparse_head_amd/_build/, the library next to this file.
@@ -19,7 +23,11 @@ LIB = os.path.join(HERE, "libfibatt.so")
 SOURCES = ["abi.hip", "fwd.hip", "fwd_slab_bf16.hip", "fwd_tile_bf16.hip", "bwd.hip",
            "bwd_slab_bf16.hip", "bwd_tile_bf16.hip", "cls.hip"]
 
+HOST_SOURCES = ["host.cpp"]
+
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", shutil.which("g++") or "g++")
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -41,11 +49,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _compile_host(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"{CXX} failed for {src}:\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        hip_objs = ex.map(_compile, SOURCES)
+        host_objs = ex.map(_compile_host, HOST_SOURCES)
+        objs = list(hip_objs) + list(host_objs)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

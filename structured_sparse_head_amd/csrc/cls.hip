@@ -461,19 +461,6 @@ hipError_t bwd_col(const Problem& p, const ClsArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int cls_splits(const Problem& p) { return (p.N + kSplitRows - 1) / kSplitRows; }
-
-int64_t fwd_cls_workspace_floats(const Problem& p) {
-  const int s = cls_splits(p);
-  return s > 1 ? static_cast<int64_t>(p.B) * p.H * s * (p.D + 2) : 0;
-}
-
-int64_t bwd_cls_workspace_floats(const Problem& p) {
-  const int s = cls_splits(p);
-  const int64_t slabs = static_cast<int64_t>(p.B) * p.H;
-  return slabs * (p.N + p.D) + p.D + (s > 1 ? slabs * s * (2 * p.D + 1) : 0);
-}
-
 hipError_t launch_fwd_cls(const Problem& p0, const void* q, const void* k, const void* v,
                           void* o, float* lse, float* ws, hipStream_t stream, Path path) {
   Problem p = p0;

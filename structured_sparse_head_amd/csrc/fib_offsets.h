@@ -15,6 +15,14 @@
 
 #include <stdint.h>
 
+// Functions shared with device code carry __host__ __device__ under the HIP
+// compiler; the host layer is also built by a plain C++ compiler.
+#if defined(__HIPCC__)
+#define FIBATT_HD __host__ __device__
+#else
+#define FIBATT_HD
+#endif
+
 namespace fibatt {
 
 // Largest number of distinct distances a head can have for lim < 2^31:
@@ -23,7 +31,7 @@ constexpr int kMaxOffsets = 64;
 
 // Writes up to `cap` distances into `out` (ascending) and returns how many
 // exist in total.  Requires a >= 0, b >= 1, lim >= 0.
-__host__ __device__ inline int fib_offsets_gen(int64_t a, int64_t b, int64_t lim,
+FIBATT_HD inline int fib_offsets_gen(int64_t a, int64_t b, int64_t lim,
                                                int32_t* out, int cap) {
   int n = 0;
   const int64_t lo = a < b ? a : b;

@@ -11,53 +11,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "fib_offsets.h"
+#include "problem.h"
 
 namespace fibatt {
-
-constexpr int kMaxHeads = 128;
-constexpr int kMaxSigned = 2 * kMaxOffsets;
-
-// Per-head sequence parameters handed to every kernel by value.  Kernel
-// arguments are copied at every launch, so kernels are instantiated for a
-// small table (up to 16 heads, ~200 bytes) and for the full one.
-// Two modes: with `table` null, head h's distances are the terms of
-// Fib(a[h], b[h]) up to lim[h]; with `table` set (a caller-supplied device
-// array of distances), head h's distances are table[a[h] .. a[h] + b[h]),
-// ascending, each below N.
-template <int MH>
-struct HeadTableT {
-  int32_t a[MH];
-  int32_t b[MH];
-  int32_t lim[MH];  // min(w, N - 1)
-  const int32_t* table;
-};
-using HeadTable = HeadTableT<kMaxHeads>;
-constexpr int kSmallHeads = 16;
-
-template <int MH>
-HeadTableT<MH> shrink_heads(const HeadTable& t, int H) {
-  HeadTableT<MH> r{};
-  for (int h = 0; h < H && h < MH; ++h) {
-    r.a[h] = t.a[h];
-    r.b[h] = t.b[h];
-    r.lim[h] = t.lim[h];
-  }
-  r.table = t.table;
-  return r;
-}
-
-// Where a tensor's rows live: element (b, h, n, e) of a [B, H, N, D] view is
-// at sb b + sh h + sn n + e (elements; the D elements of a row contiguous).
-// A dense [B, H, N, D] tensor has sb = H N D, sh = N D, sn = D.
-struct Layout {
-  int64_t sb, sh, sn;
-  // Byte offset of row 0 of slab b H + h, and the byte stride of rows.
-  __host__ __device__ size_t slab_bytes(size_t slab, int H, int esize) const {
-    return (static_cast<size_t>(slab / H) * sb + static_cast<size_t>(slab % H) * sh) * esize;
-  }
-  __host__ __device__ size_t row_bytes(int esize) const { return static_cast<size_t>(sn) * esize; }
-};
 
 using bf16_t = uint16_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

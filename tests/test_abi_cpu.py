@@ -58,6 +58,26 @@ def test_wythoff_modified_matches_oracle():
     assert np.array_equal(a, oa) and np.array_equal(b, ob)
 
 
+def test_wythoff_rows_near_the_int32_limit():
+    # Rows whose floor(i phi) needs more than 64 bits in 5 n^2 (n ~ 1.9e9 and
+    # up): the modified pair (i - 1, floor(i phi)) still fits int32 below
+    # i = 1,327,217,885, the plain row does not.
+    getcontext().prec = 80
+    phi = (Decimal(1) + Decimal(5).sqrt()) / 2
+    for i in (1_200_000_000, 1_300_000_000, 1_327_217_884, 1_327_217_885, 2 ** 31 - 1):
+        p = int((Decimal(i) * phi).to_integral_value(rounding="ROUND_FLOOR"))
+        if p <= 2 ** 31 - 1:
+            assert fa.wythoff_modified(i) == (i - 1, p), i
+        else:
+            with pytest.raises(fa.FibattError) as ei:
+                fa.wythoff_modified(i)
+            assert ei.value.code == fa.E_RANGE
+        with pytest.raises(fa.FibattError) as ei:  # a = floor(p phi) > 2^31 - 1
+            fa.wythoff(i)
+        assert ei.value.code == fa.E_RANGE
+    assert fa.wythoff_modified(1_200_000_000) == (1_199_999_999, 1_941_640_786)
+
+
 def test_wythoff_modified_rejects_bad_rows():
     for i in (0, -5):
         with pytest.raises(fa.FibattError) as ei:
@@ -394,6 +414,44 @@ def test_strided_backward_rejects_bad_layouts(field, layout, msg):
     setattr(ls, field, fb.Layout(*layout))
     assert _bwd_s(c.desc, ls) == fa.E_INVAL
     assert msg in fa.lib().fibatt_last_error()
+
+
+@pytest.mark.parametrize("field,layout", [
+    ("o", (0, 65 * 64, 64)),        # B = 2 slabs of a batch would share rows
+    ("o", (3 * 65 * 64, 0, 64)),    # H = 3 heads would share rows
+])
+def test_strided_forward_rejects_broadcast_outputs(field, layout):
+    c = _Case()
+    ls = _dense_layouts()
+    setattr(ls, field, fb.Layout(*layout))
+    assert _fwd_s(c.desc, ls) == fa.E_INVAL
+    assert b"broadcast strides are for inputs only" in fa.lib().fibatt_last_error()
+
+
+@pytest.mark.parametrize("field,layout", [
+    ("dq", (0, 65 * 64, 64)),
+    ("dk", (3 * 65 * 64, 0, 64)),
+    ("dv", (0, 0, 64)),
+])
+def test_strided_backward_rejects_broadcast_outputs(field, layout):
+    c = _Case()
+    ls = _dense_layouts()
+    setattr(ls, field, fb.Layout(*layout))
+    assert _bwd_s(c.desc, ls) == fa.E_INVAL
+    assert b"broadcast strides are for inputs only" in fa.lib().fibatt_last_error()
+
+
+def test_strided_zero_strides_allowed_where_nothing_is_shared():
+    # Inputs may broadcast; an output may have a zero stride along an axis of
+    # extent 1.  Both then pass the layout checks and stop at a NULL pointer.
+    c = _Case()
+    ls = _with(_dense_layouts(), q=fb.Layout(0, 0, 64), k=fb.Layout(0, 65 * 64, 64))
+    assert _fwd_s(c.desc, ls, ptrs=[GOOD] * 4 + [None, GOOD]) == fa.E_INVAL
+    assert b"lse is NULL" in fa.lib().fibatt_last_error()
+    one = _Case(B=1)
+    ls1 = _with(_dense_layouts(B=1), o=fb.Layout(0, 65 * 64, 64))
+    assert _fwd_s(one.desc, ls1, ptrs=[GOOD] * 4 + [None, GOOD]) == fa.E_INVAL
+    assert b"lse is NULL" in fa.lib().fibatt_last_error()
 
 
 def test_strided_layouts_of_unused_tensors_are_ignored():

@@ -28,7 +28,9 @@
  *    each other.
  *  - Ownership: the caller allocates and frees every buffer (device memory
  *    for tensors, host memory for the per-head parameter arrays).  The library
- *    allocates no device memory and keeps no state between calls.
+ *    allocates no device memory and keeps no state between calls, except for
+ *    the fixed scratch array of fibatt_bwd_noalloc (one per GPU, part of the
+ *    library's code object, not allocated at run time).
  *  - Streams: GPU work is enqueued on the HIP stream passed as `stream`
  *    (a hipStream_t; NULL means the default stream) and the call returns
  *    without synchronising.  A fault inside a kernel surfaces at the caller's
@@ -90,7 +92,9 @@ int fibatt_wythoff(int32_t i, int32_t* a, int32_t* b);
  * Wythoff row i >= 1: with (a, b) = fibatt_wythoff(i), *b = b - a and
  * *a = a - (b - a), the Fibonacci recurrence run two steps back, so that
  * Fib(*a, *b) = *a, *b, a, b, ...  For row 1 this is (0, 1): head 1 then
- * attends distance 0 as well.  Errors as fibatt_wythoff. */
+ * attends distance 0 as well.  Computed as its closed form
+ * (i - 1, floor(i*phi)) in exact integers.  Errors: E_INVAL if i < 1 or a
+ * pointer is NULL, E_RANGE if floor(i*phi) would exceed INT32_MAX. */
 int fibatt_wythoff_modified(int32_t i, int32_t* a, int32_t* b);
 
 /* Per-head windows interpolated between w_min and w_max (Fibottention paper,
@@ -264,6 +268,23 @@ int fibatt_bwd_strided(const fibatt_desc* desc, int32_t cls,
                        const void* k, const void* v, const float* lse,
                        const void* dout, float* dq, float* dk, float* dv,
                        float* workspace, void* stream);
+
+/* Backward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, layouts, results and error
+ * behaviour as fibatt_bwd, minus `workspace`: the kernels' scratch (D per
+ * row) is a fixed array of FIBATT_NOALLOC_MAX_ROWS floats (16 MiB) in the
+ * library's device memory, one copy per GPU, held until the process ends.
+ * The call allocates nothing.
+ *  - B*H*N above FIBATT_NOALLOC_MAX_ROWS: FIBATT_E_RANGE, nothing enqueued.
+ *  - Every call on one GPU uses that GPU's single array (its contents on
+ *    entry are ignored and left clobbered): calls that overlap on one GPU,
+ *    i.e. run concurrently on different streams, race and give undefined
+ *    results; calls ordered on one stream are safe. */
+#define FIBATT_NOALLOC_MAX_ROWS (1 << 22)
+int fibatt_bwd_noalloc(const fibatt_desc* desc, const void* q, const void* k,
+                       const void* v, const float* lse, const void* dout,
+                       float* dq, float* dk, float* dv, void* stream);
 
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */

@@ -27,7 +27,8 @@ EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fiba
             "fibatt_bwd_cls", "fibatt_fwd_cls_workspace_floats",
             "fibatt_bwd_cls_workspace_floats", "fibatt_fwd_table", "fibatt_bwd_table",
             "fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats",
-            "fibatt_fwd_strided", "fibatt_bwd_strided", "fibatt_last_error")
+            "fibatt_fwd_strided", "fibatt_bwd_strided", "fibatt_bwd_noalloc",
+            "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -121,6 +122,8 @@ def lib() -> ctypes.CDLL:
     L.fibatt_bwd_strided.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32,
                                      ctypes.POINTER(Layouts)] + [vp] * 10
     L.fibatt_bwd_strided.restype = ctypes.c_int
+    L.fibatt_bwd_noalloc.argtypes = [ctypes.POINTER(Desc)] + [vp] * 9
+    L.fibatt_bwd_noalloc.restype = ctypes.c_int
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -324,6 +327,23 @@ class Fibottention:
         s = _current_stream(dev) if stream is None else stream
         fn = self._lib.fibatt_bwd_cls if self.cls else self._lib.fibatt_bwd
         _check(fn(self._dp, *ptrs, s))
+        return dq, dk, dv
+
+    def backward_noalloc(self, q, k, v, lse, do, dq, dk, dv, stream: Optional[int] = None):
+        """fibatt_bwd_noalloc: the backward with the library's fixed scratch
+        array instead of a workspace (dense tensors, no class-token mask); the
+        caller passes the outputs, and nothing is allocated on the device."""
+        if self.cls:
+            raise ValueError("fibatt_bwd_noalloc has no class-token variant")
+        for t in (q, k, v, do):
+            if tuple(t.shape) != self.shape or t.dtype != self.dtype:
+                raise ValueError(f"expected {self.shape} {self.dtype}, got {tuple(t.shape)} {t.dtype}")
+        for t in (dq, dk, dv):
+            if tuple(t.shape) != self.shape or t.dtype != torch.float32:
+                raise ValueError(f"dq, dk, dv must be {self.shape} float32")
+        ptrs = self._args(q, k, v, lse, do, dq, dk, dv)
+        s = _current_stream(q.device) if stream is None else stream
+        _check(self._lib.fibatt_bwd_noalloc(self._dp, *ptrs, s))
         return dq, dk, dv
 
 

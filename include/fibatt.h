@@ -286,6 +286,33 @@ int fibatt_bwd_noalloc(const fibatt_desc* desc, const void* q, const void* k,
                        const void* v, const float* lse, const void* dout,
                        float* dq, float* dk, float* dv, void* stream);
 
+/* Measurement aids (not part of the attention itself). */
+
+/* Binds two HIP events (hipEvent_t values created by the caller) to the GPU
+ * execution of the next call on this thread that enqueues work: start_event
+ * to the start of its first kernel, stop_event to the end of its last
+ * kernel, both recorded by the GPU around the kernels themselves
+ * (hipExtLaunchKernelGGL).  hipEventElapsedTime(start, stop) is then the
+ * time of that call's kernels without the launch gaps around them (the
+ * kernel durations a profiler reports).  The binding is used by that one
+ * call and then cleared, also when the call fails; passing NULL for both
+ * clears it.  Errors: E_INVAL if exactly one event is NULL. */
+int fibatt_time_next_call(void* start_event, void* stop_event);
+
+/* The HBM traffic of a pass with nothing else in it, as a reference for the
+ * bandwidth the GPU delivers at that read/write mix: reads n_src device
+ * arrays of `bytes` each and writes n_dst device arrays of
+ * dst_scale * `bytes` each (16-byte units, coalesced; every unit written is
+ * the xor of the units read).  The forward of bf16 inputs has the mix
+ * n_src = 3, n_dst = 1, dst_scale = 1 (Q, K, V read, O written); its
+ * backward n_src = 4, n_dst = 3, dst_scale = 2 (Q, K, V, dO read; fp32 dQ,
+ * dK, dV written).  src and dst are HOST arrays of device pointers (16-byte
+ * aligned).  Errors: E_INVAL for counts outside 1..4, dst_scale not 1 or 2,
+ * bytes not a positive multiple of 16, NULL or misaligned pointers; E_HIP. */
+int fibatt_hbm_stream(const void* const* src, int32_t n_src, void* const* dst,
+                      int32_t n_dst, int64_t bytes, int32_t dst_scale,
+                      void* stream);
+
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */
 const char* fibatt_last_error(void);

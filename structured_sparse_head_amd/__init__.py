@@ -24,8 +24,10 @@ from .fibatt import (  # noqa: F401
     FibottentionTable,
     backward,
     forward,
+    hbm_stream,
     lib,
     offsets,
+    time_next_call,
     windows,
     wythoff,
     wythoff_modified,

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfibatt.so")
 SOURCES = ["abi.hip", "fwd.hip", "fwd_slab_bf16.hip", "fwd_tile_bf16.hip", "bwd.hip",
-           "bwd_slab_bf16.hip", "bwd_tile_bf16.hip", "cls.hip", "noalloc.hip"]
+           "bwd_slab_bf16.hip", "bwd_tile_bf16.hip", "cls.hip", "noalloc.hip", "stream_ref.hip"]
 
 HOST_SOURCES = ["host.cpp"]
 

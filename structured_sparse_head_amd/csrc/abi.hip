@@ -17,10 +17,29 @@ using fibatt::host::fail;
 using fibatt::host::ok;
 using fibatt::host::path_from_env;
 
+namespace fibatt {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace fibatt
+
 extern "C" {
+
+int fibatt_time_next_call(void* start_event, void* stop_event) {
+  fibatt::LaunchEvents& ev = fibatt::launch_events();
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(FIBATT_E_INVAL, "start_event and stop_event must both be set or both be NULL");
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  ev.armed = stop_event != nullptr;
+  ev.started = false;
+  return ok();
+}
 
 int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k, const void* v, void* o,
                float* lse, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
@@ -36,6 +55,7 @@ int fibatt_fwd(const fibatt_desc* desc, const void* q, const void* k, const void
 int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k, const void* v,
                const float* lse, const void* dout, float* dq, float* dk, float* dv,
                float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
@@ -53,6 +73,7 @@ int fibatt_bwd(const fibatt_desc* desc, const void* q, const void* k, const void
 
 int fibatt_fwd_cls(const fibatt_desc* desc, const void* q, const void* k, const void* v, void* o,
                    float* lse, float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
@@ -71,6 +92,7 @@ int fibatt_fwd_cls(const fibatt_desc* desc, const void* q, const void* k, const 
 int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k, const void* v,
                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
                    float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
@@ -89,6 +111,7 @@ int fibatt_bwd_cls(const fibatt_desc* desc, const void* q, const void* k, const 
 
 int fibatt_fwd_table(const fibatt_table_desc* desc, const void* q, const void* k, const void* v,
                      void* o, float* lse, float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_table_desc(desc, &p);
   if (rc) return rc;
@@ -109,6 +132,7 @@ int fibatt_fwd_table(const fibatt_table_desc* desc, const void* q, const void* k
 int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q, const void* k, const void* v,
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_table_desc(desc, &p);
   if (rc) return rc;
@@ -130,6 +154,7 @@ int fibatt_bwd_table(const fibatt_table_desc* desc, const void* q, const void* k
 int fibatt_fwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layouts* layouts,
                        const void* q, const void* k, const void* v, void* o, float* lse,
                        float* workspace, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;
@@ -157,6 +182,7 @@ int fibatt_bwd_strided(const fibatt_desc* desc, int32_t cls, const fibatt_layout
                        const void* q, const void* k, const void* v, const float* lse,
                        const void* dout, float* dq, float* dk, float* dv, float* workspace,
                        void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;

@@ -425,13 +425,13 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
         kSlabLdsBudget);
     if (attr != hipSuccess) return attr;
     a.tiles = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
+    launch(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
   } else {
     const int per = NT / G;
     a.tiles = (p.N + per - 1) / per;
     const unsigned blocks = static_cast<unsigned>(slabs * a.tiles);
-    hipLaunchKernelGGL((bwd_dq_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream,
+    launch((bwd_dq_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream, a);
+    launch((bwd_dkdv_stream_kernel<T, D, G, NT, MH, CLS>), dim3(blocks), dim3(NT), 0, stream,
                        a);
   }
   return hipGetLastError();

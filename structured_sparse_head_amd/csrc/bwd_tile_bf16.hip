@@ -324,10 +324,10 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
 template <int MH, int KG, int NQ, bool CLS>
 void launch_dq(const BwdTileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
   if (strided)
-    hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
+    launch((bwd_dq_tile_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
                        dim3(kTileThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dq_tile_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
+    launch((bwd_dq_tile_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
                        dim3(kTileThreads), 0, stream, a);
 }
 
@@ -376,10 +376,10 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   else
     launch_dq<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, p.strided, grid, stream);
   if (p.strided)
-    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS, true>), dim3(grid), dim3(kTileThreads),
+    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, true>), dim3(grid), dim3(kTileThreads),
                        0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_tile_kernel<MH, NQ, CLS, false>), dim3(grid),
+    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, false>), dim3(grid),
                        dim3(kTileThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -408,10 +408,10 @@ template <typename T, int D>
 hipError_t fwd_row_t(const Problem& p, ClsArgs a, hipStream_t stream) {
   constexpr int G = cls_group<T, D>();
   const unsigned slabs = static_cast<unsigned>(static_cast<size_t>(p.B) * p.H);
-  hipLaunchKernelGGL((fwd_cls_row_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
+  launch((fwd_cls_row_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
                      dim3(kClsThreads), 0, stream, a);
   if (a.splits > 1)
-    hipLaunchKernelGGL((fwd_cls_combine_kernel<T, D>), dim3(slabs), dim3(D), 0, stream, a);
+    launch((fwd_cls_combine_kernel<T, D>), dim3(slabs), dim3(D), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -419,10 +419,10 @@ template <typename T, int D>
 hipError_t bwd_row_t(const Problem& p, ClsArgs a, hipStream_t stream) {
   constexpr int G = cls_group<T, D>();
   const unsigned slabs = static_cast<unsigned>(static_cast<size_t>(p.B) * p.H);
-  hipLaunchKernelGGL((bwd_cls_row_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
+  launch((bwd_cls_row_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
                      dim3(kClsThreads), 0, stream, a);
   if (a.splits > 1)
-    hipLaunchKernelGGL((bwd_cls_row_combine_kernel<D>), dim3(slabs), dim3(D), 0, stream, a);
+    launch((bwd_cls_row_combine_kernel<D>), dim3(slabs), dim3(D), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -430,10 +430,10 @@ template <typename T, int D>
 hipError_t bwd_col_t(const Problem& p, ClsArgs a, hipStream_t stream) {
   constexpr int G = cls_group<T, D>();
   const unsigned slabs = static_cast<unsigned>(static_cast<size_t>(p.B) * p.H);
-  hipLaunchKernelGGL((bwd_cls_col_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
+  launch((bwd_cls_col_kernel<T, D, G, kClsThreads>), dim3(slabs * a.splits),
                      dim3(kClsThreads), 0, stream, a);
   if (a.splits > 1)
-    hipLaunchKernelGGL((bwd_cls_col_combine_kernel<D>), dim3(slabs), dim3(D), 0, stream, a);
+    launch((bwd_cls_col_combine_kernel<D>), dim3(slabs), dim3(D), 0, stream, a);
   return hipGetLastError();
 }
 

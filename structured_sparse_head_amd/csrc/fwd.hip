@@ -297,11 +297,11 @@ hipError_t launch_fwd_t(const Problem& p, const void* q, const void* k, const vo
         kSlabLdsBudget);
     if (attr != hipSuccess) return attr;
     a.tiles = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
+    launch(kern, dim3(static_cast<unsigned>(slabs)), dim3(NTS), lds, stream, a);
   } else {
     const int rows = NT / G;
     a.tiles = (p.N + rows - 1) / rows;
-    hipLaunchKernelGGL((fwd_stream_kernel<T, D, G, NT, C, MH, CLS>),
+    launch((fwd_stream_kernel<T, D, G, NT, C, MH, CLS>),
                        dim3(static_cast<unsigned>(slabs * a.tiles)), dim3(NT), 0, stream, a);
   }
   return hipGetLastError();

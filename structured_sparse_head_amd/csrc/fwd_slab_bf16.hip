@@ -500,7 +500,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   if (attr != hipSuccess) return attr;
   const int cus = cu_count();
   const int grid = a.slabs < cus ? a.slabs : cus;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsF), lds, stream, a);
+  launch(kern, dim3(grid), dim3(kThreadsF), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -211,10 +211,10 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
 template <int MH, int KG, int NQ, bool CLS>
 void launch_kg(const TileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
   if (strided)
-    hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
+    launch((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, true>), dim3(grid),
                        dim3(kTileThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
+    launch((fwd_tile_bf16_kernel<MH, KG, NQ, CLS, false>), dim3(grid),
                        dim3(kTileThreads), 0, stream, a);
 }
 

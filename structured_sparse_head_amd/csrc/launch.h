@@ -2,12 +2,53 @@
 // units.  Arguments have been validated by the caller.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "kernel_common.h"
 
 namespace fibatt {
+
+// Events bound by fibatt_time_next_call to the next work-enqueuing call on
+// this thread: `start` to the start of its first kernel, `stop` to the end
+// of its last one.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool armed = false;
+  bool started = false;
+};
+LaunchEvents& launch_events();
+
+// Clears the events when an entry point returns: they belong to one call.
+struct LaunchGuard {
+  ~LaunchGuard() {
+    LaunchEvents& ev = launch_events();
+    ev.armed = false;
+    ev.started = false;
+    ev.start = ev.stop = nullptr;
+  }
+};
+
+// Every kernel of the library is launched through here: with events armed it
+// goes through hipExtLaunchKernelGGL, which records them at the kernel's own
+// start and end on the GPU.
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                   Args&&... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.armed) {
+    hipExtLaunchKernelGGL(kern, grid, block, static_cast<uint32_t>(lds), stream,
+                          ev.started ? nullptr : ev.start, ev.stop, 0,
+                          std::forward<Args>(args)...);
+    ev.started = true;
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, std::forward<Args>(args)...);
+  }
+}
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, hipStream_t stream, Path path);

@@ -55,6 +55,7 @@ using fibatt::host::path_from_env;
 extern "C" int fibatt_bwd_noalloc(const fibatt_desc* desc, const void* q, const void* k,
                                   const void* v, const float* lse, const void* dout, float* dq,
                                   float* dk, float* dv, void* stream) {
+  fibatt::LaunchGuard guard;
   fibatt::Problem p;
   int rc = check_desc(desc, &p);
   if (rc) return rc;

@@ -28,7 +28,7 @@ EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fiba
             "fibatt_bwd_cls_workspace_floats", "fibatt_fwd_table", "fibatt_bwd_table",
             "fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats",
             "fibatt_fwd_strided", "fibatt_bwd_strided", "fibatt_bwd_noalloc",
-            "fibatt_last_error")
+            "fibatt_time_next_call", "fibatt_hbm_stream", "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -124,6 +124,11 @@ def lib() -> ctypes.CDLL:
     L.fibatt_bwd_strided.restype = ctypes.c_int
     L.fibatt_bwd_noalloc.argtypes = [ctypes.POINTER(Desc)] + [vp] * 9
     L.fibatt_bwd_noalloc.restype = ctypes.c_int
+    L.fibatt_time_next_call.argtypes = [vp, vp]
+    L.fibatt_time_next_call.restype = ctypes.c_int
+    L.fibatt_hbm_stream.argtypes = [ctypes.POINTER(vp), ctypes.c_int32, ctypes.POINTER(vp),
+                                    ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp]
+    L.fibatt_hbm_stream.restype = ctypes.c_int
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -483,3 +488,29 @@ class FibottentionQKVFunction(torch.autograd.Function):
         dq, dk, dv = FibottentionQKVFunction._heads(g)
         ctx.op.backward(q, k, v, lse, do, dq=dq, dk=dk, dv=dv)
         return g.to(qkv.dtype), None, None, None, None
+
+
+def time_next_call(start_event: int, stop_event: int) -> None:
+    """fibatt_time_next_call: bind two hipEvent_t handles to the kernels of
+    the next call on this thread (measurement aid)."""
+    _check(lib().fibatt_time_next_call(start_event, stop_event))
+
+
+def hbm_stream(src: Sequence[torch.Tensor], dst: Sequence[torch.Tensor], nbytes: int,
+               dst_scale: int = 1, stream: Optional[int] = None) -> None:
+    """fibatt_hbm_stream: read `nbytes` from each tensor of src and write
+    dst_scale * nbytes to each of dst (the HBM byte mix of a pass, nothing
+    else); measurement aid."""
+    for t in list(src) + list(dst):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("hbm_stream takes contiguous device tensors")
+    for t in src:
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError("a source tensor is smaller than nbytes")
+    for t in dst:
+        if t.numel() * t.element_size() < dst_scale * nbytes:
+            raise ValueError("a destination tensor is smaller than dst_scale * nbytes")
+    S = (ctypes.c_void_p * len(src))(*[t.data_ptr() for t in src])
+    D = (ctypes.c_void_p * len(dst))(*[t.data_ptr() for t in dst])
+    s = _current_stream(src[0].device) if stream is None else stream
+    _check(lib().fibatt_hbm_stream(S, len(src), D, len(dst), nbytes, dst_scale, s))

@@ -8,6 +8,7 @@ slab and streaming) are exercised where a shape allows both.
 
 import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -72,16 +73,21 @@ def _f64(t):
     return t.to(torch.float64).numpy()
 
 
+def _pick(t, batches, heads):
+    """The selected batch entries and heads of a [B, H, ...] CPU tensor."""
+    if batches is not None:
+        t = t[list(batches)]
+    if heads is not None:
+        t = t[:, list(heads)]
+    return t
+
+
 def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True, cls=False):
     """Element-by-element comparison on the selected (batch, head) slabs."""
-    sel_b = slice(None) if batches is None else list(batches)
-    x = {n: _f64(inp[n])[sel_b] for n in inp}
+    x = {n: _f64(_pick(inp[n], batches, heads)) for n in inp}
+    g = {n: _f64(_pick(t, batches, heads)) for n, t in gpu.items()}
     if heads is not None:
-        x = {n: t[:, heads] for n, t in x.items()}
         F = [F[h] for h in heads]
-    g = {n: _f64(t)[sel_b] for n, t in gpu.items()}
-    if heads is not None:
-        g = {n: t[:, heads] for n, t in g.items()}
     o, lse = oracle.forward(x["q"], x["k"], x["v"], F, cls=cls)
     err = {"o": float(np.abs(g["o"] - o).max()) if o.size else 0.0}
     fin = np.isfinite(lse)
@@ -92,10 +98,39 @@ def _compare(gpu, inp, F, tol, batches=None, heads=None, with_bwd=True, cls=Fals
         dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], F, cls=cls)
         for n, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
             err[n] = float(np.abs(g[n] - ref).max()) if ref.size else 0.0
-    _say(f"    max-abs errors: {err}")
+    _say(f"    batches {batches} heads {heads}: max-abs errors {err}")
     for n, e in err.items():
         assert e <= tol, (n, e, tol)
     return err
+
+
+def _compare_all(gpu, inp, F, tol, units, threads=4):
+    """_compare over every (batches, heads) unit, units on a thread pool.
+
+    The oracle's work is large numpy slice operations, which release the
+    GIL, so threads give real parallelism without forking a process that
+    has already opened the GPU.
+    """
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        futures = [ex.submit(_compare, gpu, inp, F, tol, batches=bs, heads=hs)
+                   for bs, hs in units]
+        for f in futures:
+            f.result()
+
+
+# Full-size runs of workloads 3-5, made once per module and shared by the
+# tests that check them against the oracle slab by slab.
+_FULL = {}
+
+
+def _full_run(num):
+    if num not in _FULL:
+        wl = workloads.WORKLOADS[num]
+        _say(f"case: workload {num} {wl.name}, full GPU run (forward and backward)")
+        inp = workloads.make_inputs(wl)
+        a, b, w, F = _heads(wl.H, wl.N, w=workloads.windows(wl))
+        _FULL[num] = (wl, inp, F, _gpu_run(inp, a, b, w))
+    return _FULL[num]
 
 
 @pytest.mark.parametrize("path", [None, "slab", "stream"])
@@ -126,31 +161,26 @@ def test_workload2_vit_b(path):
         _set_path(None)
 
 
-def test_workload3_video_sampled_batches():
-    wl = workloads.WORKLOADS[3]
-    _say(f"case: workload 3 {wl.name}, full GPU run, oracle on batches 0 and 15")
-    inp = workloads.make_inputs(wl)
-    a, b, w, F = _heads(wl.H, wl.N, w=workloads.windows(wl))
-    gpu = _gpu_run(inp, a, b, w)
-    _compare(gpu, inp, F, TOL[torch.bfloat16], batches=[0, 15])
+def test_workload3_video_every_batch_entry():
+    """All 16 batch entries x 12 heads, every element of O, LSE, dQ, dK, dV."""
+    wl, inp, F, gpu = _full_run(3)
+    _compare_all(gpu, inp, F, TOL[torch.bfloat16],
+                 [([bi], None) for bi in range(wl.B)])
 
 
-def test_workload4_highres_sampled_batches():
-    wl = workloads.WORKLOADS[4]
-    _say(f"case: workload 4 {wl.name}, full GPU run, oracle on batch 3")
-    inp = workloads.make_inputs(wl)
-    a, b, w, F = _heads(wl.H, wl.N)
-    gpu = _gpu_run(inp, a, b, w)
-    _compare(gpu, inp, F, TOL[torch.bfloat16], batches=[3])
+def test_workload4_highres_every_batch_entry():
+    """All 4 batch entries x 16 heads, every element."""
+    wl, inp, F, gpu = _full_run(4)
+    _compare_all(gpu, inp, F, TOL[torch.bfloat16],
+                 [([bi], None) for bi in range(wl.B)])
 
 
-def test_workload5_long_sampled_heads():
-    wl = workloads.WORKLOADS[5]
-    _say(f"case: workload 5 {wl.name}, full GPU run, oracle on heads 0 and 15")
-    inp = workloads.make_inputs(wl)
-    a, b, w, F = _heads(wl.H, wl.N)
-    gpu = _gpu_run(inp, a, b, w)
-    _compare(gpu, inp, F, TOL[torch.bfloat16], heads=[0, 15])
+@pytest.mark.parametrize("group", range(4))
+def test_workload5_long_every_head(group):
+    """Heads 4*group .. 4*group+3 of 16 (N = 65536, d = 128), every element."""
+    wl, inp, F, gpu = _full_run(5)
+    _compare_all(gpu, inp, F, TOL[torch.bfloat16],
+                 [(None, [h]) for h in range(4 * group, 4 * group + 4)])
 
 
 EDGE = [

@@ -19,6 +19,9 @@
 //  * dkdv: per key row and group of four displacements, the queries' Q and dO
 //    rows are read once for both the recomputed scores and the accumulation
 //    of dV += P dO and dK += dS Q.
+// The accumulations over a group of four displacements use v_dot2_f32_bf16 on
+// pairs of them (axpy4_dot2: P and dS rounded to bf16, sums in fp32), except
+// dQ for d_h = 128, whose padded slots read nothing.
 // Lanes past the last row repeat row N - 1 and write identical values.
 #include "tile_bf16_common.h"
 
@@ -205,15 +208,25 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   for (int g = 0; g < KG; ++g) {
     if (4 * g < nd) {
       float ds[4];
-      gather4q(pw[g] * (dpw[g] - dd), ds);
+      gather4q(pw[g] * (dpw[g] - dd), ds);  // 0 in padded slots (P = 0 there)
       int d[4];
       group_deltas(s_deltas, g, d);
+      if constexpr (NQ == 1) {
+        u32x4 kf[4][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (4 * g + j < nd) {
-          u32x4 kf[2];
-          load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rk, kf);
-          axpy_bf16(acc, ds[j], kf);
+        for (int j = 0; j < 4; ++j)
+          load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rk, kf[j]);
+        axpy4_dot2(acc, pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), kf);
+      } else {
+        // d_h = 128 is bound by rows fetched from beyond L2: no reads for
+        // the padded slots.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (4 * g + j < nd) {
+            u32x4 kf[2];
+            load_row_q(kbase + static_cast<size_t>(clamp_row(rr + d[j], N)) * rk, kf);
+            axpy_bf16(acc, ds[j], kf);
+          }
         }
       }
     }
@@ -297,11 +310,8 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
     float pg[4], dsg[4];
     gather4q(p, pg);
     gather4q(p * (dp - d_j), dsg);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      axpy_bf16(dv, pg[j], of[j]);
-      axpy_bf16(dk, dsg[j], qf[j]);
-    }
+    axpy4_dot2(dv, pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3]), of);
+    axpy4_dot2(dk, pack_bf16x2(dsg[0], dsg[1]), pack_bf16x2(dsg[2], dsg[3]), qf);
   }
   if constexpr (CLS) {
     u32x4 q0f[2], o0f[2];

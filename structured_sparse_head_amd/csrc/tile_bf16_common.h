@@ -100,6 +100,43 @@ __device__ __forceinline__ void axpy_bf16(float (&acc)[16], float p, const u32x4
   }
 }
 
+// Two fp32 values rounded to bf16 (nearest even) and packed, x in the low
+// half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y))) << 16);
+}
+
+// acc += sum_j c_j x_j over a group of four bf16 fragments x_j (this lane's
+// 16 elements each), with the coefficients packed as bf16 pairs c01 = (c_0,
+// c_1) and c23 = (c_2, c_3).  Element e of two fragments is interleaved
+// into one bf16 pair (v_perm_b32) and v_dot2_f32_bf16 adds both products
+// to the fp32 accumulator: 16 instructions per fragment instead of 32 for
+// widening and fp32 FMAs.  The coefficients lose their low mantissa bits
+// (relative 2^-9), as a bf16 matrix-core product would.
+__device__ __forceinline__ void axpy4_dot2(float (&acc)[16], uint32_t c01, uint32_t c23,
+                                           const u32x4 (&x)[4][2]) {
+  constexpr uint32_t kLo = 0x05040100u;  // (a.lo, b.lo): bytes 0, 1 of a, then of b
+  constexpr uint32_t kHi = 0x07060302u;  // (a.hi, b.hi)
+  const bf16x2_t p01 = __builtin_bit_cast(bf16x2_t, c01);
+  const bf16x2_t p23 = __builtin_bit_cast(bf16x2_t, c23);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t a = x[0][u >> 2][u & 3], b = x[1][u >> 2][u & 3];
+    const uint32_t c = x[2][u >> 2][u & 3], d = x[3][u >> 2][u & 3];
+    float lo = __builtin_amdgcn_fdot2_f32_bf16(
+        p01, __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b, a, kLo)), acc[2 * u], false);
+    float hi = __builtin_amdgcn_fdot2_f32_bf16(
+        p01, __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b, a, kHi)), acc[2 * u + 1], false);
+    lo = __builtin_amdgcn_fdot2_f32_bf16(
+        p23, __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(d, c, kLo)), lo, false);
+    hi = __builtin_amdgcn_fdot2_f32_bf16(
+        p23, __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(d, c, kHi)), hi, false);
+    acc[2 * u] = lo;
+    acc[2 * u + 1] = hi;
+  }
+}
+
 // Workgroup b's tile index (-1 for none), b running on XCD x = b mod 8.
 //  * Small slabs (per_xcd > 0): XCD x takes the contiguous range
 //    [x * per_xcd, (x + 1) * per_xcd) of all tiles, so a slab's tiles share

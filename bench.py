@@ -18,7 +18,11 @@ Prints one JSON line:
     written; backward: Q, K, V, dO, O and LSE read, fp32 dQ, dK, dV written)
     and, as a second denominator, a hand-written HIP stream kernel that moves
     the same bytes with nothing else in it (fibatt_hbm_stream);
-  * workloads: the same per-pass figures for all five workloads;
+  * workloads: the same per-pass figures for all five workloads, and, where
+    the committed counters match the current sources, the L2-miss read rate
+    (FETCH_SIZE / time) over the rate at which the XCDs' L2s can be filled
+    from beyond them (fibatt_fabric_read, l2_fill_ref_gbps): the bound of
+    the long-sequence kernels, whose rows at large distances miss L2;
   * cpu_baseline: the fp64 CPU oracle on this host's cores (a process pool,
     one BLAS thread per worker), run before the GPU is touched;
   * pages_context: the figures the Fibottention pages state themselves.
@@ -134,6 +138,44 @@ def measured_traffic(workload, pass_name):
             return None
         total += table[key]
     return total
+
+
+def measured_fetch(workload, pass_name):
+    """L2-miss read bytes per pass (FETCH_SIZE, scaled) from the same summary,
+    or None (see measured_traffic)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    table = {}
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 5 and not f[0].startswith("#"):
+                table[(f[0], f[1], f[2])] = int(f[3])
+    total = 0
+    for k in KERNELS[workload][pass_name]:
+        key = (f"W{workload}", k, source_hash(k))
+        if key not in table:
+            return None
+        total += table[key]
+    return total
+
+
+FABRIC_MIB = 64     # larger than all eight L2s together (32 MiB)
+FABRIC_PASSES = 4
+
+
+def fabric_ref(hip, torch, fa, dev, n=20):
+    """Rate (GB/s) at which the XCDs' L2s fill from beyond them
+    (fibatt_fabric_read over a buffer larger than every L2), median of n."""
+    buf = torch.zeros(FABRIC_MIB * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
+    out = torch.empty(fa.FABRIC_OUT_BYTES // 4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        fa.fabric_read(buf, FABRIC_PASSES, out)
+    t = kernel_times(hip, lambda i: fa.fabric_read(buf, FABRIC_PASSES, out), n)
+    delivered = 8 * buf.numel() * 4 * FABRIC_PASSES
+    del buf, out
+    return delivered / (t[n // 2] * 1e-3) / 1e9
 
 
 def pages_context(wl, pairs_per_pass):
@@ -690,6 +732,7 @@ def main():
 
     # Per-workload block: kernel-only medians for every workload.
     block = {}
+    fabric_gbps = fabric_ref(hip, torch, fa, dev) if others else None
     for num in others:
         owl = workloads.WORKLOADS[num]
         if num == wl.number and not (args.cls or args.modified):
@@ -728,6 +771,14 @@ def main():
             "fwd_traffic": measured_traffic(num, "fwd"),
             "bwd_traffic": measured_traffic(num, "bwd"),
         }
+        # L2-miss reads (FETCH_SIZE from the committed counters, current
+        # sources only) per second, over the rate the L2s can be filled.
+        for pname, rec in (("fwd", rf), ("bwd", rb)):
+            fetch = measured_fetch(num, pname)
+            if fetch is not None and fabric_gbps:
+                gbps = fetch / (rec["median_us"] * 1e-6) / 1e9
+                entry[f"{pname}_l2_fill_gbps"] = gbps
+                entry[f"{pname}_frac_of_l2_fill_ref"] = gbps / fabric_gbps
         if num in cpu_samples:
             entry["cpu_oracle"] = cpu_samples[num]
         elif num == wl.number and cpu is not None:
@@ -735,6 +786,7 @@ def main():
         block[str(num)] = entry
     if block:
         line["workloads"] = block
+        line["l2_fill_ref_gbps"] = fabric_gbps
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -313,6 +313,19 @@ int fibatt_hbm_stream(const void* const* src, int32_t n_src, void* const* dst,
                       int32_t n_dst, int64_t bytes, int32_t dst_scale,
                       void* stream);
 
+/* The rate at which the XCDs' L2 caches fill from beyond them, as a
+ * reference for kernels whose L2 misses bound them: every one of the 8 XCDs
+ * reads the whole device buffer buf (`bytes`, a multiple of 4 MiB), `passes`
+ * times; a buffer larger than one XCD's L2 (4 MiB) misses there on every
+ * read.  The bytes delivered to the CUs are 8 * bytes * passes.  out is a
+ * device array of FIBATT_FABRIC_OUT_BYTES that receives one 16-byte xor of
+ * the data per workgroup (so no read can be dropped).  Errors: E_INVAL for
+ * bytes not a positive multiple of 4 MiB, passes < 1, NULL or misaligned
+ * pointers; E_HIP. */
+#define FIBATT_FABRIC_OUT_BYTES (16 * 8 * 128)
+int fibatt_fabric_read(const void* buf, int64_t bytes, int32_t passes, void* out,
+                       void* stream);
+
 /* Message describing the last error on the calling thread ("" if none).
  * The pointer stays valid until the thread's next fibatt_* call. */
 const char* fibatt_last_error(void);

@@ -13,6 +13,7 @@ from .fibatt import (  # noqa: F401
     EXPORTED,
     F32,
     LIB_PATH,
+    FABRIC_OUT_BYTES,
     MAX_HEADS,
     OK,
     FibattError,
@@ -23,6 +24,7 @@ from .fibatt import (  # noqa: F401
     FibottentionQKVFunction,
     FibottentionTable,
     backward,
+    fabric_read,
     forward,
     hbm_stream,
     lib,

@@ -19,9 +19,10 @@
 //  * dkdv: per key row and group of four displacements, the queries' Q and dO
 //    rows are read once for both the recomputed scores and the accumulation
 //    of dV += P dO and dK += dS Q.
-// The accumulations over a group of four displacements use v_dot2_f32_bf16 on
-// pairs of them (axpy4_dot2: P and dS rounded to bf16, sums in fp32), except
-// dQ for d_h = 128, whose padded slots read nothing.
+// For d_h = 64 the accumulations over a group of four displacements use
+// v_dot2_f32_bf16 on pairs of them (axpy4_dot2: P and dS rounded to bf16,
+// sums in fp32).  d_h = 128 keeps fp32 coefficients: it is bound by its
+// vector-memory traffic, where fewer VALU instructions measured slower.
 // Lanes past the last row repeat row N - 1 and write identical values.
 #include "tile_bf16_common.h"
 
@@ -310,8 +311,16 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
     float pg[4], dsg[4];
     gather4q(p, pg);
     gather4q(p * (dp - d_j), dsg);
-    axpy4_dot2(dv, pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3]), of);
-    axpy4_dot2(dk, pack_bf16x2(dsg[0], dsg[1]), pack_bf16x2(dsg[2], dsg[3]), qf);
+    if constexpr (NQ == 1) {
+      axpy4_dot2(dv, pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3]), of);
+      axpy4_dot2(dk, pack_bf16x2(dsg[0], dsg[1]), pack_bf16x2(dsg[2], dsg[3]), qf);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        axpy_bf16(dv, pg[j], of[j]);
+        axpy_bf16(dk, dsg[j], qf[j]);
+      }
+    }
   }
   if constexpr (CLS) {
     u32x4 q0f[2], o0f[2];

@@ -1,9 +1,17 @@
-// fibatt_hbm_stream: a measurement aid that moves a pass's HBM bytes with
-// nothing else in it (reads of n_src arrays, writes of n_dst arrays), so the
-// bandwidth HBM delivers at that read/write mix on this GPU can be set beside
-// the attention kernels' achieved bandwidth.  Grid-stride over 16-byte
-// units, non-temporal loads; every written unit is the xor of the units read,
-// so no load can be dropped.
+// Measurement aids.
+//
+// fibatt_hbm_stream moves a pass's HBM bytes with nothing else in it (reads
+// of n_src arrays, writes of n_dst arrays), so the bandwidth HBM delivers at
+// that read/write mix on this GPU can be set beside the attention kernels'
+// achieved bandwidth.  Grid-stride over 16-byte units, non-temporal loads;
+// every written unit is the xor of the units read, so no load can be
+// dropped.
+//
+// fibatt_fabric_read measures the rate at which the XCDs' L2 caches can be
+// filled from beyond them (Infinity Cache or HBM): every XCD streams the
+// whole buffer, `passes` times, so with a buffer larger than an L2 every
+// read misses there.  The long-sequence kernels' L2 misses (their
+// FETCH_SIZE) are bounded by this rate.
 #include <hip/hip_runtime.h>
 
 #include "../../include/fibatt.h"
@@ -36,6 +44,39 @@ __global__ void __launch_bounds__(kThreads) hbm_stream_kernel(StreamArgs a) {
       if (a.scale == 2) a.dst[j][a.units + i] = x ^ u32x4{1u, 2u, 3u, 4u};
     }
   }
+}
+
+constexpr int kFabricPerXcd = 128;  // workgroups per XCD
+constexpr int kFabricUnroll = 8;     // 16-byte units per thread and trip
+
+// Workgroup b runs on XCD b mod 8 (the dispatcher deals workgroups to the
+// XCDs round-robin); the kFabricPerXcd workgroups of an XCD stride over all
+// `units` of the buffer, `passes` times.  units is a multiple of
+// kFabricPerXcd * 256 * kFabricUnroll, so every index is in range.  Each
+// workgroup writes the xor of what it read to out[blockIdx.x].
+__global__ void __launch_bounds__(kThreads) fabric_read_kernel(const u32x4* __restrict__ a,
+                                                               u32x4* __restrict__ out,
+                                                               int64_t units, int passes) {
+  __shared__ u32x4 red[kThreads];
+  const int64_t k = blockIdx.x / 8;
+  const int64_t step = static_cast<int64_t>(kFabricPerXcd) * kThreads * kFabricUnroll;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int p = 0; p < passes; ++p) {
+    for (int64_t i = k * kThreads * kFabricUnroll + threadIdx.x; i < units; i += step) {
+      u32x4 x[kFabricUnroll];
+#pragma unroll
+      for (int u = 0; u < kFabricUnroll; ++u) x[u] = a[i + u * kThreads];
+#pragma unroll
+      for (int u = 0; u < kFabricUnroll; ++u) acc ^= x[u];
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w /= 2) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] ^= red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
 }  // namespace
@@ -75,5 +116,24 @@ extern "C" int fibatt_hbm_stream(const void* const* src, int32_t n_src, void* co
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(FIBATT_E_HIP, "fibatt_hbm_stream launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int fibatt_fabric_read(const void* buf, int64_t bytes, int32_t passes, void* out,
+                                  void* stream) {
+  fibatt::LaunchGuard guard;
+  constexpr int64_t kQuantum =
+      static_cast<int64_t>(kFabricPerXcd) * kThreads * kFabricUnroll * 16;  // 4 MiB
+  if (bytes <= 0 || bytes % kQuantum)
+    return fail(FIBATT_E_INVAL, "fibatt_fabric_read: bytes must be a positive multiple of 4 MiB");
+  if (passes < 1) return fail(FIBATT_E_INVAL, "fibatt_fabric_read: passes must be >= 1");
+  int rc;
+  if ((rc = check_ptr(buf, "buf")) || (rc = check_ptr(out, "out"))) return rc;
+  fibatt::launch(fabric_read_kernel, dim3(8 * kFabricPerXcd), dim3(kThreads), 0,
+                 static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf),
+                 static_cast<u32x4*>(out), bytes / 16, static_cast<int>(passes));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(FIBATT_E_HIP, "fibatt_fabric_read launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -28,7 +28,8 @@ EXPORTED = ("fibatt_wythoff", "fibatt_wythoff_modified", "fibatt_windows", "fiba
             "fibatt_bwd_cls_workspace_floats", "fibatt_fwd_table", "fibatt_bwd_table",
             "fibatt_fwd_table_workspace_floats", "fibatt_bwd_table_workspace_floats",
             "fibatt_fwd_strided", "fibatt_bwd_strided", "fibatt_bwd_noalloc",
-            "fibatt_time_next_call", "fibatt_hbm_stream", "fibatt_last_error")
+            "fibatt_time_next_call", "fibatt_hbm_stream", "fibatt_fabric_read",
+            "fibatt_last_error")
 
 
 class FibattError(RuntimeError):
@@ -128,6 +129,8 @@ def lib() -> ctypes.CDLL:
     L.fibatt_time_next_call.restype = ctypes.c_int
     L.fibatt_hbm_stream.argtypes = [ctypes.POINTER(vp), ctypes.c_int32, ctypes.POINTER(vp),
                                     ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp]
+    L.fibatt_fabric_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp]
+    L.fibatt_fabric_read.restype = ctypes.c_int
     L.fibatt_hbm_stream.restype = ctypes.c_int
     L.fibatt_last_error.argtypes = []
     L.fibatt_last_error.restype = ctypes.c_char_p
@@ -514,3 +517,21 @@ def hbm_stream(src: Sequence[torch.Tensor], dst: Sequence[torch.Tensor], nbytes:
     D = (ctypes.c_void_p * len(dst))(*[t.data_ptr() for t in dst])
     s = _current_stream(src[0].device) if stream is None else stream
     _check(lib().fibatt_hbm_stream(S, len(src), D, len(dst), nbytes, dst_scale, s))
+
+
+FABRIC_OUT_BYTES = 16 * 8 * 128
+
+
+def fabric_read(buf: torch.Tensor, passes: int, out: torch.Tensor,
+                stream: Optional[int] = None) -> None:
+    """fibatt_fabric_read: every XCD reads all of `buf` (contiguous device
+    tensor, a multiple of 4 MiB) `passes` times; `out` receives one 16-byte
+    xor per workgroup (FABRIC_OUT_BYTES).  Measurement aid."""
+    for t in (buf, out):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("fabric_read takes contiguous device tensors")
+    if out.numel() * out.element_size() < FABRIC_OUT_BYTES:
+        raise ValueError("out is smaller than FABRIC_OUT_BYTES")
+    s = _current_stream(buf.device) if stream is None else stream
+    _check(lib().fibatt_fabric_read(buf.data_ptr(), buf.numel() * buf.element_size(), passes,
+                                    out.data_ptr(), s))

@@ -490,3 +490,26 @@ def test_strided_entry_points_reject_bad_arguments():
         assert b"aligned" in fa.lib().fibatt_last_error()
     bad = _Case(w=[65, 66, 65])
     assert _fwd_s(bad.desc, ls) == fa.E_INVAL
+
+
+def test_measurement_aids_reject_bad_arguments():
+    L = fa.lib()
+    fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+    arr = (ctypes.c_void_p * 1)(fake.value)
+    # fibatt_hbm_stream
+    assert L.fibatt_hbm_stream(arr, 0, arr, 1, 1024, 1, None) == fb.E_INVAL
+    assert L.fibatt_hbm_stream(arr, 1, arr, 5, 1024, 1, None) == fb.E_INVAL
+    assert L.fibatt_hbm_stream(arr, 1, arr, 1, 1024, 3, None) == fb.E_INVAL
+    assert L.fibatt_hbm_stream(arr, 1, arr, 1, 1000, 1, None) == fb.E_INVAL
+    assert "multiple of 16" in L.fibatt_last_error().decode()
+    # fibatt_fabric_read
+    mib4 = 4 * 1024 * 1024
+    assert L.fibatt_fabric_read(fake, mib4 + 16, 1, fake, None) == fb.E_INVAL
+    assert "multiple of 4 MiB" in L.fibatt_last_error().decode()
+    assert L.fibatt_fabric_read(fake, 0, 1, fake, None) == fb.E_INVAL
+    assert L.fibatt_fabric_read(fake, mib4, 0, fake, None) == fb.E_INVAL
+    assert L.fibatt_fabric_read(None, mib4, 1, fake, None) == fb.E_INVAL
+    assert L.fibatt_fabric_read(ctypes.c_void_p(0x10004), mib4, 1, fake, None) == fb.E_INVAL
+    # fibatt_time_next_call: both or neither event
+    assert L.fibatt_time_next_call(fake, None) == fb.E_INVAL
+    assert L.fibatt_time_next_call(None, None) == fb.OK

@@ -1,5 +1,7 @@
 """The measurement aids of the library on the GPU: fibatt_hbm_stream moves
-the bytes it says (every written unit is the xor of the units read), and
+the bytes it says (every written unit is the xor of the units read),
+fibatt_fabric_read reads every unit of its buffer once per pass on every XCD
+(each workgroup's xor is that of the units it strides over), and
 fibatt_time_next_call brackets exactly one call's kernels (its time lies
 inside the time of events recorded around the call, and the binding is gone
 afterwards)."""
@@ -36,6 +38,31 @@ def test_hbm_stream_writes_the_xor_of_its_reads(n_src, n_dst, scale):
         if scale == 2:
             pat = torch.tensor([1, 2, 3, 4], dtype=torch.int32, device="cuda:0").repeat(words // 4)
             assert torch.equal(d[words:], x ^ pat)
+
+
+@pytest.mark.parametrize("mib,passes", [(4, 1), (12, 1), (8, 2), (4, 3)])
+def test_fabric_read_xors_every_unit(mib, passes):
+    words = mib * 1024 * 1024 // 4
+    buf = _rand_words(words, 100 + mib)
+    out = torch.full((fa.FABRIC_OUT_BYTES // 4,), -1, dtype=torch.int32, device="cuda:0")
+    fa.fabric_read(buf, passes, out)
+    torch.cuda.synchronize()
+    # Workgroup b (XCD b % 8, index k = b // 8 of 128) reads the 2048-unit
+    # chunks c with c % 128 == k; its xor over an even number of passes is 0.
+    r = buf.view(-1, 128, 2048, 4)
+    x = r[0].clone()
+    for i in range(1, r.shape[0]):
+        x ^= r[i]
+    while x.shape[1] > 1:
+        h = x.shape[1] // 2
+        x = x[:, :h] ^ x[:, h:]
+    x = x[:, 0]  # [128, 4]
+    if passes % 2 == 0:
+        x = torch.zeros_like(x)
+    got = out.view(-1, 4)
+    assert got.shape[0] == 8 * 128
+    for b in range(8 * 128):
+        assert torch.equal(got[b], x[b // 8]), b
 
 
 def _events(n):

@@ -19,12 +19,17 @@
 //  * dkdv: per key row and group of four displacements, the queries' Q and dO
 //    rows are read once for both the recomputed scores and the accumulation
 //    of dV += P dO and dK += dS Q.
+// With d_h = 64 and the plain mask (when the slab's byte offsets fit 32
+// bits) the same two kernels run as bwd_dq_win_kernel and bwd_dkdv_win_kernel:
+// tiles of 128 rows with the near gathered rows in an LDS window
+// (window_bf16_common.h).
 // For d_h = 64 the accumulations over a group of four displacements use
 // v_dot2_f32_bf16 on pairs of them (axpy4_dot2: P and dS rounded to bf16,
 // sums in fp32).  d_h = 128 keeps fp32 coefficients: it is bound by its
 // vector-memory traffic, where fewer VALU instructions measured slower.
 // Lanes past the last row repeat row N - 1 and write identical values.
 #include "tile_bf16_common.h"
+#include "window_bf16_common.h"
 
 namespace fibatt {
 namespace {
@@ -340,6 +345,276 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
                 1.0f);
 }
 
+// d_h = 64 (plain mask, slab offsets within 32 bits): the same two kernels on
+// tiles of 128 rows with the gathered rows within win::kDn of the tile staged
+// in an LDS window (K and V for dq, Q and dO for dkdv; layout and lane order
+// in window_bf16_common.h), the far ones read through buffer loads.
+template <int MH, int KG, bool STR>
+__global__ void __launch_bounds__(win::kThreads) __attribute__((amdgpu_waves_per_eu(win::kWavesPerSimd)))
+bwd_dq_win_kernel(BwdTileArgs<MH> a) {
+  using namespace win;
+  constexpr int kRowB16 = Geo<1>::kRowB;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const kwin = smem;
+  char* const vwin = smem + kTensorBytes;
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
+  __shared__ int s_nd;
+  __shared__ int s_gn;
+  const int w = tile_of_block(a.per_xcd, a.chunk, a.tiles);
+  if (w < 0 || w >= a.work) return;  // whole workgroup, before any barrier
+  const int slab = w / a.tiles;
+  const int tile = w - slab * a.tiles;
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const int lane = tid & 63;
+  const int part = lane & 3;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int qrow = tid >> 2;
+  const int la = lane_unit_a(lane);
+  const int dlb = lane_unit_b(lane) - la;
+  const int t0 = tile * kT;
+  const int row = t0 + qrow;
+  const int rr = row < N ? row : N - 1;
+  const size_t rbase = static_cast<size_t>(slab) * N;
+  const int rk = STR ? static_cast<int>(a.lk.row_bytes(2)) : kRowB16;
+  const int rv = STR ? static_cast<int>(a.lv.row_bytes(2)) : kRowB16;
+  const Rsrc kres = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.k, a.lk, slab, a.H, N, 0), N, rk);
+  const Rsrc vres = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.v, a.lv, slab, a.H, N, 0), N, rv);
+  const int wa = ((rr - t0 + kDn) << 7) + la;  // window offset of row rr's fragment a
+  const int ka = rr * rk + la, va = rr * rv + la;
+
+  // The window, the lane's own Q and dO rows and its LSE are requested
+  // before the displacement list is built.
+  u32x4 wk[kFill][2], wv[kFill][2];
+#pragma unroll
+  for (int i = 0; i < kFill; ++i) {
+    const int x = qrow + i * kT;
+    if (x < kR) {
+      const int r = t0 - kDn + x;
+      buf_frag(kres, r * rk + la, dlb, wk[i]);
+      buf_frag(vres, r * rv + la, dlb, wv[i]);
+    }
+  }
+  u32x4 qf[2], df[2];
+  {
+    const char* qp = tile_row_ptr<STR, kRowB16>(a.q, a.lq, slab, a.H, N, rr);
+    const char* dp = tile_row_ptr<STR, kRowB16>(a.dout, a.ldo, slab, a.H, N, rr);
+    qf[0] = *reinterpret_cast<const u32x4*>(qp + la);
+    qf[1] = *reinterpret_cast<const u32x4*>(qp + la + dlb);
+    df[0] = *reinterpret_cast<const u32x4*>(dp + la);
+    df[1] = *reinterpret_cast<const u32x4*>(dp + la + dlb);
+  }
+  const float lse_r = a.lse[rbase + rr];
+  if (tid == 0) {
+    build_deltas(a.ht, slab % a.H, s_dist, s_deltas, &s_nd);
+    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;  // a whole last group
+    s_gn = near_groups(s_deltas, s_nd);
+  }
+#pragma unroll
+  for (int i = 0; i < kFill; ++i) {
+    const int x = qrow + i * kT;
+    if (x < kR) {
+      write_frag(kwin, (x << 7) + la, dlb, wk[i]);
+      write_frag(vwin, (x << 7) + la, dlb, wv[i]);
+    }
+  }
+  __syncthreads();
+  const int nd = __builtin_amdgcn_readfirstlane(s_nd);
+  const int gn = __builtin_amdgcn_readfirstlane(s_gn);
+  uint32_t qw[8], dw[8];
+  frag_words(qf, qw);
+  frag_words(df, dw);
+  const float lse2 = lse_r * kLog2e;
+
+  auto load_group = [&](int g, const char* wbase, const Rsrc& res, int ga, int rs,
+                        u32x4 (&f)[4][2]) {
+    int d[4];
+    group_deltas(s_deltas, g, d);
+    if (g < gn) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) read_frag(wbase, wa + (d[j] << 7), dlb, f[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_frag(res, ga + d[j] * rs, dlb, f[j]);
+    }
+  };
+
+  // Pass 1: P and dP, one pair per lane and group; D = sum P dP.
+  float pw[KG], dpw[KG];
+  float dl = 0.f;
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    pw[g] = 0.f;
+    dpw[g] = 0.f;
+    if (4 * g < nd) {
+      u32x4 kf[4][2], vf[4][2];
+      load_group(g, kwin, kres, ka, rk, kf);
+      load_group(g, vwin, vres, va, rv, vf);
+      float ps[4], pp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ps[j] = dot_part(qw, kf[j]);
+        pp[j] = dot_part(dw, vf[j]);
+      }
+      const float sc = reduce4q(ps, b0, b1);
+      const float dp = reduce4q(pp, b0, b1);
+      const int kk = rr + s_deltas[4 * g + part];
+      const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
+      const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse2)) : 0.f;
+      pw[g] = p;
+      dpw[g] = dp;
+      dl = __builtin_fmaf(p, dp, dl);
+    }
+  }
+  const float dd = quad_sum4(dl);
+
+  // Pass 2: dQ = sum dS K / sqrt(d).
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    if (4 * g < nd) {
+      float ds[4];
+      gather4q(pw[g] * (dpw[g] - dd), ds);  // 0 in padded slots (P = 0 there)
+      u32x4 kf[4][2];
+      load_group(g, kwin, kres, ka, rk, kf);
+      axpy4_dot2(acc, pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), kf);
+    }
+  }
+  if (row < N) {
+    store_frag_f32(reinterpret_cast<char*>(tile_row_f32<STR, 64>(a.dq, a.ldq, slab, a.H, N, rr)),
+                   la, dlb, acc, a.scale);
+    if (part == 0) a.ws[rbase + rr] = dd;
+  }
+}
+
+template <int MH, bool STR>
+__global__ void __launch_bounds__(win::kThreads) __attribute__((amdgpu_waves_per_eu(win::kWavesPerSimd)))
+bwd_dkdv_win_kernel(BwdTileArgs<MH> a) {
+  using namespace win;
+  constexpr int kRowB16 = Geo<1>::kRowB;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const qwin = smem;
+  char* const owin = smem + kTensorBytes;
+  __shared__ int s_dist[kMaxOffsets];
+  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
+  __shared__ int s_nd;
+  __shared__ int s_gn;
+  const int w = tile_of_block(a.per_xcd, a.chunk, a.tiles);
+  if (w < 0 || w >= a.work) return;  // whole workgroup, before any barrier
+  const int slab = w / a.tiles;
+  const int tile = w - slab * a.tiles;
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const int lane = tid & 63;
+  const int part = lane & 3;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int qrow = tid >> 2;
+  const int la = lane_unit_a(lane);
+  const int dlb = lane_unit_b(lane) - la;
+  const int t0 = tile * kT;
+  const int row = t0 + qrow;
+  const int rr = row < N ? row : N - 1;  // key row
+  const size_t rbase = static_cast<size_t>(slab) * N;
+  const int rq = STR ? static_cast<int>(a.lq.row_bytes(2)) : kRowB16;
+  const int ro = STR ? static_cast<int>(a.ldo.row_bytes(2)) : kRowB16;
+  const Rsrc qres = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.q, a.lq, slab, a.H, N, 0), N, rq);
+  const Rsrc ores = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.dout, a.ldo, slab, a.H, N, 0), N, ro);
+  const int wa = ((rr - t0 + kDn) << 7) + la;
+  const int qa = rr * rq + la, oa = rr * ro + la;
+
+  u32x4 wq[kFill][2], wo[kFill][2];
+#pragma unroll
+  for (int i = 0; i < kFill; ++i) {
+    const int x = qrow + i * kT;
+    if (x < kR) {
+      const int r = t0 - kDn + x;
+      buf_frag(qres, r * rq + la, dlb, wq[i]);
+      buf_frag(ores, r * ro + la, dlb, wo[i]);
+    }
+  }
+  u32x4 kf0[2], vf0[2];
+  {
+    const char* kp = tile_row_ptr<STR, kRowB16>(a.k, a.lk, slab, a.H, N, rr);
+    const char* vp = tile_row_ptr<STR, kRowB16>(a.v, a.lv, slab, a.H, N, rr);
+    kf0[0] = *reinterpret_cast<const u32x4*>(kp + la);
+    kf0[1] = *reinterpret_cast<const u32x4*>(kp + la + dlb);
+    vf0[0] = *reinterpret_cast<const u32x4*>(vp + la);
+    vf0[1] = *reinterpret_cast<const u32x4*>(vp + la + dlb);
+  }
+  if (tid == 0) {
+    build_deltas(a.ht, slab % a.H, s_dist, s_deltas, &s_nd);
+    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;
+    s_gn = near_groups(s_deltas, s_nd);
+  }
+#pragma unroll
+  for (int i = 0; i < kFill; ++i) {
+    const int x = qrow + i * kT;
+    if (x < kR) {
+      write_frag(qwin, (x << 7) + la, dlb, wq[i]);
+      write_frag(owin, (x << 7) + la, dlb, wo[i]);
+    }
+  }
+  __syncthreads();
+  const int nd = __builtin_amdgcn_readfirstlane(s_nd);
+  const int gn = __builtin_amdgcn_readfirstlane(s_gn);
+  uint32_t kw[8], vw[8];
+  frag_words(kf0, kw);
+  frag_words(vf0, vw);
+  float dk[16], dv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    dk[e] = 0.f;
+    dv[e] = 0.f;
+  }
+  for (int g = 0; 4 * g < nd; ++g) {
+    int d[4];
+    group_deltas(s_deltas, g, d);
+    // This lane's query (slot p of the group) and its LSE and D.
+    const int jj = rr + s_deltas[4 * g + part];
+    const bool ok = 4 * g + part < nd && static_cast<unsigned>(jj) < static_cast<unsigned>(N);
+    const int jc = clamp_row(jj, N);
+    const float lse_j = a.lse[rbase + jc];
+    const float d_j = a.ws[rbase + jc];
+    u32x4 qf[4][2], of[4][2];
+    if (g < gn) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        read_frag(qwin, wa + (d[j] << 7), dlb, qf[j]);
+        read_frag(owin, wa + (d[j] << 7), dlb, of[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        buf_frag(qres, qa + d[j] * rq, dlb, qf[j]);
+        buf_frag(ores, oa + d[j] * ro, dlb, of[j]);
+      }
+    }
+    float ps[4], pp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ps[j] = dot_part(kw, qf[j]);
+      pp[j] = dot_part(vw, of[j]);
+    }
+    const float sc = reduce4q(ps, b0, b1);
+    const float dp = reduce4q(pp, b0, b1);
+    const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse_j * kLog2e)) : 0.f;
+    float pg[4], dsg[4];
+    gather4q(p, pg);
+    gather4q(p * (dp - d_j), dsg);
+    axpy4_dot2(dv, pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3]), of);
+    axpy4_dot2(dk, pack_bf16x2(dsg[0], dsg[1]), pack_bf16x2(dsg[2], dsg[3]), qf);
+  }
+  if (row < N) {
+    store_frag_f32(reinterpret_cast<char*>(tile_row_f32<STR, 64>(a.dk, a.ldk, slab, a.H, N, rr)),
+                   la, dlb, dk, a.scale);
+    store_frag_f32(reinterpret_cast<char*>(tile_row_f32<STR, 64>(a.dv, a.ldv, slab, a.H, N, rr)),
+                   la, dlb, dv, 1.0f);
+  }
+}
+
 template <int MH, int KG, int NQ, bool CLS>
 void launch_dq(const BwdTileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
   if (strided)
@@ -403,6 +678,73 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   return hipGetLastError();
 }
 
+template <int MH, int KG>
+hipError_t launch_dq_win(const BwdTileArgs<MH>& a, bool strided, unsigned grid,
+                         hipStream_t stream) {
+  constexpr size_t kLds = 2 * win::kTensorBytes;
+  static const hipError_t attr_s = win::allow_lds(bwd_dq_win_kernel<MH, KG, true>, kLds);
+  static const hipError_t attr_d = win::allow_lds(bwd_dq_win_kernel<MH, KG, false>, kLds);
+  if ((strided ? attr_s : attr_d) != hipSuccess) return strided ? attr_s : attr_d;
+  launch(strided ? bwd_dq_win_kernel<MH, KG, true> : bwd_dq_win_kernel<MH, KG, false>,
+         dim3(grid), dim3(win::kThreads), kLds, stream, a);
+  return hipSuccess;
+}
+
+// The backward for d_h = 64 with the plain mask on the window kernels.
+template <int MH>
+hipError_t launch_win(const Problem& p, const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      float* ws, hipStream_t stream) {
+  BwdTileArgs<MH> a;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.dout = static_cast<const char*>(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = ws;
+  a.H = p.H;
+  a.N = p.N;
+  a.scale = 0.125f;  // 1 / sqrt(64)
+  a.c = kLog2e * a.scale;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.ldo = p.ldo;
+  a.ldq = p.ldq;
+  a.ldk = p.ldk;
+  a.ldv = p.ldv;
+  a.ht = shrink_heads<MH>(p.heads, p.H);
+  const long long slabs = static_cast<long long>(p.B) * p.H;
+  a.tiles = (p.N + win::kT - 1) / win::kT;
+  const long long work = slabs * a.tiles;
+  if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
+  a.work = static_cast<int>(work);
+  const long long grid_ll = tile_grid(slabs, a.tiles, 2ll * p.N * win::kRowB, a.per_xcd, a.chunk);
+  if (grid_ll > 0x7fffffffll) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(grid_ll);
+  const int groups = (max_signed(p) + 3) / 4;
+  hipError_t e;
+  if (groups <= 4)
+    e = launch_dq_win<MH, 4>(a, p.strided, grid, stream);
+  else if (groups <= 8)
+    e = launch_dq_win<MH, 8>(a, p.strided, grid, stream);
+  else if (groups <= 12)
+    e = launch_dq_win<MH, 12>(a, p.strided, grid, stream);
+  else
+    e = launch_dq_win<MH, (kMaxSigned + 3) / 4>(a, p.strided, grid, stream);
+  if (e != hipSuccess) return e;
+  constexpr size_t kLds = 2 * win::kTensorBytes;
+  static const hipError_t attr_s = win::allow_lds(bwd_dkdv_win_kernel<MH, true>, kLds);
+  static const hipError_t attr_d = win::allow_lds(bwd_dkdv_win_kernel<MH, false>, kLds);
+  if ((p.strided ? attr_s : attr_d) != hipSuccess) return p.strided ? attr_s : attr_d;
+  launch(p.strided ? bwd_dkdv_win_kernel<MH, true> : bwd_dkdv_win_kernel<MH, false>, dim3(grid),
+         dim3(win::kThreads), kLds, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool bwd_tile_bf16_fits(const Problem& p) {
@@ -417,6 +759,11 @@ hipError_t launch_cls(const Problem& p, const void* q, const void* k, const void
     if (p.H <= kSmallHeads)
       return launch_t<kSmallHeads, 2, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
     return launch_t<kMaxHeads, 2, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+  }
+  if (!CLS && win::fits(p)) {
+    if (p.H <= kSmallHeads)
+      return launch_win<kSmallHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    return launch_win<kMaxHeads>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
   }
   if (p.H <= kSmallHeads)
     return launch_t<kSmallHeads, 1, CLS>(p, q, k, v, lse, dout, dq, dk, dv, ws, stream);

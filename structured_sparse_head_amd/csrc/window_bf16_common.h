@@ -84,6 +84,19 @@ __device__ __forceinline__ void buf_frag(const Rsrc& r, int off, int db, u32x4 (
   f[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + db, 0, 0));
 }
 
+// Stores a lane's 16 fp32 values (fragment a's elements in x[0..7], b's in
+// x[8..15]) times `scale` into an fp32 row of 64; la and la + db are the
+// fragments' byte offsets in a bf16 row, so 2 la and 2 (la + db) in fp32.
+__device__ __forceinline__ void store_frag_f32(char* row, int la, int db, const float (&x)[16],
+                                               float scale) {
+  float4* a = reinterpret_cast<float4*>(row + 2 * la);
+  float4* b = reinterpret_cast<float4*>(row + 2 * (la + db));
+  a[0] = make_float4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+  a[1] = make_float4(x[4] * scale, x[5] * scale, x[6] * scale, x[7] * scale);
+  b[0] = make_float4(x[8] * scale, x[9] * scale, x[10] * scale, x[11] * scale);
+  b[1] = make_float4(x[12] * scale, x[13] * scale, x[14] * scale, x[15] * scale);
+}
+
 // Whether displacement d (wave-uniform) is read from the window.
 __device__ __forceinline__ bool near(int d) {
   return static_cast<unsigned>(d + kDn) <= static_cast<unsigned>(2 * kDn);

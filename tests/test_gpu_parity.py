@@ -605,6 +605,18 @@ TABLES = [
      True),
     ("fp32 N70 class token random sets", 2, 70, 128, torch.float32,
      [sorted(_rng_sets.choice(70, size=s, replace=False).tolist()) for s in (0, 3, 30)], True),
+    # The long-sequence d_h = 64 kernels read displacements |delta| <= 88
+    # from an LDS window when all four of a group are that near: groups
+    # entirely inside, straddling and outside the edge, far-only heads, and
+    # distances reaching both ends of the slab.
+    ("bf16 N600 window edge", 2, 600, 64, torch.bfloat16,
+     [[1, 2, 87, 88], [88, 89, 90, 200], [0, 87, 88, 89, 300, 599], [89]], False),
+    ("bf16 N600 window edge class token", 1, 600, 64, torch.bfloat16,
+     [[1, 2, 87, 88], [0, 87, 88, 89, 300, 599]], True),
+    ("bf16 N300 sliding windows 64 and 40", 1, 300, 64, torch.bfloat16,
+     [list(range(1, 65)), list(range(0, 40))], False),
+    ("bf16 N2100 far distances", 1, 2100, 64, torch.bfloat16,
+     [[500, 1000, 2000], [1, 1500, 2099]], False),
 ]
 
 
@@ -633,7 +645,7 @@ def test_distance_table_heads(case, path):
 
 
 @pytest.mark.parametrize("shape", [(2, 12, 197, 64, torch.bfloat16), (1, 4, 700, 128, torch.bfloat16),
-                                   (2, 3, 65, 64, torch.float32)])
+                                   (1, 6, 1569, 64, torch.bfloat16), (2, 3, 65, 64, torch.float32)])
 def test_fibonacci_table_matches_wythoff_heads_bitwise(shape):
     B, H, N, d, dtype = shape
     _say(f"case: Fibonacci table vs (a, b, w) heads B={B} H={H} N={N} d={d} {dtype}")

@@ -91,8 +91,8 @@ def pass_bytes(wl, esize):
 KERNELS = {
     1: {"fwd": ["fwd_slab_kernel"], "bwd": ["bwd_slab_kernel"]},
     2: {"fwd": ["fwd_slab_bf16_kernel"], "bwd": ["bwd_slab_bf16_kernel"]},
-    3: {"fwd": ["fwd_win_bf16_kernel"], "bwd": ["bwd_dq_win_kernel", "bwd_dkdv_win_kernel"]},
-    4: {"fwd": ["fwd_win_bf16_kernel"], "bwd": ["bwd_dq_win_kernel", "bwd_dkdv_win_kernel"]},
+    3: {"fwd": ["fwd_win_bf16_kernel"], "bwd": ["bwd_dq_win_kernel", "bwd_dkdv_tile_kernel"]},
+    4: {"fwd": ["fwd_win_bf16_kernel"], "bwd": ["bwd_dq_win_kernel", "bwd_dkdv_tile_kernel"]},
     5: {"fwd": ["fwd_tile_bf16_kernel"], "bwd": ["bwd_dq_tile_kernel", "bwd_dkdv_tile_kernel"]},
 }
 SOURCES = {
@@ -107,8 +107,6 @@ SOURCES = {
     "bwd_dkdv_tile_kernel": ["bwd_tile_bf16.hip", "tile_bf16_common.h", "slab_bf16_common.h"],
     "bwd_dq_win_kernel": ["bwd_tile_bf16.hip", "window_bf16_common.h", "tile_bf16_common.h",
                           "slab_bf16_common.h"],
-    "bwd_dkdv_win_kernel": ["bwd_tile_bf16.hip", "window_bf16_common.h", "tile_bf16_common.h",
-                            "slab_bf16_common.h"],
 }
 
 

@@ -20,9 +20,8 @@
 //    rows are read once for both the recomputed scores and the accumulation
 //    of dV += P dO and dK += dS Q.
 // With d_h = 64 and the plain mask (when the slab's byte offsets fit 32
-// bits) the same two kernels run as bwd_dq_win_kernel and bwd_dkdv_win_kernel:
-// tiles of 128 rows with the near gathered rows in an LDS window
-// (window_bf16_common.h).
+// bits) the query pass runs as bwd_dq_win_kernel: tiles of 128 rows with the
+// K and V rows near the tile in an LDS window (window_bf16_common.h).
 // For d_h = 64 the accumulations over a group of four displacements use
 // v_dot2_f32_bf16 on pairs of them (axpy4_dot2: P and dS rounded to bf16,
 // sums in fp32).  d_h = 128 keeps fp32 coefficients: it is bound by its
@@ -490,131 +489,6 @@ bwd_dq_win_kernel(BwdTileArgs<MH> a) {
   }
 }
 
-template <int MH, bool STR>
-__global__ void __launch_bounds__(win::kThreads) __attribute__((amdgpu_waves_per_eu(win::kWavesPerSimd)))
-bwd_dkdv_win_kernel(BwdTileArgs<MH> a) {
-  using namespace win;
-  constexpr int kRowB16 = Geo<1>::kRowB;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const qwin = smem;
-  char* const owin = smem + kTensorBytes;
-  __shared__ int s_dist[kMaxOffsets];
-  __shared__ __attribute__((aligned(16))) int s_deltas[kMaxSigned + 4];
-  __shared__ int s_nd;
-  __shared__ int s_gn;
-  const int w = tile_of_block(a.per_xcd, a.chunk, a.tiles);
-  if (w < 0 || w >= a.work) return;  // whole workgroup, before any barrier
-  const int slab = w / a.tiles;
-  const int tile = w - slab * a.tiles;
-  const int tid = threadIdx.x;
-  const int N = a.N;
-  const int lane = tid & 63;
-  const int part = lane & 3;
-  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
-  const int qrow = tid >> 2;
-  const int la = lane_unit_a(lane);
-  const int dlb = lane_unit_b(lane) - la;
-  const int t0 = tile * kT;
-  const int row = t0 + qrow;
-  const int rr = row < N ? row : N - 1;  // key row
-  const size_t rbase = static_cast<size_t>(slab) * N;
-  const int rq = STR ? static_cast<int>(a.lq.row_bytes(2)) : kRowB16;
-  const int ro = STR ? static_cast<int>(a.ldo.row_bytes(2)) : kRowB16;
-  const Rsrc qres = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.q, a.lq, slab, a.H, N, 0), N, rq);
-  const Rsrc ores = slab_rsrc(tile_row_ptr<STR, kRowB16>(a.dout, a.ldo, slab, a.H, N, 0), N, ro);
-  const int wa = ((rr - t0 + kDn) << 7) + la;
-  const int qa = rr * rq + la, oa = rr * ro + la;
-
-  u32x4 wq[kFill][2], wo[kFill][2];
-#pragma unroll
-  for (int i = 0; i < kFill; ++i) {
-    const int x = qrow + i * kT;
-    if (x < kR) {
-      const int r = t0 - kDn + x;
-      buf_frag(qres, r * rq + la, dlb, wq[i]);
-      buf_frag(ores, r * ro + la, dlb, wo[i]);
-    }
-  }
-  u32x4 kf0[2], vf0[2];
-  {
-    const char* kp = tile_row_ptr<STR, kRowB16>(a.k, a.lk, slab, a.H, N, rr);
-    const char* vp = tile_row_ptr<STR, kRowB16>(a.v, a.lv, slab, a.H, N, rr);
-    kf0[0] = *reinterpret_cast<const u32x4*>(kp + la);
-    kf0[1] = *reinterpret_cast<const u32x4*>(kp + la + dlb);
-    vf0[0] = *reinterpret_cast<const u32x4*>(vp + la);
-    vf0[1] = *reinterpret_cast<const u32x4*>(vp + la + dlb);
-  }
-  if (tid == 0) {
-    build_deltas(a.ht, slab % a.H, s_dist, s_deltas, &s_nd);
-    for (int i = 0; i < 4; ++i) s_deltas[s_nd + i] = 0;
-    s_gn = near_groups(s_deltas, s_nd);
-  }
-#pragma unroll
-  for (int i = 0; i < kFill; ++i) {
-    const int x = qrow + i * kT;
-    if (x < kR) {
-      write_frag(qwin, (x << 7) + la, dlb, wq[i]);
-      write_frag(owin, (x << 7) + la, dlb, wo[i]);
-    }
-  }
-  __syncthreads();
-  const int nd = __builtin_amdgcn_readfirstlane(s_nd);
-  const int gn = __builtin_amdgcn_readfirstlane(s_gn);
-  uint32_t kw[8], vw[8];
-  frag_words(kf0, kw);
-  frag_words(vf0, vw);
-  float dk[16], dv[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    dk[e] = 0.f;
-    dv[e] = 0.f;
-  }
-  for (int g = 0; 4 * g < nd; ++g) {
-    int d[4];
-    group_deltas(s_deltas, g, d);
-    // This lane's query (slot p of the group) and its LSE and D.
-    const int jj = rr + s_deltas[4 * g + part];
-    const bool ok = 4 * g + part < nd && static_cast<unsigned>(jj) < static_cast<unsigned>(N);
-    const int jc = clamp_row(jj, N);
-    const float lse_j = a.lse[rbase + jc];
-    const float d_j = a.ws[rbase + jc];
-    u32x4 qf[4][2], of[4][2];
-    if (g < gn) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        read_frag(qwin, wa + (d[j] << 7), dlb, qf[j]);
-        read_frag(owin, wa + (d[j] << 7), dlb, of[j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        buf_frag(qres, qa + d[j] * rq, dlb, qf[j]);
-        buf_frag(ores, oa + d[j] * ro, dlb, of[j]);
-      }
-    }
-    float ps[4], pp[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ps[j] = dot_part(kw, qf[j]);
-      pp[j] = dot_part(vw, of[j]);
-    }
-    const float sc = reduce4q(ps, b0, b1);
-    const float dp = reduce4q(pp, b0, b1);
-    const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse_j * kLog2e)) : 0.f;
-    float pg[4], dsg[4];
-    gather4q(p, pg);
-    gather4q(p * (dp - d_j), dsg);
-    axpy4_dot2(dv, pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3]), of);
-    axpy4_dot2(dk, pack_bf16x2(dsg[0], dsg[1]), pack_bf16x2(dsg[2], dsg[3]), qf);
-  }
-  if (row < N) {
-    store_frag_f32(reinterpret_cast<char*>(tile_row_f32<STR, 64>(a.dk, a.ldk, slab, a.H, N, rr)),
-                   la, dlb, dk, a.scale);
-    store_frag_f32(reinterpret_cast<char*>(tile_row_f32<STR, 64>(a.dv, a.ldv, slab, a.H, N, rr)),
-                   la, dlb, dv, 1.0f);
-  }
-}
-
 template <int MH, int KG, int NQ, bool CLS>
 void launch_dq(const BwdTileArgs<MH>& a, bool strided, unsigned grid, hipStream_t stream) {
   if (strided)
@@ -625,10 +499,12 @@ void launch_dq(const BwdTileArgs<MH>& a, bool strided, unsigned grid, hipStream_
                        dim3(kTileThreads), 0, stream, a);
 }
 
-template <int MH, int NQ, bool CLS>
-hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
-                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                    float* ws, hipStream_t stream) {
+// Arguments shared by every backward kernel of this file, except the tile
+// geometry (tiles, work, per_xcd, chunk), which each launch fills in.
+template <int MH>
+BwdTileArgs<MH> make_args(const Problem& p, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                          float* ws, int d_h) {
   BwdTileArgs<MH> a;
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k);
@@ -641,7 +517,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.ws = ws;
   a.H = p.H;
   a.N = p.N;
-  a.scale = 1.0f / sqrtf(static_cast<float>(Geo<NQ>::kD));
+  a.scale = 1.0f / sqrtf(static_cast<float>(d_h));
   a.c = kLog2e * a.scale;
   a.lq = p.lq;
   a.lk = p.lk;
@@ -651,14 +527,44 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
   a.ldk = p.ldk;
   a.ldv = p.ldv;
   a.ht = shrink_heads<MH>(p.heads, p.H);
+  return a;
+}
+
+// Tiles of `rows` rows over rows of `row_bytes` bytes: fills in the tile
+// geometry of `a` and returns the grid, or -1 when the tile count or the grid
+// does not fit an int.
+template <int MH>
+long long set_tiles(const Problem& p, int rows, int row_bytes, BwdTileArgs<MH>& a) {
   const long long slabs = static_cast<long long>(p.B) * p.H;
-  a.tiles = (p.N + Geo<NQ>::kRows - 1) / Geo<NQ>::kRows;
+  a.tiles = (p.N + rows - 1) / rows;
   const long long work = slabs * a.tiles;
-  if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
+  if (work > 0x7fffffffll - kXcds) return -1;
   a.work = static_cast<int>(work);
-  const long long grid_ll =
-      tile_grid(slabs, a.tiles, 2ll * p.N * Geo<NQ>::kRowB, a.per_xcd, a.chunk);
-  if (grid_ll > 0x7fffffffll) return hipErrorInvalidValue;
+  const long long grid = tile_grid(slabs, a.tiles, 2ll * p.N * row_bytes, a.per_xcd, a.chunk);
+  return grid > 0x7fffffffll ? -1 : grid;
+}
+
+// The key pass on tiles (dK, dV), after a query pass has written D.
+template <int MH, int NQ, bool CLS>
+hipError_t launch_dkdv(const Problem& p, BwdTileArgs<MH> a, hipStream_t stream) {
+  const long long grid = set_tiles(p, Geo<NQ>::kRows, Geo<NQ>::kRowB, a);
+  if (grid < 0) return hipErrorInvalidValue;
+  if (p.strided)
+    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, true>), dim3(static_cast<unsigned>(grid)),
+           dim3(kTileThreads), 0, stream, a);
+  else
+    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, false>), dim3(static_cast<unsigned>(grid)),
+           dim3(kTileThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int MH, int NQ, bool CLS>
+hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                    float* ws, hipStream_t stream) {
+  BwdTileArgs<MH> a = make_args<MH>(p, q, k, v, lse, dout, dq, dk, dv, ws, Geo<NQ>::kD);
+  const long long grid_ll = set_tiles(p, Geo<NQ>::kRows, Geo<NQ>::kRowB, a);
+  if (grid_ll < 0) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   if (groups <= 4)
@@ -669,13 +575,7 @@ hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* 
     launch_dq<MH, 12, NQ, CLS>(a, p.strided, grid, stream);
   else
     launch_dq<MH, (kMaxSigned + 3) / 4, NQ, CLS>(a, p.strided, grid, stream);
-  if (p.strided)
-    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, true>), dim3(grid), dim3(kTileThreads),
-                       0, stream, a);
-  else
-    launch((bwd_dkdv_tile_kernel<MH, NQ, CLS, false>), dim3(grid),
-                       dim3(kTileThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_dkdv<MH, NQ, CLS>(p, a, stream);
 }
 
 template <int MH, int KG>
@@ -690,40 +590,16 @@ hipError_t launch_dq_win(const BwdTileArgs<MH>& a, bool strided, unsigned grid,
   return hipSuccess;
 }
 
-// The backward for d_h = 64 with the plain mask on the window kernels.
+// The backward for d_h = 64 with the plain mask: the query pass on the
+// window kernel, the key pass on tiles.  (A key pass on LDS windows of Q and
+// dO measured slower than the tile kernel: more L2 misses and HBM bytes.)
 template <int MH>
 hipError_t launch_win(const Problem& p, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
                       float* ws, hipStream_t stream) {
-  BwdTileArgs<MH> a;
-  a.q = static_cast<const char*>(q);
-  a.k = static_cast<const char*>(k);
-  a.v = static_cast<const char*>(v);
-  a.dout = static_cast<const char*>(dout);
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.ws = ws;
-  a.H = p.H;
-  a.N = p.N;
-  a.scale = 0.125f;  // 1 / sqrt(64)
-  a.c = kLog2e * a.scale;
-  a.lq = p.lq;
-  a.lk = p.lk;
-  a.lv = p.lv;
-  a.ldo = p.ldo;
-  a.ldq = p.ldq;
-  a.ldk = p.ldk;
-  a.ldv = p.ldv;
-  a.ht = shrink_heads<MH>(p.heads, p.H);
-  const long long slabs = static_cast<long long>(p.B) * p.H;
-  a.tiles = (p.N + win::kT - 1) / win::kT;
-  const long long work = slabs * a.tiles;
-  if (work > 0x7fffffffll - kXcds) return hipErrorInvalidValue;
-  a.work = static_cast<int>(work);
-  const long long grid_ll = tile_grid(slabs, a.tiles, 2ll * p.N * win::kRowB, a.per_xcd, a.chunk);
-  if (grid_ll > 0x7fffffffll) return hipErrorInvalidValue;
+  BwdTileArgs<MH> a = make_args<MH>(p, q, k, v, lse, dout, dq, dk, dv, ws, 64);
+  const long long grid_ll = set_tiles(p, win::kT, win::kRowB, a);
+  if (grid_ll < 0) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(grid_ll);
   const int groups = (max_signed(p) + 3) / 4;
   hipError_t e;
@@ -736,13 +612,7 @@ hipError_t launch_win(const Problem& p, const void* q, const void* k, const void
   else
     e = launch_dq_win<MH, (kMaxSigned + 3) / 4>(a, p.strided, grid, stream);
   if (e != hipSuccess) return e;
-  constexpr size_t kLds = 2 * win::kTensorBytes;
-  static const hipError_t attr_s = win::allow_lds(bwd_dkdv_win_kernel<MH, true>, kLds);
-  static const hipError_t attr_d = win::allow_lds(bwd_dkdv_win_kernel<MH, false>, kLds);
-  if ((p.strided ? attr_s : attr_d) != hipSuccess) return p.strided ? attr_s : attr_d;
-  launch(p.strided ? bwd_dkdv_win_kernel<MH, true> : bwd_dkdv_win_kernel<MH, false>, dim3(grid),
-         dim3(win::kThreads), kLds, stream, a);
-  return hipGetLastError();
+  return launch_dkdv<MH, 1, false>(p, a, stream);
 }
 
 }  // namespace

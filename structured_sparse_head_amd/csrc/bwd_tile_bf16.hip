@@ -20,7 +20,7 @@
 //    rows are read once for both the recomputed scores and the accumulation
 //    of dV += P dO and dK += dS Q.
 // With d_h = 64 and the plain mask (when the slab's byte offsets fit 32
-// bits) the query pass runs as bwd_dq_win_kernel: tiles of 128 rows with the
+// bits) the query pass runs as bwd_dq_win_kernel: tiles of 256 rows with the
 // K and V rows near the tile in an LDS window (window_bf16_common.h).
 // For d_h = 64 the accumulations over a group of four displacements use
 // v_dot2_f32_bf16 on pairs of them (axpy4_dot2: P and dS rounded to bf16,
@@ -344,10 +344,10 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dkdv_tile_kernel(BwdTileArgs
                 1.0f);
 }
 
-// d_h = 64 (plain mask, slab offsets within 32 bits): the same two kernels on
-// tiles of 128 rows with the gathered rows within win::kDn of the tile staged
-// in an LDS window (K and V for dq, Q and dO for dkdv; layout and lane order
-// in window_bf16_common.h), the far ones read through buffer loads.
+// d_h = 64 (plain mask, slab offsets within 32 bits): the query pass on tiles
+// of win::kT rows with the K and V rows within win::kDn of the tile staged in
+// an LDS window (layout and lane order in window_bf16_common.h), the far ones
+// read through buffer loads.
 template <int MH, int KG, bool STR>
 __global__ void __launch_bounds__(win::kThreads) __attribute__((amdgpu_waves_per_eu(win::kWavesPerSimd)))
 bwd_dq_win_kernel(BwdTileArgs<MH> a) {
@@ -419,6 +419,9 @@ bwd_dq_win_kernel(BwdTileArgs<MH> a) {
     }
   }
   __syncthreads();
+  // A wave whose rows all lie past the slab (the last tile) has no more work
+  // and no barrier follows.
+  if (t0 + 16 * __builtin_amdgcn_readfirstlane(tid >> 6) >= N) return;
   const int nd = __builtin_amdgcn_readfirstlane(s_nd);
   const int gn = __builtin_amdgcn_readfirstlane(s_gn);
   uint32_t qw[8], dw[8];

@@ -34,7 +34,7 @@
 //    dense class-token row kernel.
 //
 // d_h = 64 runs fwd_win_bf16_kernel instead (when the slab's byte offsets
-// fit 32 bits): tiles of 128 rows with the near K and V rows staged in an LDS
+// fit 32 bits): tiles of 256 rows with the near K and V rows staged in an LDS
 // window (window_bf16_common.h), far rows through buffer loads, the groups
 // walked in runtime loops and P V accumulated with v_dot2_f32_bf16 on pairs
 // of displacements.
@@ -215,10 +215,10 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     a.lse[static_cast<size_t>(slab) * N + rr] = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-// d_h = 64: the same two passes on tiles of 128 rows, with the K and V rows
-// within win::kDn of the tile staged in LDS (layout and rationale with
-// win::frag_off) and the far ones read through buffer loads whose offsets
-// take one add per row.  P V uses v_dot2_f32_bf16 on pairs of displacements
+// d_h = 64: the same two passes on tiles of win::kT rows, with the K and V rows
+// within win::kDn of the tile staged in LDS (layout and lane order in
+// window_bf16_common.h) and the far ones read through buffer loads whose
+// offsets take one add per row.  P V uses v_dot2_f32_bf16 on pairs of displacements
 // (axpy4_dot2).
 template <int MH, int KG, bool CLS, bool STR>
 __global__ void __launch_bounds__(win::kThreads) __attribute__((amdgpu_waves_per_eu(win::kWavesPerSimd)))
@@ -294,6 +294,9 @@ fwd_win_bf16_kernel(TileArgs<MH> a) {
     }
   }
   __syncthreads();
+  // A wave whose rows all lie past the slab (the last tile) has no more work
+  // and no barrier follows.
+  if (t0 + 16 * __builtin_amdgcn_readfirstlane(tid >> 6) >= N) return;
   const int nd = __builtin_amdgcn_readfirstlane(s_nd);
   const int gn = __builtin_amdgcn_readfirstlane(s_gn);  // near groups
   const int ng = (nd + 3) >> 2;                          // all groups

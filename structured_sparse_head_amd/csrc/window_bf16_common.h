@@ -6,13 +6,15 @@
 // near zero and sparse far away (1, 2, 3, 5, 8, ... for the first Wythoff
 // row).  Reading every (row, delta) fragment through the vector memory path
 // is bounded by its data return (64 bytes per clock per CU).  Here a
-// workgroup of 8 waves takes a tile of kT = 128 rows (one lane quad per row,
-// as in the tile kernels) and first stages in LDS the rows of the gathered
-// tensors (K and V, or Q and dO) within kDn of the tile: a window of
-// kR = kT + 2 kDn rows, row t0 - kDn + x at position x (128 bytes per
+// workgroup of 16 waves takes a tile of kT = 256 rows (one lane quad per
+// row, as in the tile kernels) and first stages in LDS the rows of the two
+// gathered tensors (K and V) within kDn = 152 of the tile: a window of
+// kR = kT + 2 kDn = 560 rows, row t0 - kDn + x at position x (128 bytes per
 // row).  Displacements with |delta| <= kDn then read the window and the
 // others global memory, so the near ones cost kR / kT row reads per tile row
-// and tensor instead of one per (row, delta).
+// and tensor instead of one per (row, delta).  (Measured against tiles of
+// 128 rows with windows of 88 rows either side, two workgroups per CU: 2-4%
+// faster at N = 1569 and 4097; a window of 184 rows was no faster.)
 //
 // Lane order.  Lane l (quad q = l / 4 holds a row, part p = l % 4) works on
 // 16-byte units p and p + 4 of its row (elements 8p .. 8p+7 and
@@ -33,16 +35,17 @@
 namespace fibatt {
 namespace win {
 
-constexpr int kThreads = 512;               // 8 waves
+constexpr int kThreads = 1024;              // 16 waves
 constexpr int kT = kThreads / 4;            // rows per tile
-constexpr int kDn = 88;                     // |delta| read from the window
-constexpr int kR = kT + 2 * kDn;            // window rows (304)
+constexpr int kDn = 152;                    // |delta| read from the window
+constexpr int kR = kT + 2 * kDn;            // window rows (560)
 constexpr int kRowB = 128;                  // bf16 row of 64 elements
-constexpr int kTensorBytes = kR * kRowB;    // one tensor's window (38,912 bytes)
+constexpr int kTensorBytes = kR * kRowB;    // one tensor's window (71,680 bytes)
 constexpr int kFill = (kR + kT - 1) / kT;   // window rows a thread stages
-// Two workgroups per CU (the window takes half of the LDS): 4 waves per SIMD,
-// which the register allocation is held to.
+// One workgroup per CU (two windows take 140 KiB of the 160 KiB LDS): 4 waves
+// per SIMD, which the register allocation is held to.
 constexpr int kWavesPerSimd = 4;
+static_assert(2 * kTensorBytes + 1024 <= 160 * 1024, "two windows and the lists fit the LDS");
 
 // Byte offsets within a row of lane l's fragments a and b.
 __device__ __forceinline__ int lane_unit_a(int lane) {

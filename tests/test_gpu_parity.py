@@ -605,14 +605,17 @@ TABLES = [
      True),
     ("fp32 N70 class token random sets", 2, 70, 128, torch.float32,
      [sorted(_rng_sets.choice(70, size=s, replace=False).tolist()) for s in (0, 3, 30)], True),
-    # The long-sequence d_h = 64 kernels read displacements |delta| <= 88
+    # The long-sequence d_h = 64 kernels read displacements |delta| <= 152
     # from an LDS window when all four of a group are that near: groups
     # entirely inside, straddling and outside the edge, far-only heads, and
-    # distances reaching both ends of the slab.
+    # distances reaching both ends of the slab; tiles are 256 rows, so
+    # N = 257 leaves one row in the last tile.
     ("bf16 N600 window edge", 2, 600, 64, torch.bfloat16,
-     [[1, 2, 87, 88], [88, 89, 90, 200], [0, 87, 88, 89, 300, 599], [89]], False),
+     [[1, 2, 151, 152], [152, 153, 154, 300], [0, 151, 152, 153, 400, 599], [153]], False),
     ("bf16 N600 window edge class token", 1, 600, 64, torch.bfloat16,
-     [[1, 2, 87, 88], [0, 87, 88, 89, 300, 599]], True),
+     [[1, 2, 151, 152], [0, 151, 152, 153, 400, 599]], True),
+    ("bf16 N257 one-row last tile", 2, 257, 64, torch.bfloat16,
+     [[1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233], [0, 256], [200]], False),
     ("bf16 N300 sliding windows 64 and 40", 1, 300, 64, torch.bfloat16,
      [list(range(1, 65)), list(range(0, 40))], False),
     ("bf16 N2100 far distances", 1, 2100, 64, torch.bfloat16,

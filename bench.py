@@ -18,7 +18,8 @@ Prints one JSON line:
     written; backward: Q, K, V, dO, O and LSE read, fp32 dQ, dK, dV written)
     and, as a second denominator, a hand-written HIP stream kernel that moves
     the same bytes with nothing else in it (fibatt_hbm_stream);
-  * workloads: the same per-pass figures for all five workloads, and, where
+  * workloads: the same per-pass figures for all five workloads, their
+    algorithmic flops per second over the 157.3 TFLOP/s vector-ALU peak, and, where
     the committed counters match the current sources, the L2-miss read rate
     (FETCH_SIZE / time) over the rate at which the XCDs' L2s can be filled
     from beyond them (fibatt_fabric_read, l2_fill_ref_gbps): the bound of
@@ -47,6 +48,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+VALU_PEAK_TFLOPS = 157.3  # MI355X vector fp32 (packed or dot2), published
+FLOPS_PER_PAIR_ELEM = {"fwd": 4, "bwd": 10}  # scope table: per pair and element of d_h
 MAX_POOL = 16           # worker processes for the CPU oracle (the host's share of cores)
 
 
@@ -773,6 +776,12 @@ def main():
             "fwd_traffic": measured_traffic(num, "fwd"),
             "bwd_traffic": measured_traffic(num, "bwd"),
         }
+        # Algorithmic flops (4 d_h per pair forward, 10 d_h backward) per
+        # second, over the vector-ALU peak: the other bound at long sequences.
+        for pname, rec in (("fwd", rf), ("bwd", rb)):
+            tf_s = FLOPS_PER_PAIR_ELEM[pname] * owl.d * opairs / (rec["median_us"] * 1e-6) / 1e12
+            entry[f"{pname}_tflops"] = tf_s
+            entry[f"{pname}_valu_frac"] = tf_s / VALU_PEAK_TFLOPS
         # L2-miss reads (FETCH_SIZE from the committed counters, current
         # sources only) per second, over the rate the L2s can be filled.
         for pname, rec in (("fwd", rf), ("bwd", rb)):

@@ -160,6 +160,73 @@ __global__ void __launch_bounds__(kTileThreads) bwd_dq_tile_kernel(BwdTileArgs<M
   frag_words(df, dw);
   const float lse2 = lse_r * kLog2e;
 
+  if constexpr (NQ == 2) {
+    // d_h = 128: one pass.  With A = sum_k P dP K and S = sum_k P K over the
+    // row's keys, dQ sqrt(d) = sum_k P (dP - D) K = A - D S, and
+    // D = sum_k P dP is complete at the end, so every K row is read once (a
+    // second pass re-read each one, which at long sequences misses L2
+    // again).  The coefficients stay fp32.
+    float acc_a[16], acc_s[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc_a[e] = 0.f;
+      acc_s[e] = 0.f;
+    }
+    float dl = 0.f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      if (4 * g < nd) {
+        int d[4];
+        group_deltas(s_deltas, g, d);
+        u32x4 kf[4][2], vf[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t r = static_cast<size_t>(clamp_row(rr + d[j], N));
+          load_row_q(kbase + r * rk, kf[j]);
+          load_row_q(vbase + r * rv, vf[j]);
+        }
+        float ps[4], pp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ps[j] = dot_part(qw, kf[j]);
+          pp[j] = dot_part(dw, vf[j]);
+        }
+        const float sc = halves_sum<NQ>(reduce4q(ps, b0, b1));
+        const float dp = halves_sum<NQ>(reduce4q(pp, b0, b1));
+        const int kk = rr + s_deltas[4 * g + part];
+        const bool ok = 4 * g + part < nd && static_cast<unsigned>(kk) < static_cast<unsigned>(N);
+        const float p = ok ? fast_exp2(__builtin_fmaf(sc, a.c, -lse2)) : 0.f;
+        dl = __builtin_fmaf(p, dp, dl);
+        float pg[4], pdg[4];
+        gather4q(p, pg);  // 0 in padded slots
+        gather4q(p * dp, pdg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) axpy2_bf16(acc_a, pdg[j], acc_s, pg[j], kf[j]);
+      }
+    }
+    float dd = quad_sum4(dl);  // both halves of a row hold the same P, dP
+    float pq = 0.f, dpq = 0.f;
+    u32x4 k0f[2];
+    if constexpr (CLS) {
+      u32x4 v0f[2];
+      load_row_q(kbase, k0f);
+      load_row_q(vbase, v0f);
+      const float s = halves_sum<NQ>(quad_sum4(dot_part(qw, k0f)));
+      dpq = halves_sum<NQ>(quad_sum4(dot_part(dw, v0f)));
+      pq = (rr >= 1 && !has_delta(s_deltas, nd, rr)) ? fast_exp2(__builtin_fmaf(s, a.c, -lse2))
+                                                    : 0.f;
+      dd = rr == 0 ? a.ws[rbase] : __builtin_fmaf(pq, dpq, dd);  // row 0: the dense D_0
+    }
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(-dd, acc_s[e], acc_a[e]);
+    if constexpr (CLS) axpy_bf16(acc, pq * (dpq - dd), k0f);
+    store_row_f32(tile_row_f32<STR, G::kD>(a.dq, a.ldq, slab, a.H, N, rr) + 64 * half, part, acc,
+                  a.scale);
+    if (part == 0 && half == 0) a.ws[rbase + rr] = dd;
+    return;
+  }
+
   // Pass 1: P and dP, one pair per lane and group; D = sum P dP.
   float pw[KG], dpw[KG];
   float dl = 0.f;

@@ -100,6 +100,21 @@ __device__ __forceinline__ void axpy_bf16(float (&acc)[16], float p, const u32x4
   }
 }
 
+// acc_a += pa * x and acc_b += pb * x for this lane's 16 bf16 elements
+// (each widened to fp32 once).
+__device__ __forceinline__ void axpy2_bf16(float (&acc_a)[16], float pa, float (&acc_b)[16],
+                                           float pb, const u32x4 (&x)[2]) {
+  const uint32_t w[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float lo = __uint_as_float(w[u] << 16), hi = __uint_as_float(w[u] & 0xffff0000u);
+    acc_a[2 * u] = __builtin_fmaf(pa, lo, acc_a[2 * u]);
+    acc_a[2 * u + 1] = __builtin_fmaf(pa, hi, acc_a[2 * u + 1]);
+    acc_b[2 * u] = __builtin_fmaf(pb, lo, acc_b[2 * u]);
+    acc_b[2 * u + 1] = __builtin_fmaf(pb, hi, acc_b[2 * u + 1]);
+  }
+}
+
 // Two fp32 values rounded to bf16 (nearest even) and packed, x in the low
 // half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {

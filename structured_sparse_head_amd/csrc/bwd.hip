@@ -214,8 +214,7 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
     frag_load_cached<T, D, G>(rq.row(j0), part, qf0);
     frag_load_cached<T, D, G>(rdo.row(j0), part, dof0);
   }
-  stage_rows_lds<T, D, NT, false>(lds_a, rk.base, rk.rs, N, tid);
-  stage_rows_lds<T, D, NT, false>(lds_b, rv.base, rv.rs, N, tid);
+  stage2_rows_lds<T, D, NT, false>(lds_a, rk.base, rk.rs, lds_b, rv.base, rv.rs, N, tid);
   __syncthreads();
   const int nd = s_nd;
 
@@ -267,8 +266,7 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
   __syncthreads();
 
   // Key-centric pass: Q and dO replace K and V in LDS.
-  stage_rows_lds<T, D, NT, true>(lds_a, rq.base, rq.rs, N, tid);
-  stage_rows_lds<T, D, NT, true>(lds_b, rdo.base, rdo.rs, N, tid);
+  stage2_rows_lds<T, D, NT, true>(lds_a, rq.base, rq.rs, lds_b, rdo.base, rdo.rs, N, tid);
   __syncthreads();
   for (int kr = k0; kr < N; kr += NT / G) {
     if (CLS && kr == 0) continue;

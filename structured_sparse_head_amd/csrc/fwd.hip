@@ -45,6 +45,8 @@ struct FwdArgs {
 
 template <typename T, int D, int G>
 struct LdsKV {
+  // Rows come from LDS: reads are unconditional and pipelined (attend_row).
+  static constexpr bool kPipelined = true;
   const char* k;
   const char* v;
   __device__ void load_k(int r, int part, uint32_t (&f)[Geom<T, D, G>::kWPL]) const {
@@ -57,6 +59,10 @@ struct LdsKV {
 
 template <typename T, int D, int G>
 struct GlobalKV {
+  // Rows come from L2/HBM: only keys in range are read, and latency is left
+  // to the other waves (a second register set costs more occupancy than it
+  // saves, measured on long fp32 sequences).
+  static constexpr bool kPipelined = false;
   const char* k;  // slab base
   const char* v;
   size_t rsk, rsv;  // row strides, bytes
@@ -76,43 +82,89 @@ __device__ __forceinline__ void attend_row(const KV& kv, int j, int N, int part,
                                            float (&acc)[Geom<T, D, G>::kDL], float& m, float& l) {
   using Gm = Geom<T, D, G>;
   using M = FragMath<T, Gm::kWPL>;
-  for (int i0 = 0; i0 < nd; i0 += C) {
-    float s[C];
-    int key[C];
+  if constexpr (KV::kPipelined) {
+    for (int i0 = 0; i0 < nd; i0 += C) {
+      // Keys out of range (or past the list) read row j itself and are
+      // masked: every read is unconditional, so the compiler can have several
+      // in flight instead of waiting out each one under its own lane mask.
+      // The chunk's distances are read first (one wait), then its keys.
+      float s[C];
+      int key[C];
+      bool in[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int i = i0 + c;
-      const int kk = j + deltas[i < nd ? i : 0];
-      const bool ok = (i < nd) && (kk >= 0) && (kk < N);
-      key[c] = ok ? kk : -1;
-      float sc = -INFINITY;
-      if (ok) {
-        uint32_t kf[Gm::kWPL];
-        kv.load_k(kk, part, kf);
-        sc = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+      for (int c = 0; c < C; ++c) {
+        const int i = i0 + c;
+        const int kk = j + deltas[i < nd ? i : 0];
+        in[c] = (i < nd) && (kk >= 0) && (kk < N);
+        key[c] = in[c] ? kk : j;
       }
-      s[c] = sc;
-    }
-    float mc = s[0];
+      uint32_t kf[2][Gm::kWPL];  // key c + 1 is read while key c is scored
+      kv.load_k(key[0], part, kf[0]);
 #pragma unroll
-    for (int c = 1; c < C; ++c) mc = fmaxf(mc, s[c]);
-    const float mn = fmaxf(m, mc);
-    if (mn == -INFINITY) continue;  // nothing in range yet
-    const float alpha = fast_exp2(m - mn);  // 0 when m = -inf
-    l *= alpha;
+      for (int c = 0; c < C; ++c) {
+        if (c + 1 < C) kv.load_k(key[c + 1], part, kf[(c + 1) & 1]);
+        const float sc = group_sum<G>(M::dot(qf, kf[c & 1])) * scale_log2;
+        s[c] = in[c] ? sc : -INFINITY;
+      }
+      float mc = s[0];
 #pragma unroll
-    for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
+      for (int c = 1; c < C; ++c) mc = fmaxf(mc, s[c]);
+      const float mn = fmaxf(m, mc);
+      if (mn == -INFINITY) continue;  // nothing in range yet
+      const float alpha = fast_exp2(m - mn);  // 0 when m = -inf
+      l *= alpha;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      if (key[c] >= 0) {
-        const float p = fast_exp2(s[c] - mn);
+      for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
+      uint32_t vf[2][Gm::kWPL];
+      kv.load_v(key[0], part, vf[0]);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (c + 1 < C) kv.load_v(key[c + 1], part, vf[(c + 1) & 1]);
+        const float p = fast_exp2(s[c] - mn);  // 0 for a masked key
         l += p;
-        uint32_t vf[Gm::kWPL];
-        kv.load_v(key[c], part, vf);
-        M::axpy(acc, p, vf);
+        M::axpy(acc, p, vf[c & 1]);
       }
+      m = mn;
     }
-    m = mn;
+  } else {
+    for (int i0 = 0; i0 < nd; i0 += C) {
+      float s[C];
+      int key[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int i = i0 + c;
+        const int kk = j + deltas[i < nd ? i : 0];
+        const bool ok = (i < nd) && (kk >= 0) && (kk < N);
+        key[c] = ok ? kk : -1;
+        float sc = -INFINITY;
+        if (ok) {
+          uint32_t kf[Gm::kWPL];
+          kv.load_k(kk, part, kf);
+          sc = group_sum<G>(M::dot(qf, kf)) * scale_log2;
+        }
+        s[c] = sc;
+      }
+      float mc = s[0];
+#pragma unroll
+      for (int c = 1; c < C; ++c) mc = fmaxf(mc, s[c]);
+      const float mn = fmaxf(m, mc);
+      if (mn == -INFINITY) continue;  // nothing in range yet
+      const float alpha = fast_exp2(m - mn);  // 0 when m = -inf
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < Gm::kDL; ++t) acc[t] *= alpha;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (key[c] >= 0) {
+          const float p = fast_exp2(s[c] - mn);
+          l += p;
+          uint32_t vf[Gm::kWPL];
+          kv.load_v(key[c], part, vf);
+          M::axpy(acc, p, vf);
+        }
+      }
+      m = mn;
+    }
   }
 }
 
@@ -187,18 +239,17 @@ __global__ void __launch_bounds__(NT) fwd_slab_kernel(FwdArgs<MH> a) {
   constexpr int es = static_cast<int>(sizeof(T));
   char* lds_k = smem;
   char* lds_v = smem + N * Gm::kRowBytes;
-  stage_rows_lds<T, D, NT, true>(lds_k, a.k + a.lk.slab_bytes(slab, a.H, es), a.lk.row_bytes(es),
-                                 N, tid);
-  stage_rows_lds<T, D, NT, true>(lds_v, a.v + a.lv.slab_bytes(slab, a.H, es), a.lv.row_bytes(es),
-                                 N, tid);
   const char* qbase = a.q + a.lq.slab_bytes(slab, a.H, es);
   const size_t rsq = a.lq.row_bytes(es);
   const int part = tid % G;
-  // The first row's Q is requested before the staging barrier, so its
-  // latency overlaps it.
+  // The first row's Q is requested before K and V are staged, so its
+  // latency overlaps the staging.
   const int j0 = tid / G;
   uint32_t qf0[Gm::kWPL];
   if (j0 < N) frag_load_global<T, D, G>(qbase + static_cast<size_t>(j0) * rsq, part, qf0);
+  stage2_rows_lds<T, D, NT, true>(lds_k, a.k + a.lk.slab_bytes(slab, a.H, es), a.lk.row_bytes(es),
+                                  lds_v, a.v + a.lv.slab_bytes(slab, a.H, es), a.lv.row_bytes(es),
+                                  N, tid);
   __syncthreads();
   const int nd = s_nd;
   const LdsKV<T, D, G> kv{lds_k, lds_v};

@@ -108,27 +108,52 @@ __device__ __forceinline__ void frag_store_lds(char* base, int r, int part,
   }
 }
 
-// Copy `rows` rows of D elements, `rs` bytes apart in global memory, into
-// LDS in the swizzled layout.  Consecutive threads move consecutive 16-byte
-// chunks, so the global reads are coalesced within each row.
+// Copy `rows` rows of D elements of two tensors (a and b, rows `rs_a` and
+// `rs_b` bytes apart in global memory) into LDS in the swizzled layout.
+// Consecutive threads move consecutive 16-byte chunks, so the global reads
+// are coalesced within each row.  Each thread requests up to kStageBatch
+// chunks of both tensors before it writes any of them: one load followed by
+// its LDS write per step would wait out a full memory round trip per chunk.
 // kLastUse marks the final read of the data: those loads are issued
 // non-temporal so they do not displace lines that will be read again.
+constexpr int kStageBatch = 4;
+
 template <typename T, int D, int NT, bool kLastUse>
-__device__ __forceinline__ void stage_rows_lds(char* lds, const char* src, size_t rs, int rows,
-                                               int tid) {
+__device__ __forceinline__ void stage2_rows_lds(char* lds_a, const char* src_a, size_t rs_a,
+                                                char* lds_b, const char* src_b, size_t rs_b,
+                                                int rows, int tid) {
   using Gm = Geom<T, D, 1>;
   const int total = rows * Gm::kCPR;
-  for (int idx = tid; idx < total; idx += NT) {
-    const int r = idx / Gm::kCPR;
-    const int c = idx % Gm::kCPR;
-    const u32x4* s = reinterpret_cast<const u32x4*>(src + r * rs) + c;
-    u32x4 x;
-    if constexpr (kLastUse) {
-      x = __builtin_nontemporal_load(s);
-    } else {
-      x = *s;
+  for (int base = tid; base < total; base += kStageBatch * NT) {
+    u32x4 xa[kStageBatch], xb[kStageBatch];
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      const int idx = base + i * NT;
+      if (idx < total) {
+        const int r = idx / Gm::kCPR;
+        const int c = idx % Gm::kCPR;
+        const u32x4* sa = reinterpret_cast<const u32x4*>(src_a + r * rs_a) + c;
+        const u32x4* sb = reinterpret_cast<const u32x4*>(src_b + r * rs_b) + c;
+        if constexpr (kLastUse) {
+          xa[i] = __builtin_nontemporal_load(sa);
+          xb[i] = __builtin_nontemporal_load(sb);
+        } else {
+          xa[i] = *sa;
+          xb[i] = *sb;
+        }
+      }
     }
-    *reinterpret_cast<u32x4*>(lds + r * Gm::kRowBytes + lds_chunk<Gm::kCPR>(r, c) * 16) = x;
+#pragma unroll
+    for (int i = 0; i < kStageBatch; ++i) {
+      const int idx = base + i * NT;
+      if (idx < total) {
+        const int r = idx / Gm::kCPR;
+        const int c = idx % Gm::kCPR;
+        const int off = r * Gm::kRowBytes + lds_chunk<Gm::kCPR>(r, c) * 16;
+        *reinterpret_cast<u32x4*>(lds_a + off) = xa[i];
+        *reinterpret_cast<u32x4*>(lds_b + off) = xb[i];
+      }
+    }
   }
 }
 

@@ -427,9 +427,10 @@ struct ClsLds {
 // Row 0 of the class-token mask for one slab, by one wave during the query
 // passes (same slots and parts as dense_col0): D_0 = sum_k P_0k dP_0k over
 // all keys, keeping each key's (P_0k, dP_0k) in LDS, then dQ_0 =
-// sum_k dS_0k K_k / sqrt(d) in a second sweep that also writes row 0's table
-// entries (P, dS / sqrt(d)) for the keys at head distances, the diagonal and
-// colv[0], and finally D_0 for the key passes.
+// sum_k dS_0k K_k / sqrt(d) in a second sweep; then row 0's table entries
+// (P, dS / sqrt(d)) for the keys at head distances (one lane per distance:
+// looking each key's distance up in the sweep cost a loop per key), the
+// diagonal and colv[0], and finally D_0 for the key passes.
 template <typename A>
 __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane, char* smem) {
   const char* lds_k = smem;
@@ -483,15 +484,19 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
     u32x4 kf[4];
     load_f32_q(lds_kf + part * 64, clamp_row(k, N), kf);
     axpy_q(acc, ds, kf);
-    if (part == 0 && k < N) {  // one lane of the slot's four
-      const float2 e = make_float2(pp.x, ds * a.scale);
-      const int i = k >= 1 ? dist.index(k, npos) : -1;
-      if (i >= 0) tbl[i] = e;  // query 0, displacement +k: table row 0, column i
-      if (k == 0) {
-        cl.colv[0] = e;
-        if (has0) tbl[2 * kMaxPos] = e;
-      }
-    }
+  }
+  // Row 0's table entries (P, dS / sqrt(d)): lane i takes head distance i
+  // (query 0, displacement +f_i: table row 0, column i); lane 12 the
+  // diagonal and colv[0].  The same values the sweep above used.
+  if (lane < npos) {
+    const int k = dist.at(lane);
+    const float2 pp = cl.ppd[k];
+    tbl[lane] = make_float2(pp.x, pp.x * (pp.y - d0) * a.scale);
+  } else if (lane == kMaxPos) {
+    const float2 pp = cl.ppd[0];
+    const float2 e = make_float2(pp.x, pp.x * (pp.y - d0) * a.scale);
+    cl.colv[0] = e;
+    if (has0) tbl[2 * kMaxPos] = e;
   }
   constexpr int kSpan[4] = {1, 2, 12, 20};
 #pragma unroll
@@ -541,13 +546,13 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH, STR> 
       commit_kv(smem, smem + N * kBf16Stride, smem + 2 * N * kBf16Stride, N, tid, pf);
       __syncthreads();
       const int next = slab + gridDim.x;
-      // (Row 0 before this wave's share of the next slab's loads, so the
-      // prefetch registers are free while it runs.)
-      // (Row 0 before this wave's share of the next slab's loads, so the
-      // prefetch registers are free while it runs.)
+      // Row 0 runs before this wave's share of the next slab's loads, so the
+      // prefetch registers are free while it runs.  Those loads are not
+      // waited for here: the next slab's commit does that, and waiting now
+      // (a full memory round trip after row 0) held the workgroup at the
+      // next barrier.
       if (roww) dense_row0(a, slab, N, lane, smem);
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
-      settle(pf);
       __syncthreads();
       __syncthreads();
       if (colw) dense_col0(a, slab, N, lane, smem);

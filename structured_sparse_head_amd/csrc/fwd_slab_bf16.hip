@@ -226,21 +226,26 @@ __device__ __forceinline__ void accumulate_dir(const RowSpan& vs, Dist dist, int
   }
 }
 
-// Dense class-token row for one slab, by one wave: slot l % 16 of the lane
-// takes keys slot, slot + 16, ... (N <= 240: at most 15 each) with an online
-// softmax, with the same lane parts as a row block.  The slots are then
-// combined: a common maximum over the 16 slots (lane bits 0..3), the sums
-// rescaled to it, and a lane's P V fragment summed over the 16 lanes that
-// hold the same part, which are l ^ x for x in the span of 1, 2, 12 and 20
-// (flipping bits 2 and 3 together, or bits 2 and 4, keeps the part).
+// Dense class-token row for one slab (N <= 240), split over up to
+// kDenseWaves of the waves without rows: wave i of n takes the key slots
+// t = i, i + n, ... (slot l % 16 of the lane takes keys slot + 16 t) with an
+// online softmax, with the same lane parts as a row block.  The wave's slots
+// are then combined: a common maximum over the 16 slots (lane bits 0..3),
+// the sums rescaled to it, and a lane's P V fragment summed over the 16 lanes
+// that hold the same part, which are l ^ x for x in the span of 1, 2, 12 and
+// 20 (flipping bits 2 and 3 together, or bits 2 and 4, keeps the part).  The
+// wave leaves (max, sum, P V) in LDS; after a barrier the first wave merges
+// the parts in order and stores row 0 (one wave alone took longer than the
+// rows of the other waves).
 constexpr int kDenseSlots = 15;
+constexpr int kDenseWaves = 3;
+constexpr int kDensePart = 2 + 64;  // max, sum, P V row (parts in lane order)
 
 __device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
-template <typename A>
-__device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane,
+__device__ __forceinline__ void dense_part(const float scale_log2, int N, int lane, int wi, int nw,
                                            const char* lds_k, const char* lds_v,
-                                           const char* lds_q, const Prefetch& pf) {
+                                           const char* lds_q, float* out) {
   const int slot = lane & 15;
   const int part = lane_part(lane);
   uint32_t qw[8];
@@ -250,13 +255,13 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
     qw[0] = qf[0].x; qw[1] = qf[0].y; qw[2] = qf[0].z; qw[3] = qf[0].w;
     qw[4] = qf[1].x; qw[5] = qf[1].y; qw[6] = qf[1].z; qw[7] = qf[1].w;
   }
-  const float c = a.scale_log2;
+  const float c = scale_log2;
   float m = -INFINITY, l = 0.f;
   float o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
 #pragma unroll 1
-  for (int t = 0; t < kDenseSlots; ++t) {  // uniform trip count; keys past N score -inf
+  for (int t = wi; t < kDenseSlots; t += nw) {  // uniform trip count; keys past N score -inf
     const int k = slot + 16 * t;
     const int kc = clamp_row(k, N);
     u32x4 kf[2];
@@ -264,8 +269,8 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
     const float x = dot_q(qw, kf);
     const float sk = k < N ? x : -INFINITY;
     const float mn = fmaxf(m, sk);
-    // A slot with no key yet (N < 16) keeps m = -inf: both exponentials
-    // would see -inf - (-inf), so they are chosen explicitly.
+    // A slot with no key yet keeps m = -inf: both exponentials would see
+    // -inf - (-inf), so they are chosen explicitly.
     const float alpha = mn == -INFINITY ? 1.f : fast_exp2((m - mn) * c);
     const float p = mn == -INFINITY ? 0.f : fast_exp2((sk - mn) * c);  // 0 for sk = -inf
     u32x4 vf[4];
@@ -278,7 +283,7 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
   }
   float mw = m;
 #pragma unroll
-  for (int x = 1; x < 16; x <<= 1) mw = fmaxf(mw, wave_xor(mw, x));  // key 0 exists: finite
+  for (int x = 1; x < 16; x <<= 1) mw = fmaxf(mw, wave_xor(mw, x));  // -inf if no key here
   const float sc = m == -INFINITY ? 0.f : fast_exp2((m - mw) * c);
   l *= sc;
 #pragma unroll
@@ -290,6 +295,37 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] += wave_xor(o[e], kSpan[i]);
+  if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[2 + 16 * part + e] = o[e];
+    if (lane == 0) {
+      out[0] = mw;
+      out[1] = l;
+    }
+  }
+}
+
+// Merges the nw parts of the dense row in order and stores row 0 and its
+// LSE (lanes of slot 0; key 0 is in part 0, so the maximum is finite).
+template <typename A>
+__device__ __forceinline__ void dense_store(const A& a, int slab, int N, int lane, int nw,
+                                            const float* parts, const Prefetch& pf) {
+  const int slot = lane & 15;
+  const int part = lane_part(lane);
+  const float c = a.scale_log2;
+  float mm = parts[0];
+  for (int i = 1; i < nw; ++i) mm = fmaxf(mm, parts[i * kDensePart]);
+  float l = 0.f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    const float* pi = parts + i * kDensePart;
+    const float w = pi[0] == -INFINITY ? 0.f : fast_exp2((pi[0] - mm) * c);
+    l = __builtin_fmaf(pi[1], w, l);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(pi[2 + 16 * part + e], w, o[e]);
+  }
   const float inv = 1.0f / l;
   uint32_t w[8];
 #pragma unroll
@@ -300,11 +336,11 @@ __device__ __forceinline__ void dense_row0(const A& a, int slab, int N, int lane
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
   settle(pf);
-  if (slot == 0) {  // lanes 0, 16, 32, 48: parts 0..3 of the row
+  if (slot == 0) {
     u32x4* orow = reinterpret_cast<u32x4*>(const_cast<char*>(slab_row(a, a.o, a.lo, slab, N, 0)));
     orow[part] = u32x4{w[0], w[1], w[2], w[3]};
     orow[part + 4] = u32x4{w[4], w[5], w[6], w[7]};
-    if (lane == 0) a.lse[static_cast<size_t>(slab) * N] = (mw * c + fast_log2(l)) * kLn2;
+    if (lane == 0) a.lse[static_cast<size_t>(slab) * N] = (mm * c + fast_log2(l)) * kLn2;
   }
 }
 
@@ -417,10 +453,14 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
 template <int MH, bool CLS, bool STR>
 __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH, STR> a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ float s_dense[CLS ? kDenseWaves * kDensePart : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int r0 = 16 * static_cast<int>((a.blocks >> (4 * wave)) & 15u);
+  // With the class-token mask and N <= 240 the waves without rows compute
+  // the dense row 0, one more barrier per slab merging their parts.
+  const bool dense_on = CLS && a.N <= 16 * kDenseSlots;
   const int row0 = r0 + (lane & 15);
   const int part0 = lane_part(lane);
   const int slot0 = quad_slot(lane);
@@ -452,10 +492,14 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH, STR> 
       const int next = slab + gridDim.x;
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row, part, next >= a.slabs, pf);
       attend_slab<CLS>(a, slab, N, row, part, slot, r0, lds_k, lds_v, lds_q, pf);
+      if (dense_on) __syncthreads();  // the dense row's parts are in LDS
     }
   } else {
-    // The first wave without rows computes the class-token row (N <= 240).
-    const bool dense = CLS && r0 == 16 * ((a.N + 15) / 16);
+    // The first waves without rows compute the class-token row (N <= 240).
+    const int first = (a.N + 15) / 16;  // row block of the first wave without rows
+    const int nw = 16 - first < kDenseWaves ? 16 - first : kDenseWaves;
+    const int wi = r0 / 16 - first;      // this wave's index among them
+    const bool dense = dense_on && wi < nw;
     for (; slab < a.slabs; slab += gridDim.x) {
       int N = a.N;
       asm volatile("" : "+s"(N));
@@ -466,8 +510,12 @@ __global__ void __launch_bounds__(kThreadsF) fwd_slab_bf16_kernel(Args<MH, STR> 
       const int next = slab + gridDim.x;
       issue_prefetch(a, N, next < a.slabs ? next : slab, tid, row0, part0, next >= a.slabs, pf);
       if (dense)
-        dense_row0(a, slab, N, lane, smem, smem + N * kBf16Stride,
-                   smem + N * (kBf16Stride + kF32Stride), pf);
+        dense_part(a.scale_log2, N, lane, wi, nw, smem, smem + N * kBf16Stride,
+                   smem + N * (kBf16Stride + kF32Stride), s_dense + wi * kDensePart);
+      if (dense_on) {
+        __syncthreads();
+        if (dense && wi == 0) dense_store(a, slab, N, lane, nw, s_dense, pf);
+      }
     }
   }
 }

@@ -326,14 +326,11 @@ __device__ __forceinline__ void dense_store(const A& a, int slab, int N, int lan
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(pi[2 + 16 * part + e], w, o[e]);
   }
-  const float inv = 1.0f / l;
+  const float inv = __builtin_amdgcn_rcpf(l);
   uint32_t w[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
-    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
-    w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    w[u] = pack_bf16x2(o[2 * u] * inv, o[2 * u + 1] * inv);
   }
   settle(pf);
   if (slot == 0) {
@@ -427,14 +424,11 @@ __device__ __forceinline__ void attend_slab(const A& a, int slab, int N, int row
     l += p;
     axpy_q(o, p, vf);
   }
-  const float inv = any ? 1.0f / l : 0.f;
+  const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
   uint32_t w[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
-    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
-    w[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    w[u] = pack_bf16x2(o[2 * u] * inv, o[2 * u + 1] * inv);
   }
   const float lse = any ? (mc + fast_log2(l)) * kLn2 : -INFINITY;
   // The next slab's loads complete before any store of this slab, so the

@@ -198,14 +198,11 @@ __global__ void __launch_bounds__(kTileThreads) fwd_tile_bf16_kernel(TileArgs<MH
     l += p;
     axpy_bf16(o, p, v0f);
   }
-  const float inv = any ? 1.0f / l : 0.f;
+  const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
   uint32_t ow[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const __bf16 lo = static_cast<__bf16>(o[2 * u] * inv);
-    const __bf16 hi = static_cast<__bf16>(o[2 * u + 1] * inv);
-    ow[u] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    ow[u] = pack_bf16x2(o[2 * u] * inv, o[2 * u + 1] * inv);
   }
   char* orow = (STR ? a.o + a.lo.slab_bytes(slab, a.H, 2) + rr * a.lo.row_bytes(2)
                     : a.o + base + static_cast<size_t>(rr) * kRowB) + lofs;
@@ -418,7 +415,7 @@ fwd_win_bf16_kernel(TileArgs<MH> a) {
     l += p;
     axpy_bf16(o, p, v0f);
   }
-  const float inv = any ? 1.0f / l : 0.f;
+  const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
   uint32_t ow[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) ow[u] = pack_bf16x2(o[2 * u] * inv, o[2 * u + 1] * inv);

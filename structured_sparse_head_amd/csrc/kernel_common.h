@@ -248,6 +248,15 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Two fp32 values rounded to bf16 (nearest even) and packed, x in the low
+// half: one v_cvt_pk_bf16_f32 (two scalar conversions would take four
+// instructions with the shift and the or).
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cvt){x, y}, bf16x2_cvt));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

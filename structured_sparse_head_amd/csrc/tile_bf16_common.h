@@ -115,13 +115,6 @@ __device__ __forceinline__ void axpy2_bf16(float (&acc_a)[16], float pa, float (
   }
 }
 
-// Two fp32 values rounded to bf16 (nearest even) and packed, x in the low
-// half.
-__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y))) << 16);
-}
-
 // acc += sum_j c_j x_j over a group of four bf16 fragments x_j (this lane's
 // 16 elements each), with the coefficients packed as bf16 pairs c01 = (c_0,
 // c_1) and c23 = (c_2, c_3).  Element e of two fragments is interleaved

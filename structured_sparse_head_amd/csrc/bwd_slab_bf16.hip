@@ -135,15 +135,42 @@ __device__ __forceinline__ void store_f32_q_lds(char* base, int r, int part,
               w[2 * t + 1] & 0xffff0000u};
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
+// A lane's 16 elements of its Q (and dO) row are the 4-element groups
+// part, part + 4, part + 8 and part + 12 (8 bytes each, 32 bytes apart).  The
+// lanes of parts 2u and 2u + 1 (lanes l and l ^ 16) need, together, the
+// 16-byte chunks u, u + 2, u + 4 and u + 6 of the row: the even part loads
+// chunks u and u + 4, the odd one u + 2 and u + 6, so that each load
+// instruction reads 64 contiguous bytes of every row (half the memory
+// requests of 8-byte pieces), and the two exchange the halves the other
+// needs (rows_of_chunks).
 struct Prefetch {
   u32x4 k[kChunksB];
   u32x4 v[kChunksB];
-  u32x2 q[4];     // this lane's element groups of its Q row, 8 bytes each
-  u32x2 dout[4];
+  u32x4 qa, qb;  // chunks c0 and c0 + 4 of the Q row, c0 = part / 2 + 2 (part % 2)
+  u32x4 da, db;  // the same chunks of the dO row
   float lse;
 };
+
+// This lane's groups part + 4 m (m = 0..3) as 8 words (group m in words
+// 2 m, 2 m + 1) from its chunks a, b and its partner's (lane ^ 16).
+__device__ __forceinline__ void rows_of_chunks(const u32x4& a, const u32x4& b, int part,
+                                               uint32_t (&w)[8]) {
+  const bool odd = (part & 1) != 0;
+  // The even part sends the high halves of its chunks (groups 2u + 1 and
+  // 2u + 9), the odd part the low halves (groups 2u + 4 and 2u + 12).
+  const uint32_t o0 = odd ? a.x : a.z, o1 = odd ? a.y : a.w;
+  const uint32_t o2 = odd ? b.x : b.z, o3 = odd ? b.y : b.w;
+  const uint32_t i0 = __shfl_xor(o0, 16, 64), i1 = __shfl_xor(o1, 16, 64);
+  const uint32_t i2 = __shfl_xor(o2, 16, 64), i3 = __shfl_xor(o3, 16, 64);
+  w[0] = odd ? i0 : a.x;  // group part
+  w[1] = odd ? i1 : a.y;
+  w[2] = odd ? a.z : i0;  // group part + 4
+  w[3] = odd ? a.w : i1;
+  w[4] = odd ? i2 : b.x;  // group part + 8
+  w[5] = odd ? i3 : b.y;
+  w[6] = odd ? b.z : i2;  // group part + 12
+  w[7] = odd ? b.w : i3;
+}
 
 // Loads are unconditional (indices clamped into the slab) so every prefetch
 // register is overwritten each time; only the LDS commit is masked.  With
@@ -185,13 +212,13 @@ __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, i
     qr = a.q + off;
     dr = a.dout + off;
   }
-  const u32x2* qs = reinterpret_cast<const u32x2*>(qr + part * 8);
-  const u32x2* ds = reinterpret_cast<const u32x2*>(dr + part * 8);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {  // group part + 4 m sits at byte 8 part + 32 m
-    pf.q[m] = __builtin_nontemporal_load(qs + 4 * m);
-    pf.dout[m] = __builtin_nontemporal_load(ds + 4 * m);
-  }
+  const int c0 = (part >> 1) + 2 * (part & 1);
+  const u32x4* qs = reinterpret_cast<const u32x4*>(qr) + c0;
+  const u32x4* ds = reinterpret_cast<const u32x4*>(dr) + c0;
+  pf.qa = __builtin_nontemporal_load(qs);
+  pf.qb = __builtin_nontemporal_load(qs + 4);
+  pf.da = __builtin_nontemporal_load(ds);
+  pf.db = __builtin_nontemporal_load(ds + 4);
   pf.lse = __builtin_nontemporal_load(a.lse + slab * static_cast<size_t>(N) + r);
 }
 
@@ -199,8 +226,7 @@ __device__ __forceinline__ void issue_prefetch(const A& a, int N, size_t slab, i
 __device__ __forceinline__ void settle(const Prefetch& pf) {
 #pragma unroll
   for (int c = 0; c < kChunksB; ++c) asm volatile("" ::"v"(pf.k[c]), "v"(pf.v[c]));
-#pragma unroll
-  for (int m = 0; m < 4; ++m) asm volatile("" ::"v"(pf.q[m]), "v"(pf.dout[m]));
+  asm volatile("" ::"v"(pf.qa), "v"(pf.qb), "v"(pf.da), "v"(pf.db));
   asm volatile("" ::"v"(pf.lse));
 }
 
@@ -587,13 +613,8 @@ __global__ void __launch_bounds__(kThreadsB) bwd_slab_bf16_kernel(Args<MH, STR> 
     const int wl = (r0 + 15 < N ? r0 + 15 : N - 1);
     commit_kv(lds_k, lds_v, lds_kf, N, tid, pf);
     uint32_t qw[8], dw[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      qw[2 * m] = pf.q[m].x;
-      qw[2 * m + 1] = pf.q[m].y;
-      dw[2 * m] = pf.dout[m].x;
-      dw[2 * m + 1] = pf.dout[m].y;
-    }
+    rows_of_chunks(pf.qa, pf.qb, part, qw);
+    rows_of_chunks(pf.da, pf.db, part, dw);
     const float lse2 = pf.lse * kLog2e;
     if (CLS && row == 0) {
       *reinterpret_cast<u32x4*>(lds_r0 + part * 32) = u32x4{qw[0], qw[1], qw[2], qw[3]};

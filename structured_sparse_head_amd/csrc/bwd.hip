@@ -78,28 +78,39 @@ __device__ __forceinline__ void zero_acc(float (&acc)[DL]) {
   for (int t = 0; t < DL; ++t) acc[t] = 0.f;
 }
 
+// A lane's fragment is chunks part, part + G, part + 2 G, ... of its row
+// (CH elements each: 16 bytes of the input type), so its element e sits at
+// CH (G (e / CH) + part) + e % CH of the row; fp32 chunk q of the lane's
+// fragment (4 elements, q = e / 4) lands at float4 index
+// (CH / 4) (G (q / (CH / 4)) + part) + q % (CH / 4).
+template <int CH, int G>
+__device__ __forceinline__ int frag_f4(int part, int q) {
+  constexpr int F = CH / 4;
+  return F * (G * (q / F) + part) + q % F;
+}
+
 // Stores x * scale as fp32.
-template <int DL>
+template <int DL, int CH, int G>
 __device__ __forceinline__ void store_f32_frag(float* row, int part, const float (&x)[DL],
                                                float scale) {
-  float4* p = reinterpret_cast<float4*>(row) + part * (DL / 4);
+  float4* p = reinterpret_cast<float4*>(row);
 #pragma unroll
   for (int t = 0; t < DL / 4; ++t)
-    p[t] = make_float4(x[4 * t] * scale, x[4 * t + 1] * scale, x[4 * t + 2] * scale,
-                       x[4 * t + 3] * scale);
+    p[frag_f4<CH, G>(part, t)] = make_float4(x[4 * t] * scale, x[4 * t + 1] * scale,
+                                             x[4 * t + 2] * scale, x[4 * t + 3] * scale);
 }
 
 // Stores (x - c * y) * scale as fp32.
-template <int DL>
+template <int DL, int CH, int G>
 __device__ __forceinline__ void store_f32_frag_diff(float* row, int part, const float (&x)[DL],
                                                     float c, const float (&y)[DL], float scale) {
-  float4* p = reinterpret_cast<float4*>(row) + part * (DL / 4);
+  float4* p = reinterpret_cast<float4*>(row);
 #pragma unroll
   for (int t = 0; t < DL / 4; ++t) {
     float r[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) r[u] = __builtin_fmaf(-c, y[4 * t + u], x[4 * t + u]) * scale;
-    p[t] = make_float4(r[0], r[1], r[2], r[3]);
+    p[frag_f4<CH, G>(part, t)] = make_float4(r[0], r[1], r[2], r[3]);
   }
 }
 
@@ -253,7 +264,7 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
       s_lse2[j] = lse2_j;
       if (CLS) a.ws[slab * N + j] = d_j;
     }
-    store_f32_frag_diff<Gm::kDL>(reinterpret_cast<float*>(rdq.row(j)), part, acc_a, d_j, acc_b,
+    store_f32_frag_diff<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(reinterpret_cast<float*>(rdq.row(j)), part, acc_a, d_j, acc_b,
                                  a.scale);
   }
   // The first key row's K and V come from LDS while they are still there.
@@ -293,8 +304,8 @@ __global__ void __launch_bounds__(NT) bwd_slab_kernel(BwdArgs<MH> a) {
     dkdv_row<T, D, G>(kr, N, s_deltas, nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
     if (CLS && !has_delta(s_deltas, nd, kr))
       dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
-    store_f32_frag<Gm::kDL>(reinterpret_cast<float*>(rdk.row(kr)), part, dk, a.scale);
-    store_f32_frag<Gm::kDL>(reinterpret_cast<float*>(rdv.row(kr)), part, dv, 1.0f);
+    store_f32_frag<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(reinterpret_cast<float*>(rdk.row(kr)), part, dk, a.scale);
+    store_f32_frag<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(reinterpret_cast<float*>(rdv.row(kr)), part, dv, 1.0f);
   }
 }
 
@@ -330,7 +341,7 @@ __global__ void __launch_bounds__(NT) bwd_dq_stream_kernel(BwdArgs<MH> a) {
   if (CLS && !has_delta(s_deltas, s_nd, j))
     dq_key<T, D, G>(0, a.scale_log2, lse2_j, qf, dof, acc_a, acc_b, d_j, lk, lv);
   if (part == 0) a.ws[slab * N + j] = d_j;
-  store_f32_frag_diff<Gm::kDL>(
+  store_f32_frag_diff<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(
       reinterpret_cast<float*>(slab_rows<float>(a.dq, a.ldq, slab, a.H).row(j)), part, acc_a, d_j,
       acc_b, a.scale);
 }
@@ -369,9 +380,9 @@ __global__ void __launch_bounds__(NT) bwd_dkdv_stream_kernel(BwdArgs<MH> a) {
   dkdv_row<T, D, G>(kr, N, s_deltas, s_nd, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
   if (CLS && !has_delta(s_deltas, s_nd, kr))
     dkdv_query<T, D, G>(0, a.scale_log2, kf, vf, dk, dv, lq, ldo, lrow);
-  store_f32_frag<Gm::kDL>(
+  store_f32_frag<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(
       reinterpret_cast<float*>(slab_rows<float>(a.dk, a.ldk, slab, a.H).row(kr)), part, dk, a.scale);
-  store_f32_frag<Gm::kDL>(
+  store_f32_frag<Gm::kDL, 16 / static_cast<int>(sizeof(T)), G>(
       reinterpret_cast<float*>(slab_rows<float>(a.dv, a.ldv, slab, a.H).row(kr)), part, dv, 1.0f);
 }
 

@@ -199,7 +199,7 @@ __device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, in
   const float inv = has ? 1.0f / l : 0.f;
   constexpr int es = static_cast<int>(sizeof(T));
   u32x4* orow = reinterpret_cast<u32x4*>(a.o + a.lo.slab_bytes(slab, a.H, es) + j * a.lo.row_bytes(es)) +
-                part * Gm::kCPL;
+                part;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int t = 0; t < Gm::kCPL; ++t) {
@@ -209,12 +209,12 @@ __device__ __forceinline__ void finish_row(const Args& a, size_t slab, int j, in
         const int e = 8 * t + 2 * u;
         w[u] = f32_to_bf16(acc[e] * inv) | (f32_to_bf16(acc[e + 1] * inv) << 16);
       }
-      orow[t] = u32x4{w[0], w[1], w[2], w[3]};
+      orow[t * G] = u32x4{w[0], w[1], w[2], w[3]};
     }
   } else {
 #pragma unroll
     for (int t = 0; t < Gm::kCPL; ++t) {
-      orow[t] = u32x4{__float_as_uint(acc[4 * t + 0] * inv), __float_as_uint(acc[4 * t + 1] * inv),
+      orow[t * G] = u32x4{__float_as_uint(acc[4 * t + 0] * inv), __float_as_uint(acc[4 * t + 1] * inv),
                       __float_as_uint(acc[4 * t + 2] * inv), __float_as_uint(acc[4 * t + 3] * inv)};
     }
   }

@@ -53,10 +53,10 @@ template <typename T, int D, int G>
 __device__ __forceinline__ void frag_load_global(const char* row, int part,
                                                  uint32_t (&f)[Geom<T, D, G>::kWPL]) {
   using Gm = Geom<T, D, G>;
-  const u32x4* p = reinterpret_cast<const u32x4*>(row) + part * Gm::kCPL;
+  const u32x4* p = reinterpret_cast<const u32x4*>(row) + part;
 #pragma unroll
   for (int t = 0; t < Gm::kCPL; ++t) {
-    const u32x4 x = __builtin_nontemporal_load(p + t);
+    const u32x4 x = __builtin_nontemporal_load(p + t * G);
     f[4 * t + 0] = x.x;
     f[4 * t + 1] = x.y;
     f[4 * t + 2] = x.z;
@@ -69,10 +69,10 @@ template <typename T, int D, int G>
 __device__ __forceinline__ void frag_load_cached(const char* row, int part,
                                                  uint32_t (&f)[Geom<T, D, G>::kWPL]) {
   using Gm = Geom<T, D, G>;
-  const u32x4* p = reinterpret_cast<const u32x4*>(row) + part * Gm::kCPL;
+  const u32x4* p = reinterpret_cast<const u32x4*>(row) + part;
 #pragma unroll
   for (int t = 0; t < Gm::kCPL; ++t) {
-    const u32x4 x = p[t];
+    const u32x4 x = p[t * G];
     f[4 * t + 0] = x.x;
     f[4 * t + 1] = x.y;
     f[4 * t + 2] = x.z;
@@ -87,7 +87,7 @@ __device__ __forceinline__ void frag_load_lds(const char* base, int r, int part,
   const char* row = base + r * Gm::kRowBytes;
 #pragma unroll
   for (int t = 0; t < Gm::kCPL; ++t) {
-    const int c = lds_chunk<Gm::kCPR>(r, part * Gm::kCPL + t);
+    const int c = lds_chunk<Gm::kCPR>(r, t * G + part);
     const u32x4 x = *reinterpret_cast<const u32x4*>(row + c * 16);
     f[4 * t + 0] = x.x;
     f[4 * t + 1] = x.y;
@@ -103,7 +103,7 @@ __device__ __forceinline__ void frag_store_lds(char* base, int r, int part,
   char* row = base + r * Gm::kRowBytes;
 #pragma unroll
   for (int t = 0; t < Gm::kCPL; ++t) {
-    const int c = lds_chunk<Gm::kCPR>(r, part * Gm::kCPL + t);
+    const int c = lds_chunk<Gm::kCPR>(r, t * G + part);
     *reinterpret_cast<u32x4*>(row + c * 16) = u32x4{f[4 * t + 0], f[4 * t + 1], f[4 * t + 2], f[4 * t + 3]};
   }
 }

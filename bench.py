@@ -115,11 +115,15 @@ SOURCES = {
 
 
 def source_hash(kernel):
+    """Hash of a kernel's sources and of the compile flags of its own file."""
+    from structured_sparse_head_amd.build import FILE_FLAGS
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "structured_sparse_head_amd", "csrc")
     for f in SOURCES[kernel] + ["kernel_common.h", "problem.h", "fib_offsets.h", "launch.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    for f in SOURCES[kernel]:
+        h.update(" ".join(FILE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,11 +38,21 @@ FLAGS = [
     # packed fp32 instructions stay off (the compiler would otherwise form them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Instruction scheduling per translation unit.  Each of LLVM's AMDGPU
+# scheduling strategies was timed on the ViT-B/16 passes (B64 H12 N197 d64
+# bf16, 200 launches each): the forward took 22.5 us with iterative-ilp
+# against 23.1 us by default, the backward 48.6 us with max-ilp against
+# 48.9-49.2 us.  The long-sequence kernels gained nothing from either and
+# keep the default.
+FILE_FLAGS = {
+    "fwd_slab_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "bwd_slab_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

@@ -42,11 +42,14 @@ FLAGS = [
 # scheduling strategies was timed on the ViT-B/16 passes (B64 H12 N197 d64
 # bf16, 200 launches each): the forward took 22.5 us with iterative-ilp
 # against 23.1 us by default, the backward 48.6 us with max-ilp against
-# 48.9-49.2 us.  The long-sequence and general kernels gained nothing from
-# any strategy and keep the default.
+# 48.9-49.2 us.  The long-sequence forward gains 0.4-0.7% with iterative-ilp
+# (B16 H12 N1569, B4 H16 N4097, B1 H16 N65536); the long-sequence backward
+# and the general kernels gained nothing from any strategy and keep the
+# default.
 FILE_FLAGS = {
     "fwd_slab_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "bwd_slab_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "fwd_tile_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
